@@ -1,0 +1,51 @@
+"""Build the gfx950 shared library libdcpattn.so in-tree (hipcc, no JIT)."""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libdcpattn.so")
+SOURCES = ["dcp_api.cpp", "plan.hip", "merge.hip", "gqa_shard.hip", "mla_shard.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         # packed fp32 VALU forms are kept out of the generated code
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", INCLUDE, "-I", CSRC]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+    return obj, out
+
+
+def build(verbose=False):
+    """Compile every source for gfx950 and link libdcpattn.so next to this file."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for _, out in results:
+        if out.strip() and verbose:
+            print(out)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

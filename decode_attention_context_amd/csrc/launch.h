@@ -1,0 +1,62 @@
+// launch.h — host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace dcp {
+
+// Work planning of one shard call: per-request owned-token counts, the tokens-per-item
+// split size and the flat list of (request, local token range) items.
+hipError_t launch_plan(const int32_t* seq_lens, int batch, int rank, int cp, int interleave,
+                       int64_t len_cap, int64_t target_items, int tile, int min_chunk,
+                       const WsPtrs& ws, hipStream_t stream);
+
+// LSE merge of `n` partials per row (rows = batch * heads).
+hipError_t launch_merge(const float* o_partials, const float* lse_partials, int n, int batch,
+                        int heads, int dv, void* o_out, int out_bf16, float* lse_out,
+                        hipStream_t stream);
+
+// Combine of the split partials of each request into the shard output.
+hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, float* o_out,
+                                float* lse_out, hipStream_t stream);
+
+struct GqaArgs {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  int hq, hkv, head_dim, block_size, max_blocks;
+  int64_t num_blocks;
+  int rank, cp, interleave;
+  float scale;
+  int dtype;  // 0 f32, 1 bf16
+};
+hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
+                            float* o_out, float* lse_out, hipStream_t stream);
+bool gqa_supported(int dtype, int head_dim, int group);
+
+struct MlaArgs {
+  const void* q;
+  const void* latent;
+  const int32_t* block_table;
+  int block_size, max_blocks;
+  int64_t num_blocks;
+  int rank, cp, interleave;
+  float scale;
+};
+hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& ws,
+                            float* o_out, float* lse_out, hipStream_t stream);
+
+hipError_t launch_shard_slots(const int32_t* block_table, const int32_t* seq_lens, int batch,
+                              int max_blocks, int block_size, int64_t num_blocks, int rank,
+                              int cp, int interleave, const int64_t* out_offsets,
+                              int64_t* slots_out, int32_t* err_word, hipStream_t stream);
+
+// Tokens per tile of each shard kernel (work items are whole multiples of it).
+constexpr int kGqaTile = 64;
+constexpr int kMlaTile = 64;
+
+}  // namespace dcp

@@ -1,0 +1,189 @@
+// merge.hip — LSE-weighted merge of partial attention outputs.
+//
+// The merge of the DCP execution flow ("vLLM Decode Context Parallelism for long-context
+// workloads" blog, section "DCP execution flow", step 3): partials (O_r, lse_r) computed
+// over disjoint token sets combine, with m = max of the finite lse_r and
+// w_r = exp(lse_r - m) (exactly 0 for a non-finite lse_r, whose O_r is never read), into
+//     lse = m + ln sum w_r,     O = sum w_r O_r / sum w_r,
+// which is the attention over the union of the token sets.  The same row merge combines
+// the split-K partials of one shard call, whose items cover disjoint local token ranges.
+//
+// One wave merges one (request, head) row: the n lse values are wave-uniform scalar
+// loads, then each lane streams VEC consecutive floats of every partial row (all partial
+// loads of a chunk are issued before they are summed).  The kernel is HBM-bound.
+#include "launch.h"
+
+namespace dcp {
+
+namespace {
+
+template <int VEC>
+struct VecT;
+template <>
+struct VecT<1> { using T = float; };
+template <>
+struct VecT<2> { using T = float2; };
+template <>
+struct VecT<4> { using T = float4; };
+
+template <int VEC>
+__device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename VecT<VEC>::T& v) {
+  const float* p = reinterpret_cast<const float*>(&v);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = fmaf(w, p[i], acc[i]);
+}
+
+// Merge `n` partial rows o_base[r * o_stride .. + dv) with lse l_base[r * l_stride].
+template <int VEC>
+__device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int64_t o_stride,
+                                          const float* __restrict__ l_base, int64_t l_stride,
+                                          int n, int dv, float* __restrict__ out_f32,
+                                          uint16_t* __restrict__ out_bf16,
+                                          float* __restrict__ lse_out, int lane) {
+  using V = typename VecT<VEC>::T;
+  float m = neg_inf();
+  for (int r = 0; r < n; ++r) {
+    const float x = l_base[r * l_stride];
+    if (__builtin_isfinite(x)) m = fmaxf(m, x);
+  }
+  if (m == neg_inf()) {
+    // every partial is empty
+    for (int d = lane * VEC; d < dv; d += 64 * VEC) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        if (out_f32) out_f32[d + i] = 0.f;
+        else out_bf16[d + i] = 0;
+      }
+    }
+    if (lse_out && lane == 0) *lse_out = neg_inf();
+    return;
+  }
+  const float m2 = m * kLog2e;
+  float wsum = 0.f;
+  for (int r = 0; r < n; ++r) {
+    const float x = l_base[r * l_stride];
+    wsum += __builtin_isfinite(x) ? exp2f(fmaf(x, kLog2e, -m2)) : 0.f;
+  }
+  const float inv = 1.f / wsum;
+  for (int d = lane * VEC; d < dv; d += 64 * VEC) {
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    int r = 0;
+    for (; r + 8 <= n; r += 8) {
+      V v[8];
+      float w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float x = l_base[(r + u) * l_stride];
+        w[u] = __builtin_isfinite(x) ? exp2f(fmaf(x, kLog2e, -m2)) : 0.f;
+        if (w[u] != 0.f) v[u] = *reinterpret_cast<const V*>(o_base + (r + u) * o_stride + d);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (w[u] != 0.f) vfma<VEC>(acc, w[u], v[u]);
+    }
+    for (; r < n; ++r) {
+      const float x = l_base[r * l_stride];
+      const float w = __builtin_isfinite(x) ? exp2f(fmaf(x, kLog2e, -m2)) : 0.f;
+      if (w != 0.f) vfma<VEC>(acc, w, *reinterpret_cast<const V*>(o_base + r * o_stride + d));
+    }
+    if (out_f32) {
+      V o;
+      float* po = reinterpret_cast<float*>(&o);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) po[i] = acc[i] * inv;
+      *reinterpret_cast<V*>(out_f32 + d) = o;
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) out_bf16[d + i] = (uint16_t)f32_to_bf16_rne(acc[i] * inv);
+    }
+  }
+  if (lse_out && lane == 0) *lse_out = (m2 + log2f(wsum)) * kLn2;
+}
+
+constexpr int kRowsPerBlock = 4;
+
+template <int VEC>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void merge_kernel(
+    const float* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
+    int batch, int heads, int dv, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
+    float* __restrict__ lse_out) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)batch * heads;
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  merge_row<VEC>(o_partials + row * dv, rows * dv, lse_partials + row, rows, n, dv,
+                 out_f32 ? out_f32 + row * dv : nullptr, out_bf16 ? out_bf16 + row * dv : nullptr,
+                 lse_out ? lse_out + row : nullptr, lane);
+}
+
+// Split combine: request b's items [off[b], off[b+1]) hold partials of every head.  A
+// request with a single item was written directly by the shard kernel; a request with no
+// item (empty shard) gets O = 0, lse = -inf.
+template <int VEC>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
+    const int32_t* __restrict__ off, const float* __restrict__ plse, const float* __restrict__ po,
+    int batch, int hq, int dv, float* __restrict__ o_out, float* __restrict__ lse_out) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= (int64_t)batch * hq) return;
+  const int b = (int)(row / hq), h = (int)(row - (int64_t)b * hq);
+  const int i0 = off[b], n = off[b + 1] - i0;
+  if (n == 1) return;
+  const int lane = threadIdx.x & 63;
+  merge_row<VEC>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h,
+                 hq, n, dv, o_out + row * dv, nullptr, lse_out + row, lane);
+}
+
+int pick_vec(int dv) {
+  if (dv % 256 == 0) return 4;
+  if (dv % 128 == 0) return 2;
+  return 1;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* o_partials, const float* lse_partials, int n, int batch,
+                        int heads, int dv, void* o_out, int out_bf16, float* lse_out,
+                        hipStream_t stream) {
+  const int64_t rows = (int64_t)batch * heads;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  float* of = out_bf16 ? nullptr : static_cast<float*>(o_out);
+  uint16_t* ob = out_bf16 ? static_cast<uint16_t*>(o_out) : nullptr;
+  switch (pick_vec(dv)) {
+    case 4:
+      hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(64 * kRowsPerBlock), 0, stream, o_partials,
+                         lse_partials, n, batch, heads, dv, of, ob, lse_out);
+      break;
+    case 2:
+      hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(64 * kRowsPerBlock), 0, stream, o_partials,
+                         lse_partials, n, batch, heads, dv, of, ob, lse_out);
+      break;
+    default:
+      hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(64 * kRowsPerBlock), 0, stream, o_partials,
+                         lse_partials, n, batch, heads, dv, of, ob, lse_out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, float* o_out,
+                                float* lse_out, hipStream_t stream) {
+  const int64_t rows = (int64_t)batch * hq;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  switch (pick_vec(dv)) {
+    case 4:
+      hipLaunchKernelGGL(split_combine_kernel<4>, grid, dim3(64 * kRowsPerBlock), 0, stream,
+                         ws.off, ws.plse, ws.po, batch, hq, dv, o_out, lse_out);
+      break;
+    case 2:
+      hipLaunchKernelGGL(split_combine_kernel<2>, grid, dim3(64 * kRowsPerBlock), 0, stream,
+                         ws.off, ws.plse, ws.po, batch, hq, dv, o_out, lse_out);
+      break;
+    default:
+      hipLaunchKernelGGL(split_combine_kernel<1>, grid, dim3(64 * kRowsPerBlock), 0, stream,
+                         ws.off, ws.plse, ws.po, batch, hq, dv, o_out, lse_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dcp

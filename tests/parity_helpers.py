@@ -1,0 +1,118 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the binding, fetch the
+exact inputs a request used, and compare against the CPU oracle elementwise.
+
+Tolerances (written here once, used by every parity test):
+  * outputs O computed from bf16 inputs: |x - x*| <= 2e-2 + 2e-2 |x*|
+  * outputs O computed from fp32 inputs, and every LSE: |x - x*| <= 1e-3 + 1e-3 |x*|
+  * an LSE of -inf (empty shard) must be exactly -inf, and its O exactly 0
+  * the index mapping (physical slots of a rank's tokens) must be bit-exact
+"""
+import math
+
+import numpy as np
+import torch
+
+import decode_attention_context_amd as dca
+from oracle import dcp_oracle as orc
+
+TOL_BF16_O = (2e-2, 2e-2)
+TOL_F32 = (1e-3, 1e-3)
+
+
+def assert_close(got, ref, tol, what):
+    atol, rtol = tol
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    ninf_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), ninf_ref), f"{what}: -inf pattern differs"
+    fin = ~ninf_ref
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite values"
+    err = np.abs(got[fin] - ref[fin])
+    bound = atol + rtol * np.abs(ref[fin])
+    if err.size and not np.all(err <= bound):
+        i = int(np.argmax(err - bound))
+        raise AssertionError(f"{what}: max excess {float((err - bound)[i]):.3e} "
+                             f"(err {float(err[i]):.3e}, ref {float(ref[fin][i]):.4f}); "
+                             f"max abs err {float(err.max()):.3e}")
+
+
+def o_tol(kind, dtype):
+    return TOL_BF16_O if dtype == torch.bfloat16 else TOL_F32
+
+
+def run_shards(inp, kind, cp_size, interleave, scale, ranks=None):
+    """Every rank's (O_r, lse_r) on the GPU, stacked: [C, b, H, Dv], [C, b, H]."""
+    q = inp["q"]
+    kv = inp["k_pages"] if kind == dca.GQA else inp["latent_pages"]
+    v = inp["v_pages"] if kind == dca.GQA else None
+    os_, ls_ = [], []
+    ws = None
+    for r in (range(cp_size) if ranks is None else ranks):
+        o, l, ws = dca.shard(q, kv, v, inp["block_table"], inp["seq_lens"], r, cp_size,
+                             interleave, scale, kind=kind, max_seq_len=inp["max_seq_len"],
+                             workspace=ws)
+        os_.append(o)
+        ls_.append(l)
+        assert dca.read_device_errors(ws) == 0
+    return torch.stack(os_), torch.stack(ls_)
+
+
+def request_host(inp, kind, b):
+    """Exact float64 copies of what request b reads: its query, its pages (compacted) and a
+    block-table row that addresses the compact copy."""
+    L = int(inp["seq_lens"][b].item())
+    bt = inp["block_table"]
+    if kind == dca.GQA:
+        B = inp["k_pages"].shape[2]
+    else:
+        B = inp["latent_pages"].shape[1]
+    npages = (L + B - 1) // B
+    pages = bt[b, :npages].long()
+    q = inp["q"][b].float().cpu().numpy().astype(np.float64)
+    row = np.arange(npages, dtype=np.int64)
+    if kind == dca.GQA:
+        k = inp["k_pages"][pages].float().cpu().numpy().astype(np.float64)
+        v = inp["v_pages"][pages].float().cpu().numpy().astype(np.float64)
+        return dict(q=q, k=k, v=v, row=row, L=L, B=B)
+    lat = inp["latent_pages"][pages].float().cpu().numpy().astype(np.float64)
+    return dict(q=q, lat=lat, row=row, L=L, B=B)
+
+
+def oracle_shard(h, kind, rank, cp_size, interleave, scale):
+    if kind == dca.GQA:
+        return orc.gqa_shard(h["q"], h["k"], h["v"], h["row"], h["L"], rank, cp_size,
+                             interleave, scale, h["B"])
+    return orc.mla_shard(h["q"], h["lat"], h["row"], h["L"], rank, cp_size, interleave,
+                         scale, h["B"])
+
+
+def oracle_full(h, kind, scale):
+    if kind == dca.GQA:
+        return orc.gqa_full(h["q"], h["k"], h["v"], h["row"], h["L"], scale, h["B"])
+    return orc.mla_full(h["q"], h["lat"], h["row"], h["L"], scale, h["B"])
+
+
+def check_requests(inp, kind, cp_size, interleave, scale, o_parts, l_parts, o_merged,
+                   l_merged, requests, label):
+    """Compare every rank's partial and the merged output of the sampled requests."""
+    tol = o_tol(kind, inp["q"].dtype)
+    o_parts = o_parts.cpu().numpy()
+    l_parts = l_parts.cpu().numpy()
+    o_merged = o_merged.cpu().numpy()
+    l_merged = l_merged.cpu().numpy()
+    for b in requests:
+        h = request_host(inp, kind, b)
+        for r in range(cp_size):
+            o_ref, l_ref = oracle_shard(h, kind, r, cp_size, interleave, scale)
+            assert_close(l_parts[r, b], l_ref, TOL_F32, f"{label} b={b} rank={r} lse")
+            assert_close(o_parts[r, b], o_ref, tol, f"{label} b={b} rank={r} O")
+            if np.all(np.isneginf(l_ref)):
+                assert np.all(o_parts[r, b] == 0), f"{label} b={b} rank={r}: empty shard O != 0"
+        o_ref, l_ref = oracle_full(h, kind, scale)
+        assert_close(l_merged[b], l_ref, TOL_F32, f"{label} b={b} merged lse")
+        assert_close(o_merged[b], o_ref, tol, f"{label} b={b} merged O")
+
+
+def scale_of(d):
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,137 @@
+"""GPU tests of the merge kernel alone, the exported block-table walk (bit-exact) and the
+device error word."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_context_amd as dca
+from decode_attention_context_amd import workloads as wl
+from oracle import dcp_oracle as orc
+from parity_helpers import TOL_F32, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("c,b,h,dv", [(2, 3, 8, 128), (8, 5, 128, 512), (4, 2, 3, 64),
+                                      (3, 4, 2, 100), (1, 2, 4, 256)])
+def test_merge_poisoned_partials(gpu_lib, c, b, h, dv):
+    """Merge kernel vs the oracle's merge on synthetic partials where some partials are
+    empty (lse = -inf) and carry NaN garbage, and some rows are entirely empty."""
+    print(f"[merge] C={c} b={b} H={h} Dv={dv}", flush=True)
+    g = torch.Generator().manual_seed(100 + c + dv)
+    o = torch.randn(c, b, h, dv, generator=g)
+    lse = torch.randn(c, b, h, generator=g) * 6
+    empty = torch.rand(c, b, h, generator=g) < 0.3
+    lse[empty] = -float("inf")
+    o[empty] = float("nan")
+    lse[:, 0, 0] = -float("inf")            # a row with every partial empty
+    o[:, 0, 0] = float("nan")
+    out, lse_out = dca.merge(o.cuda(), lse.cuda())
+    ref_o, ref_l = orc.merge(o.numpy(), lse.numpy())
+    assert_close(lse_out.cpu().numpy(), ref_l, (1e-5, 1e-5), "merged lse")
+    assert_close(out.cpu().numpy(), ref_o, (1e-5, 1e-5), "merged O")
+    assert torch.all(out[0, 0] == 0)
+    # bf16 output: the fp32 result rounded to nearest even
+    out_bf, _ = dca.merge(o.cuda(), lse.cuda(), out_dtype=torch.bfloat16, want_lse=False)
+    assert torch.equal(out_bf.cpu(), out.cpu().to(torch.bfloat16))
+
+
+def _slots_case(bt, lens, B, nb, C, I, label):
+    bt_d = torch.from_numpy(bt).cuda()
+    lens_d = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    for r in range(C):
+        slots, offs, ws = dca.shard_slots(bt_d, lens_d, B, nb, r, C, I, seq_lens_host=list(lens))
+        assert dca.read_device_errors(ws) == 0
+        slots = slots.cpu().numpy()
+        offs = offs.cpu().numpy()
+        for b, L in enumerate(lens):
+            ref = orc.owned_slots(bt[b], L, B, r, C, I)
+            got = slots[offs[b]:offs[b + 1]]
+            assert np.array_equal(got, ref), f"{label}: rank {r} request {b} slots differ"
+
+
+@pytest.mark.parametrize("w", list(wl.WORKLOADS.values()), ids=list(wl.WORKLOADS))
+def test_slots_bit_exact_workloads(gpu_lib, w):
+    """The walk the kernels use, exported, equals the oracle's filter over every position,
+    for every rank of every workload's real block table."""
+    print(f"[slots] {w.name}", flush=True)
+    lens = w.seq_lens()
+    B = w.block_size
+    pages = [(int(n) + B - 1) // B for n in lens]
+    nb = sum(pages)
+    rng = np.random.default_rng(w.seed)
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((w.batch, max(pages)), -1, dtype=np.int32)
+    o = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[o:o + n]
+        o += n
+    _slots_case(bt, [int(x) for x in lens], B, nb, w.cp_size, w.interleave, w.name)
+
+
+@pytest.mark.parametrize("B,C,I,lens", [
+    (16, 2, 4, [1, 7, 16, 17, 100]),        # I < B
+    (16, 3, 24, [1, 48, 95, 500]),          # B does not divide I
+    (12, 2, 8, [1, 24, 25, 300]),           # I does not divide B
+    (8, 4, 8, [32, 64, 96]),                # L = 0 mod I C
+    (4, 5, 7, [1, 2, 3, 34, 35, 36]),
+    (64, 8, 64, [1, 63, 64, 65, 511, 512, 513]),
+])
+def test_slots_bit_exact_edges(gpu_lib, B, C, I, lens):
+    rng = np.random.default_rng(B * 100 + C * 10 + I)
+    pages = [(n + B - 1) // B for n in lens]
+    nb = sum(pages) + 3
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((len(lens), max(pages)), -1, dtype=np.int32)
+    o = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[o:o + n]
+        o += n
+    _slots_case(bt, lens, B, nb, C, I, f"B={B} C={C} I={I}")
+
+
+def test_device_error_word(gpu_lib):
+    """Contract violations only the device sees are flagged, never fault, and leave the
+    remaining tokens' attention intact."""
+    w = wl.GQA_SHARE.with_(batch=2, lengths=(300, 200), seed=31)
+    inp = wl.make_inputs(w, device="cuda")
+    bt = inp["block_table"].clone()
+    # request 1 claims more tokens than its block-table row covers
+    lens = inp["seq_lens"].clone()
+    lens[1] = bt.shape[1] * w.block_size + 50
+    o, l, ws = dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], bt, lens, 0, 1, 128,
+                         w.scale)
+    assert dca.read_device_errors(ws) & dca.DEVERR_SEQ_LEN
+    assert torch.isfinite(o).all() and torch.isfinite(l).all()
+    # a block id outside the cache
+    bt2 = inp["block_table"].clone()
+    bt2[0, 1] = 10 ** 6
+    o, l, ws = dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], bt2, inp["seq_lens"], 0, 1,
+                         128, w.scale, workspace=ws)
+    assert dca.read_device_errors(ws) & dca.DEVERR_BLOCK_ID
+    assert torch.isfinite(o).all() and torch.isfinite(l).all()
+    # a clean call clears the word
+    dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"], 0,
+              1, 128, w.scale, workspace=ws)
+    assert dca.read_device_errors(ws) == 0
+
+
+def test_shard_is_deterministic(gpu_lib):
+    w = wl.MLA_DECODE.with_(batch=2, lengths=(3000, 777), seed=41)
+    inp = wl.make_inputs(w, device="cuda")
+    a = dca.shard(inp["q"], inp["latent_pages"], None, inp["block_table"], inp["seq_lens"], 1,
+                  8, 64, w.scale)
+    b = dca.shard(inp["q"], inp["latent_pages"], None, inp["block_table"], inp["seq_lens"], 1,
+                  8, 64, w.scale)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_argument_errors_launch_nothing(gpu_lib):
+    w = wl.TINY_GQA
+    inp = wl.make_inputs(w, device="cuda")
+    with pytest.raises(dca.DCPError):
+        dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
+                  2, 2, 16, w.scale)   # rank >= cp_size
+    with pytest.raises(dca.DCPError):
+        dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
+                  0, 2, 0, w.scale)    # interleave 0
