@@ -1,0 +1,314 @@
+"""Benchmark of the DCP decode-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: every DCP rank's shard attention
+(virtual ranks of one paged cache on this GPU) followed by the LSE merge of their partials,
+which yields exact unsharded attention for every request.  The default workload is the
+GQA per-GPU share shaped like Qwen3-235B: 64 decode requests x 32768 tokens, 8 query heads
+on 1 KV head, head dim 128, bf16 cache in 128-token pages, DCP size 2 with interleave 128.
+
+Printed: one JSON line with the throughput (KV tokens of context attended per second), the
+roofline of the dominant kernel (the GQA shard kernel, timed with HIP events recorded on
+its own stream around every launch) and the CPU oracle timed on a bounded sample of the
+same workload.  `secondary` adds the MLA shard kernel (MFMA utilisation) and the 8-way
+merge on the MLA decode workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def _src_hash(name):
+    p = os.path.join(ROOT, "decode_attention_context_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def owned_tokens_count(L, rank, cp, il):
+    """Tokens of an L-token sequence stored by `rank` (the library's host walker)."""
+    import decode_attention_context_amd as dca
+    return dca.local_len(L, rank, cp, il)
+
+
+def owned_pages_count(L, rank, cp, il, bs):
+    """Cache pages holding at least one token the rank stores (each block-table entry the
+    shard kernel needs)."""
+    pages = set()
+    g = rank
+    while g * il < L:
+        lo, hi = g * il, min(g * il + il, L)
+        pages.update(range(lo // bs, (hi - 1) // bs + 1))
+        g += cp
+    return len(pages)
+
+
+def gqa_launch_bytes(w, lens, rank):
+    """Algorithmic HBM bytes of one GQA shard launch: the K and V rows the rank owns, the
+    queries, the block-table entries of owned pages, and the O / lse written."""
+    elem = 2 if w.dtype == "bf16" else 4
+    tok = sum(owned_tokens_count(int(L), rank, w.cp_size, w.interleave) for L in lens)
+    pages = sum(owned_pages_count(int(L), rank, w.cp_size, w.interleave, w.block_size)
+                for L in lens)
+    kv = tok * 2 * w.num_kv_heads * w.head_dim_qk * elem
+    q = w.batch * w.num_q_heads * w.head_dim_qk * elem
+    out = w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
+    return kv + q + out + pages * 4, tok
+
+
+def mla_launch_cost(w, lens, rank):
+    tok = sum(owned_tokens_count(int(L), rank, w.cp_size, w.interleave) for L in lens)
+    pages = sum(owned_pages_count(int(L), rank, w.cp_size, w.interleave, w.block_size)
+                for L in lens)
+    byts = tok * w.head_dim_qk * 2 + w.batch * w.num_q_heads * (w.head_dim_qk * 2 +
+                                                                (w.head_dim_v + 1) * 4) + pages * 4
+    flops = tok * 2 * w.num_q_heads * (w.head_dim_qk + w.head_dim_v)
+    return byts, flops, tok
+
+
+def load_counters(kernel_key, src_name):
+    """HBM traffic measured by rocprofv3 counters for this kernel, if recorded against the
+    current source of the kernel (else None)."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    e = d.get(kernel_key)
+    if not e or e.get("source_sha") != _src_hash(src_name):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seconds_target=15.0, max_requests=16):
+    """The oracle, as it stands, on the first requests of the same workload: every shard of a
+    request plus their merge, in float64 numpy on the host's cores."""
+    import numpy as np
+    import torch
+    from oracle import dcp_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    B = w.block_size
+    done_tokens = 0
+    n_req = 0
+    t_total = 0.0
+    for b in range(min(max_requests, w.batch)):
+        L = int(inp["seq_lens"][b].item())
+        npages = (L + B - 1) // B
+        pages = inp["block_table"][b, :npages].long()
+        q = inp["q"][b].float().cpu().numpy().astype(np.float64)
+        row = np.arange(npages)
+        if w.kind == "gqa":
+            k = inp["k_pages"][pages].float().cpu().numpy().astype(np.float64)
+            v = inp["v_pages"][pages].float().cpu().numpy().astype(np.float64)
+        else:
+            lat = inp["latent_pages"][pages].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        parts = []
+        for r in range(w.cp_size):
+            if w.kind == "gqa":
+                parts.append(orc.gqa_shard(q, k, v, row, L, r, w.cp_size, w.interleave,
+                                           w.scale, B))
+            else:
+                parts.append(orc.mla_shard(q, lat, row, L, r, w.cp_size, w.interleave,
+                                           w.scale, B))
+        orc.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        t_total += time.perf_counter() - t0
+        done_tokens += L
+        n_req += 1
+        if t_total > seconds_target:
+            break
+    return {"value": done_tokens / t_total, "unit": "KV tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {n_req} of {w.batch} requests of the same workload: all "
+                      f"{w.cp_size} shard partials + merge in float64 numpy "
+                      f"({t_total:.1f} s of CPU time)"}
+
+
+def run_step_fns(dca, w, inp, kind):
+    import torch
+    q = inp["q"]
+    kv = inp["k_pages"] if kind == dca.GQA else inp["latent_pages"]
+    v = inp["v_pages"] if kind == dca.GQA else None
+    C = w.cp_size
+    o_parts = torch.empty(C, w.batch, w.num_q_heads, w.head_dim_v, device="cuda")
+    l_parts = torch.empty(C, w.batch, w.num_q_heads, device="cuda")
+    o = torch.empty(w.batch, w.num_q_heads, w.head_dim_v, device="cuda")
+    lse = torch.empty(w.batch, w.num_q_heads, device="cuda")
+    ws = dca.alloc_workspace(dca.make_desc(kind, q, kv, inp["block_table"]), w.batch,
+                             inp["max_seq_len"], C, w.interleave)
+    shard_events, merge_events = [], []
+
+    def step(record):
+        for r in range(C):
+            ev = None
+            if record:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                shard_events.append(ev)
+            dca.shard(q, kv, v, inp["block_table"], inp["seq_lens"], r, C, w.interleave,
+                      w.scale, kind=kind, max_seq_len=inp["max_seq_len"], out=o_parts[r],
+                      lse=l_parts[r], workspace=ws, events=ev)
+        if record:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record()
+        dca.merge(o_parts, l_parts, out=o, lse_out=lse)
+        if record:
+            ev[1].record()
+            merge_events.append(ev)
+
+    return step, shard_events, merge_events, ws
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_qwen3_235b_share")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the other DCP "
+              "ranks are virtual shards of one cache); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_context_amd as dca
+    from decode_attention_context_amd import workloads as wl
+
+    if args.copy_calibration:
+        n = 1 << 30
+        x = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 5}))
+        return
+
+    dca.load()
+    w = wl.WORKLOADS[args.workload]
+    kind = dca.GQA if w.kind == "gqa" else dca.MLA
+    inp = wl.make_inputs(w, device="cuda")
+    lens = w.seq_lens()
+    step, shard_ev, merge_ev, ws = run_step_fns(dca, w, inp, kind)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert dca.read_device_errors(ws) == 0
+
+    shard_ms = [a.elapsed_time(b) for a, b in shard_ev]
+    merge_ms = [a.elapsed_time(b) for a, b in merge_ev]
+    C = w.cp_size
+    # per-rank average kernel duration; algorithmic bytes per launch averaged over ranks
+    per_rank_ms = [sum(shard_ms[r::C]) / len(shard_ms[r::C]) for r in range(C)]
+    tokens_per_step = int(sum(int(L) for L in lens))
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = tokens_per_step * args.steps / elapsed
+
+    if kind == dca.GQA:
+        costs = [gqa_launch_bytes(w, lens, r) for r in range(C)]
+        bytes_avg = sum(c[0] for c in costs) / C
+        dur_s = sum(per_rank_ms) / C / 1e3
+        achieved = bytes_avg / dur_s / 1e9
+        traffic = load_counters("gqa_shard", "gqa_shard.hip")
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "gqa_shard_kernel<bf16,G=8>",
+                "algorithmic_bytes_per_launch": int(bytes_avg),
+                "avg_launch_us": round(dur_s * 1e6, 2)}
+        kernel_name = "gqa_shard"
+    else:
+        costs = [mla_launch_cost(w, lens, r) for r in range(C)]
+        flops_avg = sum(c[1] for c in costs) / C
+        dur_s = sum(per_rank_ms) / C / 1e3
+        achieved = flops_avg / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": load_counters("mla_shard", "mla_shard.hip"),
+                "kernel": "mla_shard_kernel",
+                "algorithmic_flops_per_launch": int(flops_avg),
+                "hbm_gbs": round(sum(c[0] for c in costs) / C / dur_s / 1e9, 1),
+                "avg_launch_us": round(dur_s * 1e6, 2)}
+        kernel_name = "mla_shard"
+
+    merge_us = sum(merge_ms) / len(merge_ms) * 1e3
+    merge_bytes = C * w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4 + \
+        w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
+    line = {
+        "metric": "shard decode attn: HBM GB/s (% peak), KV tokens/s; MLA MFMA util; merge GB/s",
+        "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": int(max(lens)),
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
+                   "block_size": w.block_size, "cp_size": C, "interleave": w.interleave,
+                   "step": f"{C} virtual-rank shard launches + 1 merge"},
+        "roofline": roof,
+        "kernels": {f"{kernel_name}_us_per_rank": [round(x * 1e3, 2) for x in per_rank_ms],
+                    "merge_us": round(merge_us, 2),
+                    "merge_gbs": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1)},
+    }
+    if not args.no_secondary and kind == dca.GQA:
+        line["secondary"] = secondary_mla(dca, wl, torch)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+
+
+def secondary_mla(dca, wl, torch, steps=20):
+    """MLA decode workload (64 x 67584, 128 heads, C = 8): rank-0 shard kernel MFMA
+    utilisation and HBM rate, and the 8-partial merge rate."""
+    w = wl.MLA_DECODE
+    inp = wl.make_inputs(w, device="cuda")
+    lens = w.seq_lens()
+    step, shard_ev, merge_ev, ws = run_step_fns(dca, w, inp, dca.MLA)
+    for _ in range(3):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    C = w.cp_size
+    shard_ms = [a.elapsed_time(b) for a, b in shard_ev]
+    dur = sum(shard_ms) / len(shard_ms) / 1e3
+    costs = [mla_launch_cost(w, lens, r) for r in range(C)]
+    byts = sum(c[0] for c in costs) / C
+    flops = sum(c[1] for c in costs) / C
+    merge_us = sum(a.elapsed_time(b) for a, b in merge_ev) / len(merge_ev) * 1e3
+    merge_bytes = (C + 1) * w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
+    del inp
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "mla_shard_avg_us": round(dur * 1e6, 2),
+            "mla_mfma_util": round(flops / dur / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mla_tflops": round(flops / dur / 1e12, 1),
+            "mla_hbm_gbs": round(byts / dur / 1e9, 1),
+            "mla_hbm_frac": round(byts / dur / 1e9 / HBM_PEAK_GBS, 4),
+            "mla_kv_tokens_per_s": round(sum(c[2] for c in costs) / C / dur, 1),
+            "merge8_us": round(merge_us, 2),
+            "merge8_gbs": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1)}
+
+
+if __name__ == "__main__":
+    main()

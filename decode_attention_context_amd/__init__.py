@@ -204,6 +204,9 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
         _check("dcp_attn_shard", st)
     else:
         ev0, ev1 = events
+        for ev in (ev0, ev1):
+            if not ev.cuda_event:       # torch creates the HIP event on its first record
+                ev.record(stream)
         st = lib.dcp_attn_shard_timed(ctypes.byref(desc), _ptr(q), _ptr(kv_pages),
                                       _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), batch,
                                       int(max_seq_len), rank, cp_size, interleave, float(scale),

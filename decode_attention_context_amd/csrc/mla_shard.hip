@@ -30,6 +30,13 @@
 //     so the online-softmax rescale is lane-local (and skipped when no max changed).
 #include "launch.h"
 
+#ifndef MLA_HT
+#define MLA_HT 1
+#endif
+#ifndef MLA_NW
+#define MLA_NW 4
+#endif
+
 namespace dcp {
 
 namespace {
@@ -51,10 +58,7 @@ constexpr int kRowChunks = kRowBytes / 16;   // 72
 constexpr int kTileBytes = kTile * kRowBytes;  // 73728
 constexpr int kKSteps = kDk / 32;            // 18
 constexpr int kDvTiles = kDv / 16;           // 32
-// Query heads per wave = 16 * kHeadTiles; the workgroup has 128 / that many waves.
-constexpr int kHeadTiles = 1;
-constexpr int kWaves = kHeads / (16 * kHeadTiles);
-constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;
+constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
 
 struct MlaKArgs {
   const uint16_t* q;
@@ -82,10 +86,20 @@ __device__ __forceinline__ u32x2 lds_tr16(const char DCP_LDS* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-__global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
+// HT = 16-head tiles per wave, NW = waves per workgroup.  A workgroup covers
+// 16 * HT * NW query heads; the 128 heads form kGroups = 128 / (16 HT NW) head groups,
+// each a workgroup of its own.  Workgroup ids are laid out so that every head group of one
+// work item lands on the same XCD (ids congruent mod 8) and is dispatched close in time, so
+// the groups' reads of the same latent tiles meet in that XCD's L2.
+template <int HT, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void mla_shard_kernel(MlaKArgs a) {
+  constexpr int kGroups = kHeads / (16 * HT * NW);
+  constexpr int kDmaPerWave = kTileBytes / 1024 / NW;
   __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes];
 
-  const int item = blockIdx.x;
+  const int blk = blockIdx.x;
+  const int hg = (blk / kXcds) % kGroups;
+  const int item = (blk / (kXcds * kGroups)) * kXcds + blk % kXcds;
   if (item >= a.header[1]) return;
   const int4 it = a.items[item];
   const int b = it.x, j0 = it.y, j1 = it.z;
@@ -95,7 +109,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const int w = threadIdx.x >> 6;
   const int g = lane >> 4;      // 16-lane group
   const int i16 = lane & 15;
-  const int head0 = 16 * kHeadTiles * w + i16;   // head of head tile ht: head0 + 16 ht
+  // head of head tile ht: head0 + 16 ht
+  const int head0 = 16 * HT * (NW * hg + w) + i16;
   const uint32_t B = (uint32_t)a.block_size;
   const int32_t* btb = a.bt + (size_t)b * a.max_blocks;
 
@@ -126,40 +141,44 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   // ---- HBM -> LDS copy of one tile (1 KiB per instruction, kDmaPerWave per wave)
   auto issue_tile = [&](char* buf, uint32_t row) {
     // An opaque copy of the lane id keeps the slot arithmetic below from being hoisted out
-    // of the tile loop (it is cheap to redo, and hoisted it would pin 2 * kDmaPerWave
-    // registers for the whole kernel).
+    // of the tile loop (cheap to redo; hoisted it would pin 2 * kDmaPerWave registers).
     int lane_o;
     asm volatile("v_mov_b32 %0, %1" : "=v"(lane_o) : "v"(lane));
+    uint32_t rr[kDmaPerWave];
+    int cc[kDmaPerWave];
 #pragma unroll
-    for (int k = 0; k < kDmaPerWave; ++k) {
-      const int blk = w * kDmaPerWave + k;
-      const int s = blk * 64 + lane_o;          // 16-B slot in the tile
+    for (int k = 0; k < kDmaPerWave; ++k) {   // every row-index shuffle first ...
+      const int s = (w * kDmaPerWave + k) * 64 + lane_o;   // 16-B slot in the tile
       const int r = s / kRowChunks;
-      const int c = (s - r * kRowChunks) ^ (r & 7);
-      const uint32_t rr = __shfl(row, r, 64);
-      const char* src = a.lat + (size_t)rr * kRowBytes + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (void DCP_LDS*)(buf + blk * 1024), 16, 0, 0);
+      cc[k] = (s - r * kRowChunks) ^ (r & 7);
+      rr[k] = __shfl(row, r, 64);
+    }
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {   // ... then the copies back to back
+      const char* src = a.lat + (size_t)rr[k] * kRowBytes + cc[k] * 16;
+      __builtin_amdgcn_global_load_lds(src, (void DCP_LDS*)(buf + (w * kDmaPerWave + k) * 1024),
+                                       16, 0, 0);
     }
   };
 
   // ---- query (B operand of S^T = K Q^T): dims 32 ks + 8 g .. + 8 of each head tile
-  bf16x8 qreg[kHeadTiles][kKSteps];
+  bf16x8 qreg[HT][kKSteps];
 #pragma unroll
-  for (int ht = 0; ht < kHeadTiles; ++ht) {
+  for (int ht = 0; ht < HT; ++ht) {
     const uint16_t* qrow = a.q + ((size_t)b * kHeads + head0 + 16 * ht) * kDk + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
       qreg[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
 
-  f4 acc[kHeadTiles][kDvTiles];
+  f4 acc[HT][kDvTiles];
 #pragma unroll
-  for (int ht = 0; ht < kHeadTiles; ++ht)
+  for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int i = 0; i < kDvTiles; ++i) acc[ht][i] = f4{0.f, 0.f, 0.f, 0.f};
-  float m[kHeadTiles], ls[kHeadTiles];
+  float m[HT], ls[HT];
 #pragma unroll
-  for (int ht = 0; ht < kHeadTiles; ++ht) {
+  for (int ht = 0; ht < HT; ++ht) {
     m[ht] = neg_inf();
     ls[ht] = 0.f;
   }
@@ -193,92 +212,118 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     }
     const char* buf = smem + (ti & 1) * kTileBytes;
 
+    // ---- scores of the whole tile: s[ht][nt][i] is token 16 nt + 4 g + i of head tile ht
+    f4 s[HT][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // scores of tokens 32 kb + [0, 16) (s[ht][0]) and 32 kb + [16, 32) (s[ht][1])
-      f4 s[kHeadTiles][2];
+    for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int ht = 0; ht < kHeadTiles; ++ht) s[ht][0] = s[ht][1] = f4{0.f, 0.f, 0.f, 0.f};
-      const char* bk0 = buf + (2 * kb) * 16 * kRowBytes;
-      const char* bk1 = bk0 + 16 * kRowBytes;
+      for (int nt = 0; nt < 4; ++nt) s[ht][nt] = f4{0.f, 0.f, 0.f, 0.f};
+    // K operands are read two k-steps ahead of the MFMAs that use them (3-slot ring), so
+    // every read has a full step of MFMAs to hide behind
+    bf16x8 kop[3][4];
+    auto kread = [&](int ks) {
+      const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(bk0 + o);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(bk1 + o);
+      for (int nt = 0; nt < 4; ++nt)
+        kop[ks % 3][nt] = *reinterpret_cast<const bf16x8*>(buf + nt * 16 * kRowBytes + o);
+    };
+    kread(0);
+    kread(1);
 #pragma unroll
-        for (int ht = 0; ht < kHeadTiles; ++ht) {
-          s[ht][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[ht][ks], s[ht][0], 0, 0, 0);
-          s[ht][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[ht][ks], s[ht][1], 0, 0, 0);
-        }
-        // keep the scheduler from hoisting every operand read (register pressure)
-        if (ks % 3 == 2) __builtin_amdgcn_sched_barrier(0);
-      }
-      // lane holds one head per tile; s[.][0][i] is token 32 kb + 4 g + i, s[.][1][i] is
-      // token 32 kb + 16 + 4 g + i
-      bf16x8 pb[kHeadTiles];
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + 2 < kKSteps) kread(ks + 2);
 #pragma unroll
-      for (int ht = 0; ht < kHeadTiles; ++ht) {
-        float x[8];
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = s[ht][0][i] * a.sl2;
-          x[4 + i] = s[ht][1][i] * a.sl2;
-        }
-        if (vm_cur != ~0ull) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (!((vm_cur >> (32 * kb + 4 * g + i)) & 1)) x[i] = neg_inf();
-            if (!((vm_cur >> (32 * kb + 16 + 4 * g + i)) & 1)) x[4 + i] = neg_inf();
-          }
-        }
-        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(m[ht], tmax);
-        if (__ballot(mn > m[ht]) != 0) {
-          const float alpha = mn > m[ht] ? __builtin_amdgcn_exp2f(m[ht] - mn) : 1.f;
-          ls[ht] *= alpha;
-#pragma unroll
-          for (int i = 0; i < kDvTiles; ++i) acc[ht][i] *= alpha;
-        }
-        m[ht] = mn;
-        const float msafe = mn == neg_inf() ? 0.f : mn;
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(x[i] - msafe);
-          ls[ht] += p[i];
-        }
-        u32x4 pw;
-        pw.x = pack_bf16x2(p[0], p[1]);
-        pw.y = pack_bf16x2(p[2], p[3]);
-        pw.z = pack_bf16x2(p[4], p[5]);
-        pw.w = pack_bf16x2(p[6], p[7]);
-        pb[ht] = __builtin_bit_cast(bf16x8, pw);
-      }
+        for (int ht = 0; ht < HT; ++ht)
+          s[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % 3][nt], qreg[ht][ks],
+                                                               s[ht][nt], 0, 0, 0);
+      // one scheduling region per k-step
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
-      const char* bv0 = buf + (32 * kb) * kRowBytes;
-      const char* bv1 = bv0 + 16 * kRowBytes;
+    // ---- online softmax over the tile; P as the bf16 B operand of O^T += V^T P^T
+    // k-block kb covers tokens 32 kb + [0, 32): lane slots 8 g .. 8 g + 7 hold tokens
+    // 32 kb + 4 g + [0, 4) and 32 kb + 16 + 4 g + [0, 4), the order of the V^T reads below.
+    bf16x8 pb[HT][2];
 #pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt) {
-        const int o = offv[dt & 3] + 128 * (dt >> 2);
-        const u32x2 v0 = lds_tr16((const char DCP_LDS*)(bv0 + o));
-        const u32x2 v1 = lds_tr16((const char DCP_LDS*)(bv1 + o));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
+    for (int ht = 0; ht < HT; ++ht) {
+      float x[16];
 #pragma unroll
-        for (int ht = 0; ht < kHeadTiles; ++ht)
-          acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ht], acc[ht][dt], 0, 0, 0);
-        if (dt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * nt + i] = s[ht][nt][i] * a.sl2;
+      if (vm_cur != ~0ull) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((vm_cur >> (16 * nt + 4 * g + i)) & 1)) x[4 * nt + i] = neg_inf();
       }
+      float tmax = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m[ht], tmax);
+      if (__ballot(mn > m[ht]) != 0) {
+        const float alpha = mn > m[ht] ? __builtin_amdgcn_exp2f(m[ht] - mn) : 1.f;
+        ls[ht] *= alpha;
+#pragma unroll
+        for (int i = 0; i < kDvTiles; ++i) acc[ht][i] *= alpha;
+      }
+      m[ht] = mn;
+      const float msafe = mn == neg_inf() ? 0.f : mn;
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(x[i] - msafe);
+        ls[ht] += p[i];
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float* p0 = p + 8 * kb;        // token tile 2 kb
+        const float* p1 = p + 8 * kb + 4;    // token tile 2 kb + 1
+        u32x4 pw;
+        pw.x = pack_bf16x2(p0[0], p0[1]);
+        pw.y = pack_bf16x2(p0[2], p0[3]);
+        pw.z = pack_bf16x2(p1[0], p1[1]);
+        pw.w = pack_bf16x2(p1[2], p1[3]);
+        pb[ht][kb] = __builtin_bit_cast(bf16x8, pw);
+      }
+    }
+
+    // ---- O^T += V^T P^T (V^T operands of dim tile dt+1 read during the MFMAs of dt)
+    auto vop = [&](int dt, int kb) -> bf16x8 {
+      const int o = offv[dt & 3] + 128 * (dt >> 2);
+      const char* bv = buf + (32 * kb) * kRowBytes;
+      const u32x2 v0 = lds_tr16((const char DCP_LDS*)(bv + o));
+      const u32x2 v1 = lds_tr16((const char DCP_LDS*)(bv + 16 * kRowBytes + o));
+      return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
+    };
+    bf16x8 va[2][2];
+    va[0][0] = vop(0, 0);
+    va[0][1] = vop(0, 1);
+#pragma unroll
+    for (int dt = 0; dt < kDvTiles; ++dt) {
+      if (dt + 1 < kDvTiles) {
+        va[(dt + 1) & 1][0] = vop(dt + 1, 0);
+        va[(dt + 1) & 1][1] = vop(dt + 1, 1);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt & 1][kb], pb[ht][kb],
+                                                                acc[ht][dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     vm_cur = vm_next;
   }
 
   // ---- finalize: lane holds dims 16 dt + 4 g + [0, 4) of head head0 + 16 ht
 #pragma unroll
-  for (int ht = 0; ht < kHeadTiles; ++ht) {
+  for (int ht = 0; ht < HT; ++ht) {
     float lt = ls[ht] + __shfl_xor(ls[ht], 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -297,6 +342,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     }
   }
 }
+
+constexpr int kHT = MLA_HT;
+constexpr int kNW = MLA_NW;
+constexpr int kGroupsUsed = kHeads / (16 * kHT * kNW);
 
 }  // namespace
 
@@ -320,7 +369,9 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   k.items = ws.items;
   k.plse = ws.plse;
   k.po = ws.po;
-  hipLaunchKernelGGL(mla_shard_kernel, dim3((unsigned)max_items), dim3(kWaves * 64), 0, stream, k);
+  const int64_t groups8 = (max_items + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((mla_shard_kernel<kHT, kNW>), dim3((unsigned)(groups8 * kXcds * kGroupsUsed)),
+                     dim3(kNW * 64), 0, stream, k);
   return hipGetLastError();
 }
 
