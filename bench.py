@@ -194,10 +194,18 @@ def main():
         n = 1 << 30
         x = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
         for _ in range(5):
             y.copy_(x)
+        ev[1].record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 5}))
+        ms = ev[0].elapsed_time(ev[1]) / 5
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 8,
+                          "copy_us": round(ms * 1e3, 2),
+                          "copy_gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
         return
 
     dca.load()

@@ -68,6 +68,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// DPP lane permutations inside each 16-lane row (gfx9 encodings).
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15 - i within each 16 lanes
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), kCtrl,
+                                                    0xF, 0xF, false));
+}
+
+// Max / sum over all 64 lanes without LDS: a DPP butterfly inside each 16-lane row, then
+// the four row results are read into scalars.  The result is wave-uniform.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  const int vi = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(vi, 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(vi, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(vi, 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(vi, 48))));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  const int vi = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(vi, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(vi, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(vi, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(vi, 48)));
+}
+
 // float -> bf16 bits, round to nearest even (NaN -> quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -59,15 +59,16 @@ struct Plan {
 };
 
 // Work items: the planner splits the shard's tokens into about `target` items (never more
-// than target + batch), enough to cover every CU several times (GQA: one wave per item and
-// KV head; MLA: one 8-wave workgroup per item).
+// than target + batch), enough to cover every CU a few times (GQA: one 4-wave workgroup per
+// item and KV head; MLA: two 4-wave workgroups, one per half of the heads, per item).
 bool make_plan(const dcp_attn_desc* d, int batch, Plan* p) {
   const int cus = device_cus();
   if (cus <= 0) return false;
   if (d->kind == DCP_GQA) {
     p->tile = dcp::kGqaTile;
-    p->target = std::max<int64_t>(1, (int64_t)cus * 8 / d->num_kv_heads);
-    p->min_chunk = dcp::kGqaTile;
+    // two resident 4-wave workgroups per CU, about two rounds of them
+    p->target = std::max<int64_t>(1, (int64_t)cus * 4 / d->num_kv_heads);
+    p->min_chunk = 4 * dcp::kGqaTile;
   } else {
     p->tile = dcp::kMlaTile;
     p->target = (int64_t)cus;

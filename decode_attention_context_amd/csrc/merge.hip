@@ -8,9 +8,10 @@
 // which is the attention over the union of the token sets.  The same row merge combines
 // the split-K partials of one shard call, whose items cover disjoint local token ranges.
 //
-// One wave merges one (request, head) row: the n lse values are wave-uniform scalar
-// loads, then each lane streams VEC consecutive floats of every partial row (all partial
-// loads of a chunk are issued before they are summed).  The kernel is HBM-bound.
+// One wave merges one (request, head) row: the n lse values are loaded one per lane and
+// reduced with DPP (no serial chain of loads), then each lane streams VEC consecutive
+// floats of every partial row, eight partials' loads in flight at a time.  Empty partials
+// (weight 0) are never read.  The kernel is HBM-bound.
 #include "launch.h"
 
 namespace dcp {
@@ -34,6 +35,8 @@ __device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename 
 }
 
 // Merge `n` partial rows o_base[r * o_stride .. + dv) with lse l_base[r * l_stride].
+// The lse values are spread over the lanes (64 per pass) and reduced with DPP, so the row
+// costs one round trip for them; the partial rows are then streamed 8 at a time.
 template <int VEC>
 __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int64_t o_stride,
                                           const float* __restrict__ l_base, int64_t l_stride,
@@ -41,11 +44,14 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
                                           uint16_t* __restrict__ out_bf16,
                                           float* __restrict__ lse_out, int lane) {
   using V = typename VecT<VEC>::T;
-  float m = neg_inf();
-  for (int r = 0; r < n; ++r) {
+  auto lse_at = [&](int r) -> float {
+    if (r >= n) return neg_inf();
     const float x = l_base[r * l_stride];
-    if (__builtin_isfinite(x)) m = fmaxf(m, x);
-  }
+    return __builtin_isfinite(x) ? x : neg_inf();
+  };
+  float m = neg_inf();
+  for (int r0 = 0; r0 < n; r0 += 64) m = fmaxf(m, lse_at(r0 + lane));
+  m = wave_max_dpp(m);
   if (m == neg_inf()) {
     // every partial is empty
     for (int d = lane * VEC; d < dv; d += 64 * VEC) {
@@ -59,34 +65,39 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
     return;
   }
   const float m2 = m * kLog2e;
-  float wsum = 0.f;
-  for (int r = 0; r < n; ++r) {
-    const float x = l_base[r * l_stride];
-    wsum += __builtin_isfinite(x) ? exp2f(fmaf(x, kLog2e, -m2)) : 0.f;
+  float wpart = 0.f;
+  for (int r0 = 0; r0 < n; r0 += 64) {
+    const float x = lse_at(r0 + lane);
+    wpart += x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
   }
-  const float inv = 1.f / wsum;
+  const float inv = 1.f / wave_sum_dpp(wpart);
   for (int d = lane * VEC; d < dv; d += 64 * VEC) {
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    int r = 0;
-    for (; r + 8 <= n; r += 8) {
-      V v[8];
-      float w[8];
+    for (int r0 = 0; r0 < n; r0 += 64) {
+      const float x = lse_at(r0 + lane);
+      const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
+      const int nr = n - r0 < 64 ? n - r0 : 64;
+      int r = 0;
+      for (; r + 8 <= nr; r += 8) {
+        V v[8];
+        float wv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float x = l_base[(r + u) * l_stride];
-        w[u] = __builtin_isfinite(x) ? exp2f(fmaf(x, kLog2e, -m2)) : 0.f;
-        if (w[u] != 0.f) v[u] = *reinterpret_cast<const V*>(o_base + (r + u) * o_stride + d);
+        for (int u = 0; u < 8; ++u) {
+          wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r + u));
+          if (wv[u] != 0.f)
+            v[u] = *reinterpret_cast<const V*>(o_base + (int64_t)(r0 + r + u) * o_stride + d);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (wv[u] != 0.f) vfma<VEC>(acc, wv[u], v[u]);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (w[u] != 0.f) vfma<VEC>(acc, w[u], v[u]);
-    }
-    for (; r < n; ++r) {
-      const float x = l_base[r * l_stride];
-      const float w = __builtin_isfinite(x) ? exp2f(fmaf(x, kLog2e, -m2)) : 0.f;
-      if (w != 0.f) vfma<VEC>(acc, w, *reinterpret_cast<const V*>(o_base + r * o_stride + d));
+      for (; r < nr; ++r) {
+        const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r));
+        if (wr != 0.f)
+          vfma<VEC>(acc, wr, *reinterpret_cast<const V*>(o_base + (int64_t)(r0 + r) * o_stride + d));
+      }
     }
     if (out_f32) {
       V o;
@@ -99,7 +110,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
       for (int i = 0; i < VEC; ++i) out_bf16[d + i] = (uint16_t)f32_to_bf16_rne(acc[i] * inv);
     }
   }
-  if (lse_out && lane == 0) *lse_out = (m2 + log2f(wsum)) * kLn2;
+  if (lse_out && lane == 0) *lse_out = (m2 - __log2f(inv)) * kLn2;
 }
 
 constexpr int kRowsPerBlock = 4;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4;      // 16-lane group
   const int i16 = lane & 15;
   // head of head tile ht: head0 + 16 ht
