@@ -70,8 +70,9 @@ bool make_plan(const dcp_attn_desc* d, int batch, Plan* p) {
     p->target = std::max<int64_t>(1, (int64_t)cus * 4 / d->num_kv_heads);
     p->min_chunk = 4 * dcp::kGqaTile;
   } else {
+    // two head-group workgroups per item, one resident workgroup per CU (144 KiB of LDS)
     p->tile = dcp::kMlaTile;
-    p->target = (int64_t)cus;
+    p->target = std::max<int64_t>(1, (int64_t)cus / 2);
     p->min_chunk = 4 * dcp::kMlaTile;
   }
   p->max_items = (int64_t)batch + p->target;

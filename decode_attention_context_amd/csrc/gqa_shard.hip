@@ -140,6 +140,8 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     return __ballot(ok);
   };
   // ---- HBM -> LDS copy of the K and V rows of one tile (this wave's share)
+  char* lds_base = reinterpret_cast<char*>(&kv[0][0][0]);
+  asm volatile("" : "+v"(lds_base));
   auto issue_tile = [&](int buf, uint32_t row) {
     const uint32_t row0 = __builtin_amdgcn_readfirstlane(row);
     const bool contig = __ballot(row == row0 + (uint32_t)lane) == ~0ull;
@@ -152,10 +154,14 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
       const size_t rb = (size_t)rr * kRowBytes;
       // K chunks XOR-swizzled (read transposed below), V rows stored as they are (read
       // row-wise: consecutive lanes hit consecutive banks)
-      __builtin_amdgcn_global_load_lds(a.kp + rb + ((pc ^ (r & 15)) * 16),
-                                       (void DCP_LDS*)(&kv[buf][0][blk * 64]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.vp + rb + pc * 16,
-                                       (void DCP_LDS*)(&kv[buf][1][blk * 64]), 16, 0, 0);
+      // the destination is formed from an opaque byte base so that the compiler does not
+      // treat the copy as aliasing the tile being read (which would make every read wait
+      // for the copy of the next tile); the loop's own wait + barrier order the buffers
+      char* kd = lds_base + ((buf * 2 + 0) * kTileBytes + blk * 1024);
+      char* vd = lds_base + ((buf * 2 + 1) * kTileBytes + blk * 1024);
+      __builtin_amdgcn_global_load_lds(a.kp + rb + ((pc ^ (r & 15)) * 16), (void DCP_LDS*)kd, 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(a.vp + rb + pc * 16, (void DCP_LDS*)vd, 16, 0, 0);
     }
   };
 

@@ -57,6 +57,6 @@ hipError_t launch_shard_slots(const int32_t* block_table, const int32_t* seq_len
 
 // Tokens per tile of each shard kernel (work items are whole multiples of it).
 constexpr int kGqaTile = 64;
-constexpr int kMlaTile = 64;
+constexpr int kMlaTile = 32;
 
 }  // namespace dcp

@@ -48,17 +48,21 @@ typedef __attribute__((ext_vector_type(4))) float f4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 #define DCP_LDS __attribute__((address_space(3)))
+#define DCP_CONST __attribute__((address_space(4)))
 
 constexpr int kHeads = 128;
 constexpr int kDk = 576;
 constexpr int kDv = 512;
-constexpr int kTile = kMlaTile;              // 64 tokens
+constexpr int kTile = kMlaTile;              // 32 tokens per tile
+constexpr int kNBuf = 4;                     // LDS tile ring: one computed, three in flight
 constexpr int kRowBytes = kDk * 2;           // 1152
 constexpr int kRowChunks = kRowBytes / 16;   // 72
-constexpr int kTileBytes = kTile * kRowBytes;  // 73728
+constexpr int kTileBytes = kTile * kRowBytes;  // 36 KiB
 constexpr int kKSteps = kDk / 32;            // 18
 constexpr int kDvTiles = kDv / 16;           // 32
 constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr float kRescaleSlack = 8.f;          // see the online softmax below
+constexpr int kAhead = 6;                    // LDS operand prefetch distance (MFMA steps)
 
 struct MlaKArgs {
   const uint16_t* q;
@@ -86,6 +90,12 @@ __device__ __forceinline__ u32x2 lds_tr16(const char DCP_LDS* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((kVm & 0xF) | ((kVm >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // HT = 16-head tiles per wave, NW = waves per workgroup.  A workgroup covers
 // 16 * HT * NW query heads; the 128 heads form kGroups = 128 / (16 HT NW) head groups,
 // each a workgroup of its own.  Workgroup ids are laid out so that every head group of one
@@ -95,7 +105,7 @@ template <int HT, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   constexpr int kGroups = kHeads / (16 * HT * NW);
   constexpr int kDmaPerWave = kTileBytes / 1024 / NW;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kTileBytes];
 
   const int blk = blockIdx.x;
   const int hg = (blk / kXcds) % kGroups;
@@ -113,52 +123,93 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const int head0 = 16 * HT * (NW * hg + w) + i16;
   const uint32_t B = (uint32_t)a.block_size;
   const int32_t* btb = a.bt + (size_t)b * a.max_blocks;
+  // Contiguous tiles: when the interleave and the block size are multiples of the tile, the
+  // 32 tokens of a tile are consecutive positions inside one cache page, so one scalar
+  // block-table read locates the whole tile.  Otherwise every token is walked by a lane.
+  const bool fast = (a.interleave % kTile) == 0 && (a.block_size % kTile) == 0;
 
-  // ---- block-table walk: cache row of local token tj + lane
-  auto page_of = [&](int tj) -> int32_t {
-    const int j = tj + lane;
-    if (j >= j1) return 0;
-    const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-    return btb[t / B];
-  };
-  auto row_of = [&](int tj, int32_t pg, uint32_t& row) -> uint64_t {
-    const int j = tj + lane;
-    bool ok = j < j1;
-    bool bad = false;
-    row = 0;
-    if (ok) {
-      if (pg < 0 || (uint32_t)pg >= a.num_blocks) {
-        ok = false;
-        bad = true;
-      } else {
+  // The copies write through an opaque base, the tile reads go through the array itself:
+  // otherwise the compiler takes every read as aliasing the copies still in flight and
+  // waits for all of them (the ring's own counter waits and barriers order the buffers).
+  char DCP_LDS* lds_dma = (char DCP_LDS*)smem;
+  asm volatile("" : "+v"(lds_dma));
+  const char DCP_LDS* lds = (const char DCP_LDS*)smem;
+  // the block table through the constant address space: scalar loads, which do not count
+  // against the vector-memory counter the copy ring is paced with
+  const int32_t DCP_CONST* btc = reinterpret_cast<const int32_t DCP_CONST*>(
+      reinterpret_cast<uintptr_t>(btb));
+
+  // Per-lane copy slots (loop invariant): 16-B slot (w * kDmaPerWave + k) * 64 + lane of a
+  // tile holds chunk (s mod 72) ^ (row & 7) of tile row s / 72.
+  uint32_t slot_off[kDmaPerWave], slot_col[kDmaPerWave];
+  int slot_row[kDmaPerWave];
+#pragma unroll
+  for (int k = 0; k < kDmaPerWave; ++k) {
+    const int sl = (w * kDmaPerWave + k) * 64 + lane;
+    const int r = sl / kRowChunks;
+    slot_row[k] = r;
+    slot_col[k] = (uint32_t)(((sl - r * kRowChunks) ^ (r & 7)) * 16);
+    slot_off[k] = (uint32_t)r * kRowBytes + slot_col[k];
+  }
+
+  // ---- one tile's HBM -> LDS copy (kDmaPerWave instructions of 1 KiB per wave); returns
+  // the ballot of valid rows.  Chunk c of row r lands at byte 16 * (72 r + (c ^ (r & 7))).
+  auto issue_tile = [&](int ti) -> uint64_t {
+    const int tj = j0 + ti * kTile;
+    char DCP_LDS* buf = lds_dma + (ti % kNBuf) * kTileBytes;
+    uint32_t row0 = 0;
+    uint32_t lrow = 0;              // slow path: this lane's row (lane < 32)
+    uint64_t vm;
+    if (fast) {
+      const uint32_t t0 = dcp_walk_global_pos((uint32_t)tj, a.rank, a.cp, a.interleave);
+      const uint32_t lp = t0 / B;
+      const int32_t pg = btc[lp];
+      const int nvalid = min(kTile, j1 - tj);
+      const bool ok = pg >= 0 && (uint32_t)pg < a.num_blocks;
+      if (!ok && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
+      row0 = ok ? (uint32_t)pg * B + (t0 - lp * B) : 0u;
+      vm = ok ? (nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1)) : 0ull;
+    } else {
+      const int j = tj + lane;
+      bool ok = lane < kTile && j < j1;
+      bool bad = false;
+      if (ok) {
         const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-        row = (uint32_t)pg * B + t % B;
+        const uint32_t lp = t / B;
+        const int32_t pg = btb[lp];
+        if (pg < 0 || (uint32_t)pg >= a.num_blocks) {
+          ok = false;
+          bad = true;
+        } else {
+          lrow = (uint32_t)pg * B + (t - lp * B);
+        }
+      }
+      if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
+      vm = __ballot(ok);
+    }
+    if (fast) {
+      // rows row0 .. row0 + nrows - 1 are consecutive: one uniform base plus the lane's
+      // precomputed slot offset; slots of rows past the valid prefix re-read row 0 (masked)
+      const int nrows = vm ? 64 - __builtin_clzll(vm) : 0;   // valid rows form a prefix
+      const char* base = a.lat + (size_t)row0 * kRowBytes;
+      const uint32_t lim = (uint32_t)nrows * kRowBytes;
+#pragma unroll
+      for (int k = 0; k < kDmaPerWave; ++k) {
+        const uint32_t o = slot_off[k] < lim ? slot_off[k] : slot_col[k];
+        __builtin_amdgcn_global_load_lds(base + o,
+                                         (void DCP_LDS*)(buf + (w * kDmaPerWave + k) * 1024), 16,
+                                         0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kDmaPerWave; ++k) {
+        const uint32_t rr = __shfl(lrow, slot_row[k], 64);
+        const char* src = a.lat + (size_t)rr * kRowBytes + slot_col[k];
+        __builtin_amdgcn_global_load_lds(src, (void DCP_LDS*)(buf + (w * kDmaPerWave + k) * 1024),
+                                         16, 0, 0);
       }
     }
-    if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
-    return __ballot(ok);
-  };
-  // ---- HBM -> LDS copy of one tile (1 KiB per instruction, kDmaPerWave per wave)
-  auto issue_tile = [&](char* buf, uint32_t row) {
-    // An opaque copy of the lane id keeps the slot arithmetic below from being hoisted out
-    // of the tile loop (cheap to redo; hoisted it would pin 2 * kDmaPerWave registers).
-    int lane_o;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(lane_o) : "v"(lane));
-    uint32_t rr[kDmaPerWave];
-    int cc[kDmaPerWave];
-#pragma unroll
-    for (int k = 0; k < kDmaPerWave; ++k) {   // every row-index shuffle first ...
-      const int s = (w * kDmaPerWave + k) * 64 + lane_o;   // 16-B slot in the tile
-      const int r = s / kRowChunks;
-      cc[k] = (s - r * kRowChunks) ^ (r & 7);
-      rr[k] = __shfl(row, r, 64);
-    }
-#pragma unroll
-    for (int k = 0; k < kDmaPerWave; ++k) {   // ... then the copies back to back
-      const char* src = a.lat + (size_t)rr[k] * kRowBytes + cc[k] * 16;
-      __builtin_amdgcn_global_load_lds(src, (void DCP_LDS*)(buf + (w * kDmaPerWave + k) * 1024),
-                                       16, 0, 0);
-    }
+    return vm;
   };
 
   // ---- query (B operand of S^T = K Q^T): dims 32 ks + 8 g .. + 8 of each head tile
@@ -170,6 +221,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     for (int ks = 0; ks < kKSteps; ++ks)
       qreg[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
+  // the query must have landed before the copy ring starts: inside the ring the vector
+  // memory counter only paces tile copies
+  wait_vmcnt<0>();
 
   f4 acc[HT][kDvTiles];
 #pragma unroll
@@ -183,7 +237,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     ls[ht] = 0.f;
   }
 
-  // per-lane LDS offsets (chunk c of row r sits at byte 16 * (72 r + (c ^ (r & 7))))
+  // per-lane LDS offsets inside a tile
   const int xk = i16 & 7;
   const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
   const int offk1 = i16 * kRowBytes + 16 * ((4 + g) ^ xk);
@@ -195,130 +249,124 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   for (int u = 0; u < 4; ++u) offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8;
 
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  uint32_t row;
-  uint64_t vm_cur = row_of(j0, page_of(j0), row);
-  issue_tile(smem, row);
-  int32_t pg_next = ntiles > 1 ? page_of(j0 + kTile) : 0;
+  // prologue: three tiles in flight
+  uint64_t vm0 = issue_tile(0);
+  uint64_t vm1 = ntiles > 1 ? issue_tile(1) : 0ull;
+  uint64_t vm2 = ntiles > 2 ? issue_tile(2) : 0ull;
 
   for (int ti = 0; ti < ntiles; ++ti) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int tj = j0 + ti * kTile;
-    uint64_t vm_next = 0;
-    if (ti + 1 < ntiles) {
-      vm_next = row_of(tj + kTile, pg_next, row);
-      issue_tile(smem + ((ti + 1) & 1) * kTileBytes, row);
-      if (ti + 2 < ntiles) pg_next = page_of(tj + 2 * kTile);
-    }
-    const char* buf = smem + (ti & 1) * kTileBytes;
+    // wait for this wave's copies of tile ti (those of tiles ti+1, ti+2 may stay in flight)
+    const int pend = min(2, ntiles - 1 - ti);
+    if (!fast || pend == 0) wait_vmcnt<0>();
+    else if (pend == 1) wait_vmcnt<kDmaPerWave>();
+    else wait_vmcnt<2 * kDmaPerWave>();
+    // Every wave's copies of tile ti have landed and tile ti-1 is free.  A bare barrier:
+    // the fence of __syncthreads would also wait for the copies still in flight.
+    asm volatile("s_barrier" ::: "memory");
+    uint64_t vm3 = 0ull;
+    if (ti + 3 < ntiles) vm3 = issue_tile(ti + 3);
+    const char DCP_LDS* buf = lds + (ti % kNBuf) * kTileBytes;
 
-    // ---- scores of the whole tile: s[ht][nt][i] is token 16 nt + 4 g + i of head tile ht
-    f4 s[HT][4];
+    // ---- scores: s[ht][nt][i] is token 16 nt + 4 g + i of head tile ht
+    f4 s[HT][2];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) s[ht][nt] = f4{0.f, 0.f, 0.f, 0.f};
-    // K operands are read two k-steps ahead of the MFMAs that use them (3-slot ring), so
-    // every read has a full step of MFMAs to hide behind
-    bf16x8 kop[3][4];
+    for (int ht = 0; ht < HT; ++ht) s[ht][0] = s[ht][1] = f4{0.f, 0.f, 0.f, 0.f};
+    // K operands are read kAhead k-steps before the MFMAs that use them: with one wave per
+    // SIMD, a step's two MFMAs (32 cycles) cannot cover one LDS round trip by themselves
+    bf16x8 kop[kAhead + 1][2];
     auto kread = [&](int ks) {
       const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        kop[ks % 3][nt] = *reinterpret_cast<const bf16x8*>(buf + nt * 16 * kRowBytes + o);
+      for (int nt = 0; nt < 2; ++nt)
+        kop[ks % (kAhead + 1)][nt] =
+            *reinterpret_cast<const bf16x8 DCP_LDS*>(buf + nt * 16 * kRowBytes + o);
     };
-    kread(0);
-    kread(1);
+#pragma unroll
+    for (int ks = 0; ks < kAhead; ++ks) kread(ks);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      if (ks + 2 < kKSteps) kread(ks + 2);
+      if (ks + kAhead < kKSteps) kread(ks + kAhead);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
-          s[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % 3][nt], qreg[ht][ks],
-                                                               s[ht][nt], 0, 0, 0);
-      // one scheduling region per k-step
-      __builtin_amdgcn_sched_barrier(0);
+          s[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][nt],
+                                                               qreg[ht][ks], s[ht][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);   // one scheduling region per k-step
     }
 
-    // ---- online softmax over the tile; P as the bf16 B operand of O^T += V^T P^T
-    // k-block kb covers tokens 32 kb + [0, 32): lane slots 8 g .. 8 g + 7 hold tokens
-    // 32 kb + 4 g + [0, 4) and 32 kb + 16 + 4 g + [0, 4), the order of the V^T reads below.
-    bf16x8 pb[HT][2];
+    // ---- online softmax; P (bf16) as the B operand of O^T += V^T P^T, whose k slots
+    // 8 g .. 8 g + 7 are tokens 4 g + [0, 4) and 16 + 4 g + [0, 4)
+    bf16x8 pb[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      float x[16];
+      float x[8];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * nt + i] = s[ht][nt][i] * a.sl2;
-      if (vm_cur != ~0ull) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!((vm_cur >> (16 * nt + 4 * g + i)) & 1)) x[4 * nt + i] = neg_inf();
+      for (int i = 0; i < 4; ++i) {
+        x[i] = s[ht][0][i] * a.sl2;
+        x[4 + i] = s[ht][1][i] * a.sl2;
       }
-      float tmax = x[0];
+      if (vm0 != 0xffffffffull) {
 #pragma unroll
-      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
+        for (int i = 0; i < 4; ++i) {
+          if (!((vm0 >> (4 * g + i)) & 1)) x[i] = neg_inf();
+          if (!((vm0 >> (16 + 4 * g + i)) & 1)) x[4 + i] = neg_inf();
+        }
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m[ht], tmax);
-      if (__ballot(mn > m[ht]) != 0) {
-        const float alpha = mn > m[ht] ? __builtin_amdgcn_exp2f(m[ht] - mn) : 1.f;
+      // The reference max moves only when a head's tile max exceeds it by more than
+      // kRescaleSlack (log2 units): weights stay below 2^kRescaleSlack, exactly
+      // representable in bf16/fp32, and the 128-register rescale of the accumulator runs a
+      // handful of times per item instead of on most tiles.
+      const bool up = tmax > m[ht] + kRescaleSlack;
+      const float mn = up ? tmax : m[ht];
+      if (__ballot(up) != 0) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(m[ht] - mn) : 1.f;
         ls[ht] *= alpha;
 #pragma unroll
         for (int i = 0; i < kDvTiles; ++i) acc[ht][i] *= alpha;
       }
       m[ht] = mn;
       const float msafe = mn == neg_inf() ? 0.f : mn;
-      float p[16];
+      float p[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 8; ++i) {
         p[i] = __builtin_amdgcn_exp2f(x[i] - msafe);
         ls[ht] += p[i];
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const float* p0 = p + 8 * kb;        // token tile 2 kb
-        const float* p1 = p + 8 * kb + 4;    // token tile 2 kb + 1
-        u32x4 pw;
-        pw.x = pack_bf16x2(p0[0], p0[1]);
-        pw.y = pack_bf16x2(p0[2], p0[3]);
-        pw.z = pack_bf16x2(p1[0], p1[1]);
-        pw.w = pack_bf16x2(p1[2], p1[3]);
-        pb[ht][kb] = __builtin_bit_cast(bf16x8, pw);
-      }
+      u32x4 pw;
+      pw.x = pack_bf16x2(p[0], p[1]);
+      pw.y = pack_bf16x2(p[2], p[3]);
+      pw.z = pack_bf16x2(p[4], p[5]);
+      pw.w = pack_bf16x2(p[6], p[7]);
+      pb[ht] = __builtin_bit_cast(bf16x8, pw);
     }
 
-    // ---- O^T += V^T P^T (V^T operands of dim tile dt+1 read during the MFMAs of dt)
-    auto vop = [&](int dt, int kb) -> bf16x8 {
+    // ---- O^T += V^T P^T (V^T operands read kAhead dim tiles ahead)
+    auto vop = [&](int dt) -> bf16x8 {
       const int o = offv[dt & 3] + 128 * (dt >> 2);
-      const char* bv = buf + (32 * kb) * kRowBytes;
-      const u32x2 v0 = lds_tr16((const char DCP_LDS*)(bv + o));
-      const u32x2 v1 = lds_tr16((const char DCP_LDS*)(bv + 16 * kRowBytes + o));
+      const u32x2 v0 = lds_tr16(buf + o);
+      const u32x2 v1 = lds_tr16(buf + 16 * kRowBytes + o);
       return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
     };
-    bf16x8 va[2][2];
-    va[0][0] = vop(0, 0);
-    va[0][1] = vop(0, 1);
+    bf16x8 va[kAhead + 1];
+#pragma unroll
+    for (int dt = 0; dt < kAhead; ++dt) va[dt] = vop(dt);
 #pragma unroll
     for (int dt = 0; dt < kDvTiles; ++dt) {
-      if (dt + 1 < kDvTiles) {
-        va[(dt + 1) & 1][0] = vop(dt + 1, 0);
-        va[(dt + 1) & 1][1] = vop(dt + 1, 1);
-      }
+      if (dt + kAhead < kDvTiles) va[(dt + kAhead) % (kAhead + 1)] = vop(dt + kAhead);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt & 1][kb], pb[ht][kb],
-                                                                acc[ht][dt], 0, 0, 0);
+      for (int ht = 0; ht < HT; ++ht)
+        acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt % (kAhead + 1)], pb[ht],
+                                                              acc[ht][dt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    vm_cur = vm_next;
+    vm0 = vm1;
+    vm1 = vm2;
+    vm2 = vm3;
   }
 
   // ---- finalize: lane holds dims 16 dt + 4 g + [0, 4) of head head0 + 16 ht
