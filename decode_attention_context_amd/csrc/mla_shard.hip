@@ -257,83 +257,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   float negm = 0.f;      // -m, or 0 while m is -inf
   float ls = 0.f;        // this lane's share of the running sum of weights
 
-  // per-lane LDS offsets inside a tile
-  const int xk = i16 & 7;
-  const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
-  const int offk1 = i16 * kRowBytes + 16 * ((4 + g) ^ xk);
-  const int rv = 4 * g + (i16 >> 2);
-  const int xv = rv & 7;
-  const int qv = (i16 >> 1) & 1;
-  int offv[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8;
-
-  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  // prologue: three tiles in flight
-  uint64_t vm0 = issue_tile(0);
-  uint64_t vm1 = ntiles > 1 ? issue_tile(1) : 0ull;
-  uint64_t vm2 = ntiles > 2 ? issue_tile(2) : 0ull;
-  uint64_t vm3 = 0ull;
-
-  // scores of the current tile: x[i] is token 4 g + i, x[4 + i] token 16 + 4 g + i
-  float x[8];
-  float tmax = neg_inf();   // tile max (log2 units) of this lane's head
-  const char DCP_LDS* buf = lds;
-
-  // ---- front half of tile ti: wait for it, start tile ti + 3, scores and their max
-  auto front = [&](int ti) {
-    // wait for this wave's copies of tile ti (those of tiles ti+1, ti+2 may stay in flight)
-    const int pend = min(2, ntiles - 1 - ti);
-    if (!kFast || pend == 0) wait_vmcnt<0>();
-    else if (pend == 1) wait_vmcnt<kDmaPerWave>();
-    else wait_vmcnt<2 * kDmaPerWave>();
-    // Every wave's copies of tile ti have landed and tile ti-1 is free.  A bare barrier:
-    // the fence of __syncthreads would also wait for the copies still in flight.
-    asm volatile("s_barrier" ::: "memory");
-    vm3 = ti + 3 < ntiles ? issue_tile(ti + 3) : 0ull;
-    buf = lds + (ti % kNBuf) * kTileBytes;
-
-    f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    // K operands are read kAhead k-steps before the MFMAs that use them: with one wave per
-    // SIMD, a step's two MFMAs (32 cycles) cannot cover one LDS round trip by themselves
-    bf16x8 kop[kAhead + 1][2];
-    auto kread = [&](int ks) {
-      const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
-      kop[ks % (kAhead + 1)][0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(buf + o);
-      kop[ks % (kAhead + 1)][1] =
-          *reinterpret_cast<const bf16x8 DCP_LDS*>(buf + 16 * kRowBytes + o);
-    };
-#pragma unroll
-    for (int ks = 0; ks < kAhead; ++ks) kread(ks);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      if (ks + kAhead < kKSteps) kread(ks + kAhead);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][0], qreg[ks], s0, 0,
-                                                   0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][1], qreg[ks], s1, 0,
-                                                   0, 0);
-      __builtin_amdgcn_sched_barrier(0);   // one scheduling region per k-step
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = s0[i];
-      x[4 + i] = s1[i];
-    }
-    if (vm0 != 0xffffffffull) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!((vm0 >> (4 * g + i)) & 1)) x[i] = neg_inf();
-        if (!((vm0 >> (16 + 4 * g + i)) & 1)) x[4 + i] = neg_inf();
-      }
-    }
-    float t = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                    fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    t = fmaxf(t, __shfl_xor(t, 16, 64));
-    t = fmaxf(t, __shfl_xor(t, 32, 64));
-    tmax = t * a.sl2;
-  };
-
-  // ---- back half: weights against the running max, O^T += V^T P^T, ring rotation
   // Wait states between the last accumulator MFMAs and VALU reads of the accumulators.
   // Every accumulator passes through an AGPR-constrained statement here, so the reads
   // cannot be hoisted above it (out of the rare rescale branch, into the tile loop).
@@ -349,60 +272,179 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
                      "+a"(acc[i0 + 7]));
   };
 
-  auto back = [&]() {
-    float p[8];
+  // per-lane LDS offsets inside a tile
+  const int xk = i16 & 7;
+  const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
+  const int offk1 = i16 * kRowBytes + 16 * ((4 + g) ^ xk);
+  const int rv = 4 * g + (i16 >> 2);
+  const int xv = rv & 7;
+  const int qv = (i16 >> 1) & 1;
+  int offv[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], a.sl2, negm));
-    ls += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    // B operand k slots 8 g .. 8 g + 7 = tokens 4 g + [0, 4) and 16 + 4 g + [0, 4)
-    const bf16x8 pb = __builtin_bit_cast(
-        bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-    // V^T operands read kAhead dim tiles ahead
-    auto vop = [&](int dt) -> bf16x8 {
-      const int o = offv[dt & 3] + 128 * (dt >> 2);
-      const u32x2 v0 = lds_tr16(buf + o);
-      const u32x2 v1 = lds_tr16(buf + 16 * kRowBytes + o);
-      return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
-    };
-    bf16x8 va[kAhead + 1];
+  for (int u = 0; u < 4; ++u) offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8;
+
+  // K operands (A of S^T = K Q^T) for k-step ks of a tile: tokens i16 and 16 + i16
+  auto kread = [&](const char DCP_LDS* tb, int ks, bf16x8 (&dst)[2]) {
+    const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
+    dst[0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + o);
+    dst[1] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + 16 * kRowBytes + o);
+  };
+  // V^T operand (A of O^T = V^T P^T) for value-dim tile dt
+  auto vop = [&](const char DCP_LDS* tb, int dt) -> bf16x8 {
+    const int o = offv[dt & 3] + 128 * (dt >> 2);
+    const u32x2 v0 = lds_tr16(tb + o);
+    const u32x2 v1 = lds_tr16(tb + 16 * kRowBytes + o);
+    return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
+  };
+  // Score masking: x[i] is token 4 g + i, x[4 + i] token 16 + 4 g + i of the tile; rows
+  // outside the mask get -inf (branch-free: it runs in the shadow of MFMAs).
+  auto mask_scores = [&](const f4& s0, const f4& s1, uint64_t vm, float (&xo)[8]) {
+    const uint32_t lo = (uint32_t)(vm >> (4 * g)) & 0xFu;
+    const uint32_t hi = (uint32_t)(vm >> (16 + 4 * g)) & 0xFu;
 #pragma unroll
-    for (int dt = 0; dt < kAhead; ++dt) va[dt] = vop(dt);
+    for (int i = 0; i < 4; ++i) {
+      xo[i] = ((lo >> i) & 1u) ? s0[i] : neg_inf();
+      xo[4 + i] = ((hi >> i) & 1u) ? s1[i] : neg_inf();
+    }
+  };
+  // max over the 32 tokens of the tile for this lane's head (lanes i16, 16+i16, 32+i16,
+  // 48+i16 hold one head): within the lane, then across the 16-lane rows with two swaps
+  auto lane_max = [&](const float (&xi)[8]) -> float {
+    return fmaxf(fmaxf(fmaxf(xi[0], xi[1]), fmaxf(xi[2], xi[3])),
+                 fmaxf(fmaxf(xi[4], xi[5]), fmaxf(xi[6], xi[7])));
+  };
+  auto row_max = [&](float t) -> float {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t),
+                                                       false, false);
+    t = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
+                                                       false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  };
+
+  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+  // prologue: tiles 0, 1, 2 in flight
+  uint64_t vm0 = issue_tile(0);
+  uint64_t vm1 = ntiles > 1 ? issue_tile(1) : 0ull;
+  uint64_t vm2 = ntiles > 2 ? issue_tile(2) : 0ull;
+  uint64_t vm3 = 0ull;
+
+  // scores of tile 0
+  float x[8];               // scores of the tile whose weights come next
+  float tmax;               // their max (log2 units) for this lane's head
+  {
+    if (!kFast || ntiles < 2) wait_vmcnt<0>();
+    else if (ntiles == 2) wait_vmcnt<kDmaPerWave>();
+    else wait_vmcnt<2 * kDmaPerWave>();
+    asm volatile("s_barrier" ::: "memory");
+    f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 kop[kAhead + 1][2];
 #pragma unroll
-    for (int dt = 0; dt < kDvTiles; ++dt) {
-      if (dt + kAhead < kDvTiles) va[(dt + kAhead) % (kAhead + 1)] = vop(dt + kAhead);
-      if (dt == 0) mfma_acc<true>(acc[dt], va[dt % (kAhead + 1)], pb);
-      else mfma_acc<false>(acc[dt], va[dt % (kAhead + 1)], pb);
+    for (int ks = 0; ks < kAhead; ++ks) kread(lds, ks, kop[ks]);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + kAhead < kKSteps) kread(lds, ks + kAhead, kop[(ks + kAhead) % (kAhead + 1)]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][0], qreg[ks], s0, 0,
+                                                   0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][1], qreg[ks], s1, 0,
+                                                   0, 0);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    mask_scores(s0, s1, vm0, x);
+    tmax = row_max(lane_max(x)) * a.sl2;
+  }
+
+  // Software pipeline, iteration ti: (1) the running-max check for tile ti, (2) wait for
+  // tile ti+1 and start tile ti+3, (3) the MFMAs of tile ti+1's scores with tile ti's
+  // weights computed between them, (4) the MFMAs of tile ti's O^T += V^T P^T with tile
+  // ti+1's masking and max computed between them.  The ring holds tiles ti (read by (4)),
+  // ti+1 (read by (3)), ti+2 and ti+3 (landing).  On the last tile, (3) reads a stale
+  // buffer whose scores are never used.
+  for (int ti = 0; ti < ntiles; ++ti) {
+    // (1) Some head's tile max exceeds its running max by more than kRescaleSlack (always
+    // on the first tile with valid tokens): move those maxima to the tile max and
+    // rescale.  Between raises the weights stay below 2^kRescaleSlack, exactly
+    // representable in bf16 / fp32, and the final normalisation by the running sum is
+    // exact either way.
+    {
+      const bool up = tmax > m + kRescaleSlack;
+      if (__ballot(up) != 0) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
+        if (up) {
+          m = tmax;
+          negm = -tmax;
+        }
+        ls *= alpha;
+        settle_acc();
+#pragma unroll
+        for (int i = 0; i < kDvTiles; ++i) {
+          acc[i] *= alpha;
+          asm volatile("" : "+a"(acc[i]));
+        }
+      }
+    }
+    // (2) this wave's copies of tile ti+1 have landed (those of ti+2 may still fly); after
+    // the barrier every wave's have, and every wave is done with tile ti-1, whose buffer
+    // tile ti+3 now takes.  A bare barrier: the fence of __syncthreads would also wait for
+    // the copies still in flight.
+    if (kFast && ti + 2 < ntiles) wait_vmcnt<kDmaPerWave>();
+    else wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+    vm3 = ti + 3 < ntiles ? issue_tile(ti + 3) : 0ull;
+    const char DCP_LDS* bq = lds + ((ti + 1) % kNBuf) * kTileBytes;
+    const char DCP_LDS* bv = lds + (ti % kNBuf) * kTileBytes;
+
+    // (3) scores of tile ti+1; weights of tile ti
+    f4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
+    float p[8];
+    bf16x8 pb;
+    {
+      bf16x8 kop[kAhead + 1][2];
+#pragma unroll
+      for (int ks = 0; ks < kAhead; ++ks) kread(bq, ks, kop[ks]);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        if (ks + kAhead < kKSteps) kread(bq, ks + kAhead, kop[(ks + kAhead) % (kAhead + 1)]);
+        n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][0], qreg[ks], n0,
+                                                     0, 0, 0);
+        n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][1], qreg[ks], n1,
+                                                     0, 0, 0);
+        if (ks < 8) p[ks] = __builtin_amdgcn_exp2f(fmaf(x[ks], a.sl2, negm));
+        if (ks == 9)
+          pb = __builtin_bit_cast(
+              bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+        if (ks == 10) ls += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        __builtin_amdgcn_sched_barrier(0);   // one scheduling region per k-step
+      }
+    }
+
+    // (4) O^T += V^T P^T of tile ti (V^T operands read kAhead dim tiles ahead); masking and
+    // max of tile ti+1
+    {
+      float xn[8];
+      float tn = 0.f;
+      bf16x8 va[kAhead + 1];
+#pragma unroll
+      for (int dt = 0; dt < kAhead; ++dt) va[dt] = vop(bv, dt);
+#pragma unroll
+      for (int dt = 0; dt < kDvTiles; ++dt) {
+        if (dt + kAhead < kDvTiles) va[(dt + kAhead) % (kAhead + 1)] = vop(bv, dt + kAhead);
+        if (dt == 0) mfma_acc<true>(acc[dt], va[dt % (kAhead + 1)], pb);
+        else mfma_acc<false>(acc[dt], va[dt % (kAhead + 1)], pb);
+        if (dt == 1) mask_scores(n0, n1, vm1, xn);
+        if (dt == 3) tn = lane_max(xn);
+        if (dt == 5) tn = row_max(tn);
+        if (dt == 7) tn *= a.sl2;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = xn[i];
+      tmax = tn;
     }
     vm0 = vm1;
     vm1 = vm2;
     vm2 = vm3;
-  };
-
-  for (int ti = 0; ti < ntiles; ++ti) {
-    front(ti);
-    const bool up = tmax > m + kRescaleSlack;
-    if (__ballot(up) != 0) {
-      // Some head's tile max exceeds its running max by more than kRescaleSlack (always
-      // on the first tile with valid tokens): move those maxima to the tile max and
-      // rescale.  Between raises the weights stay below 2^kRescaleSlack, exactly
-      // representable in bf16 / fp32, and the final normalisation by the running sum is
-      // exact either way.
-      const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
-      if (up) {
-        m = tmax;
-        negm = -tmax;
-      }
-      ls *= alpha;
-      settle_acc();
-#pragma unroll
-      for (int i = 0; i < kDvTiles; ++i) {
-        acc[i] *= alpha;
-        asm volatile("" : "+a"(acc[i]));
-      }
-    }
-    back();
   }
 
   // ---- finalize: lane holds dims 16 dt + 4 g + [0, 4) of its head
