@@ -65,12 +65,24 @@ constexpr int kRowChunks = kRowBytes / 16;   // 72
 constexpr int kTileBytes = kTile * kRowBytes;  // 36 KiB
 constexpr int kKSteps = kDk / 32;            // 18
 constexpr int kDvTiles = kDv / 16;           // 32
-constexpr int kWaves = 4;                    // waves per workgroup, 16 heads each
-constexpr int kGroups = kHeads / (16 * kWaves);          // head groups (workgroups) per item
+constexpr int kHeadTiles = 4;                // 16-head tiles per workgroup (64 heads)
+constexpr int kGroups = kHeads / (16 * kHeadTiles);      // head groups (workgroups) per item
+constexpr int kQkWaves = kHeadTiles;         // score waves: one per head tile
+constexpr int kPvWaves = 2 * kHeadTiles;     // output waves: one per (head tile, dv half)
+constexpr int kWaves = kQkWaves + kPvWaves;  // 12 waves, three per SIMD
 constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 16-B copies per lane per tile
+constexpr int kDvHalfTiles = kDvTiles / 2;   // dv tiles of one output wave
 constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kRescaleSlack = 8.f;          // see the online softmax below
-constexpr int kAhead = 6;                    // LDS operand prefetch distance (MFMA steps)
+constexpr int kAheadK = 4;                   // K operand prefetch distance (k-steps)
+constexpr int kAheadV = 6;                   // V^T operand prefetch distance (dv tiles)
+// LDS: the tile ring, then the weight exchange (two slots: tile parity), the rescale
+// factors, and the final per-head normalisation
+constexpr int kRingBytes = kNBuf * kTileBytes;                  // 147456
+constexpr int kPOff = kRingBytes;                               // [2][4][64 lanes][16 B]
+constexpr int kAOff = kPOff + 2 * kHeadTiles * 1024;            // [2][4][16] float
+constexpr int kFOff = kAOff + 2 * kHeadTiles * 16 * 4;          // [4][16] float
+constexpr int kLdsBytes = kFOff + kHeadTiles * 16 * 4;          // 156416
 
 struct MlaKArgs {
   const uint16_t* q;
@@ -137,11 +149,28 @@ __device__ __forceinline__ void mfma_acc(f4& acc, const bf16x8& va, const bf16x8
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(va), "v"(pb));
 }
 
+__device__ __forceinline__ void wait_lgkm0() {
+  // lgkmcnt(0), vector-memory and export counters unconstrained (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
 // kFast: the interleave and the block size are multiples of the tile, so the 32 tokens of a
 // tile are consecutive slots of one cache page.
+//
+// Warp-specialised workgroup of 12 waves for 64 heads (four 16-head tiles):
+//   * score waves 0..3 (one per head tile) hold the head tile's query and compute, for tile
+//     t, S^T = K Q^T, the online-softmax state and the bf16 weights P, which they hand over
+//     through LDS together with the factor that rescales the output accumulated so far;
+//   * output waves 4..11 (one per head tile and half of the 512 value dims) hold O^T in
+//     AGPRs and, one tile behind, accumulate O^T += V^T P^T.
+// Waves are dealt round-robin over the SIMDs, so each SIMD runs one score wave and two
+// output waves (68 MFMAs per tile), and every wave issues only 33-36 LDS reads per tile.
+// One barrier per tile: at barrier t, tile t has landed (copies paced by each wave's own
+// vector-memory counter), the weights of tile t-1 are in LDS, and every read of tile t-2
+// is done, so its buffer takes the copy of tile t+2.
 template <bool kFast>
 __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   // Workgroup ids: the kGroups head groups of one work item are congruent mod 8 (same XCD)
   // and adjacent in dispatch order.
@@ -157,7 +186,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4;      // 16-lane group
   const int i16 = lane & 15;
-  const int head = 16 * (kWaves * hg + w) + i16;
   const uint32_t B = (uint32_t)a.block_size;
   const int32_t* btb = a.bt + (size_t)b * a.max_blocks;
   // the block table through the constant address space: scalar loads, which do not count
@@ -232,237 +260,222 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     }
   };
 
-  // ---- query (B operand of S^T = K Q^T): dims 32 ks + 8 g .. + 8
-  bf16x8 qreg[kKSteps];
-  {
-    const uint16_t* qrow = a.q + ((size_t)b * kHeads + head) * kDk + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-  }
-  // the query must have landed before the copy ring starts: inside the ring the vector
-  // memory counter only paces tile copies
-  wait_vmcnt<0>();
-
-  // Every definition of an accumulator comes out of an AGPR-constrained asm statement, so
-  // the register allocator keeps the loop-carried accumulators in AGPRs instead of copying
-  // them to VGPRs around every tile.
-  f4 acc[kDvTiles];
-#pragma unroll
-  for (int i = 0; i < kDvTiles; ++i) {
-    acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-    asm volatile("" : "+a"(acc[i]));
-  }
-  float m = neg_inf();   // running max (log2 units) of this lane's head
-  float negm = 0.f;      // -m, or 0 while m is -inf
-  float ls = 0.f;        // this lane's share of the running sum of weights
-
-  // Wait states between the last accumulator MFMAs and VALU reads of the accumulators.
-  // Every accumulator passes through an AGPR-constrained statement here, so the reads
-  // cannot be hoisted above it (out of the rare rescale branch, into the tile loop).
-  auto settle_acc = [&]() {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[24]), "+a"(acc[25]), "+a"(acc[26]), "+a"(acc[27]),
-                   "+a"(acc[28]), "+a"(acc[29]), "+a"(acc[30]), "+a"(acc[31]));
-#pragma unroll
-    for (int i0 = 0; i0 < 24; i0 += 8)
-      asm volatile(""
-                   : "+a"(acc[i0]), "+a"(acc[i0 + 1]), "+a"(acc[i0 + 2]), "+a"(acc[i0 + 3]),
-                     "+a"(acc[i0 + 4]), "+a"(acc[i0 + 5]), "+a"(acc[i0 + 6]),
-                     "+a"(acc[i0 + 7]));
-  };
-
-  // per-lane LDS offsets inside a tile
-  const int xk = i16 & 7;
-  const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
-  const int offk1 = i16 * kRowBytes + 16 * ((4 + g) ^ xk);
-  const int rv = 4 * g + (i16 >> 2);
-  const int xv = rv & 7;
-  const int qv = (i16 >> 1) & 1;
-  int offv[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8;
-
-  // K operands (A of S^T = K Q^T) for k-step ks of a tile: tokens i16 and 16 + i16
-  auto kread = [&](const char DCP_LDS* tb, int ks, bf16x8 (&dst)[2]) {
-    const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
-    dst[0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + o);
-    dst[1] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + 16 * kRowBytes + o);
-  };
-  // V^T operand (A of O^T = V^T P^T) for value-dim tile dt
-  auto vop = [&](const char DCP_LDS* tb, int dt) -> bf16x8 {
-    const int o = offv[dt & 3] + 128 * (dt >> 2);
-    const u32x2 v0 = lds_tr16(tb + o);
-    const u32x2 v1 = lds_tr16(tb + 16 * kRowBytes + o);
-    return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
-  };
-  // Score masking: x[i] is token 4 g + i, x[4 + i] token 16 + 4 g + i of the tile; rows
-  // outside the mask get -inf (branch-free: it runs in the shadow of MFMAs).
-  auto mask_scores = [&](const f4& s0, const f4& s1, uint64_t vm, float (&xo)[8]) {
-    const uint32_t lo = (uint32_t)(vm >> (4 * g)) & 0xFu;
-    const uint32_t hi = (uint32_t)(vm >> (16 + 4 * g)) & 0xFu;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xo[i] = ((lo >> i) & 1u) ? s0[i] : neg_inf();
-      xo[4 + i] = ((hi >> i) & 1u) ? s1[i] : neg_inf();
-    }
-  };
-  // max over the 32 tokens of the tile for this lane's head (lanes i16, 16+i16, 32+i16,
-  // 48+i16 hold one head): within the lane, then across the 16-lane rows with two swaps
-  auto lane_max = [&](const float (&xi)[8]) -> float {
-    return fmaxf(fmaxf(fmaxf(xi[0], xi[1]), fmaxf(xi[2], xi[3])),
-                 fmaxf(fmaxf(xi[4], xi[5]), fmaxf(xi[6], xi[7])));
-  };
-  auto row_max = [&](float t) -> float {
-    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t),
-                                                       false, false);
-    t = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
-                                                       false, false);
-    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-  };
-
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  // prologue: tiles 0, 1, 2 in flight
+  // prologue: tiles 0 and 1 in flight
   uint64_t vm0 = issue_tile(0);
   uint64_t vm1 = ntiles > 1 ? issue_tile(1) : 0ull;
-  uint64_t vm2 = ntiles > 2 ? issue_tile(2) : 0ull;
-  uint64_t vm3 = 0ull;
+  uint64_t vm2 = 0ull;
 
-  // scores of tile 0
-  float x[8];               // scores of the tile whose weights come next
-  float tmax;               // their max (log2 units) for this lane's head
-  {
-    if (!kFast || ntiles < 2) wait_vmcnt<0>();
-    else if (ntiles == 2) wait_vmcnt<kDmaPerWave>();
-    else wait_vmcnt<2 * kDmaPerWave>();
-    asm volatile("s_barrier" ::: "memory");
-    f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 kop[kAhead + 1][2];
-#pragma unroll
-    for (int ks = 0; ks < kAhead; ++ks) kread(lds, ks, kop[ks]);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      if (ks + kAhead < kKSteps) kread(lds, ks + kAhead, kop[(ks + kAhead) % (kAhead + 1)]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][0], qreg[ks], s0, 0,
-                                                   0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][1], qreg[ks], s1, 0,
-                                                   0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+  // Iteration t of the tile loop, common part: tile t has landed for every wave, tile t+2
+  // starts.  Both roles run exactly ntiles + 1 of these.
+  auto sync_tile = [&](int t) {
+    if (t < ntiles) {
+      if (kFast && t + 1 < ntiles) wait_vmcnt<kDmaPerWave>();
+      else wait_vmcnt<0>();
     }
-    mask_scores(s0, s1, vm0, x);
-    tmax = row_max(lane_max(x)) * a.sl2;
-  }
+    asm volatile("s_barrier" ::: "memory");
+    vm2 = t + 2 < ntiles ? issue_tile(t + 2) : 0ull;
+  };
 
-  // Software pipeline, iteration ti: (1) the running-max check for tile ti, (2) wait for
-  // tile ti+1 and start tile ti+3, (3) the MFMAs of tile ti+1's scores with tile ti's
-  // weights computed between them, (4) the MFMAs of tile ti's O^T += V^T P^T with tile
-  // ti+1's masking and max computed between them.  The ring holds tiles ti (read by (4)),
-  // ti+1 (read by (3)), ti+2 and ti+3 (landing).  On the last tile, (3) reads a stale
-  // buffer whose scores are never used.
-  for (int ti = 0; ti < ntiles; ++ti) {
-    // (1) Some head's tile max exceeds its running max by more than kRescaleSlack (always
-    // on the first tile with valid tokens): move those maxima to the tile max and
-    // rescale.  Between raises the weights stay below 2^kRescaleSlack, exactly
-    // representable in bf16 / fp32, and the final normalisation by the running sum is
-    // exact either way.
+  if (w < kQkWaves) {
+    // ================= score wave: head tile w =================
+    const int head = 16 * (kHeadTiles * hg + w) + i16;
+    // query (B operand of S^T = K Q^T): dims 32 ks + 8 g .. + 8
+    bf16x8 qreg[kKSteps];
     {
-      const bool up = tmax > m + kRescaleSlack;
-      if (__ballot(up) != 0) {
+      const uint16_t* qrow = a.q + ((size_t)b * kHeads + head) * kDk + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks)
+        qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    }
+    // the query must have landed before the copy ring is paced by the counter alone
+    wait_vmcnt<0>();
+    // The query lives in AGPRs (the MFMAs read their B operand from there), leaving the
+    // VGPRs to the operand ring: both roles then fit three waves per SIMD.
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+a"(qreg[ks]));
+    float m = neg_inf();   // running max (log2 units) of this lane's head
+    float negm = 0.f;      // -m, or 0 while m is -inf
+    float ls = 0.f;        // this lane's share of the running sum of weights
+    const int xk = i16 & 7;
+    const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
+    const int offk1 = i16 * kRowBytes + 16 * ((4 + g) ^ xk);
+    char DCP_LDS* pdst = (char DCP_LDS*)smem + kPOff + w * 1024 + lane * 16;
+    float DCP_LDS* adst = (float DCP_LDS*)(smem + kAOff) + w * 16 + i16;
+
+    for (int t = 0; t <= ntiles; ++t) {
+      wait_lgkm0();   // the previous tile's weights are in LDS before the barrier
+      sync_tile(t);
+      if (t < ntiles) {
+        const char DCP_LDS* tb = lds + (t % kNBuf) * kTileBytes;
+        f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 kop[kAheadK + 1][2];
+        auto kread = [&](int ks) {
+          const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
+          kop[ks % (kAheadK + 1)][0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + o);
+          kop[ks % (kAheadK + 1)][1] =
+              *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + 16 * kRowBytes + o);
+        };
+#pragma unroll
+        for (int ks = 0; ks < kAheadK; ++ks) kread(ks);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          if (ks + kAheadK < kKSteps) kread(ks + kAheadK);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAheadK + 1)][0], qreg[ks], s0,
+                                                       0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAheadK + 1)][1], qreg[ks], s1,
+                                                       0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // scores: x[i] is token 4 g + i, x[4 + i] token 16 + 4 g + i; masked rows -> -inf
+        float x[8];
+        {
+          const uint32_t lo = (uint32_t)(vm0 >> (4 * g)) & 0xFu;
+          const uint32_t hi = (uint32_t)(vm0 >> (16 + 4 * g)) & 0xFu;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = ((lo >> i) & 1u) ? s0[i] : neg_inf();
+            x[4 + i] = ((hi >> i) & 1u) ? s1[i] : neg_inf();
+          }
+        }
+        // tile max of this lane's head: within the lane, then across the four 16-lane
+        // rows (which hold the same head) with two swaps
+        float tm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        {
+          const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tm),
+                                                             __float_as_uint(tm), false, false);
+          tm = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+          const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm),
+                                                             __float_as_uint(tm), false, false);
+          tm = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+        }
+        const float tmax = tm * a.sl2;
+        // The running max only moves when a head's tile max exceeds it by more than
+        // kRescaleSlack (always on the first tile with valid tokens).  Between raises the
+        // weights stay below 2^kRescaleSlack, exactly representable in bf16 / fp32, and
+        // the final normalisation by the running sum is exact either way.
+        const bool up = tmax > m + kRescaleSlack;
         const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
         if (up) {
           m = tmax;
           negm = -tmax;
         }
-        ls *= alpha;
-        settle_acc();
+        float p[8];
 #pragma unroll
-        for (int i = 0; i < kDvTiles; ++i) {
-          acc[i] *= alpha;
-          asm volatile("" : "+a"(acc[i]));
+        for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], a.sl2, negm));
+        ls = ls * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        // B operand of O^T += V^T P^T: k slots 8 g .. 8 g + 7 = tokens 4 g + [0, 4) and
+        // 16 + 4 g + [0, 4); the output lane with the same index reads these 16 bytes
+        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        *reinterpret_cast<u32x4 DCP_LDS*>(pdst + (t & 1) * (kHeadTiles * 1024)) = pw;
+        if (g == 0) adst[(t & 1) * (kHeadTiles * 16)] = alpha;
+      }
+      vm0 = vm1;
+      vm1 = vm2;
+    }
+    // ---- per-head normalisation for the output waves, and the lse
+    float lt = ls;
+    {
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt),
+                                                         false, false);
+      lt = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt),
+                                                         false, false);
+      lt = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : neg_inf();
+    if (g == 0) {
+      ((float DCP_LDS*)(smem + kFOff))[w * 16 + i16] = inv;
+      if (single) a.lse_out[(size_t)b * kHeads + head] = lse;
+      else a.plse[(size_t)item * kHeads + head] = lse;
+    }
+    wait_lgkm0();
+    asm volatile("s_barrier" ::: "memory");
+  } else {
+    // ================= output wave: head tile ht, value dims 256 half .. + 256 ==========
+    const int pv = w - kQkWaves;
+    const int ht = pv >> 1;
+    const int half = pv & 1;
+    const int head = 16 * (kHeadTiles * hg + ht) + i16;
+    // Every definition of an accumulator comes out of an AGPR-constrained asm statement,
+    // so the register allocator keeps the loop-carried accumulators in AGPRs.
+    f4 acc[kDvHalfTiles];
+#pragma unroll
+    for (int i = 0; i < kDvHalfTiles; ++i) {
+      acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[i]));
+    }
+    // Wait states between the last accumulator MFMAs and VALU reads of the accumulators;
+    // every accumulator passes through an AGPR-constrained statement here, so the reads
+    // cannot be hoisted above it.
+    auto settle_acc = [&]() {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]),
+                     "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
+      asm volatile(""
+                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]),
+                     "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]));
+    };
+    // V^T operand (A of O^T = V^T P^T) for value-dim tile dt of this wave's half
+    const int rv = 4 * g + (i16 >> 2);
+    const int xv = rv & 7;
+    const int qv = (i16 >> 1) & 1;
+    int offv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8 + half * 512;
+    const char DCP_LDS* psrc = lds + kPOff + ht * 1024 + lane * 16;
+    const float DCP_LDS* asrc = (const float DCP_LDS*)(smem + kAOff) + ht * 16 + i16;
+
+    for (int t = 0; t <= ntiles; ++t) {
+      sync_tile(t);
+      if (t >= 1) {
+        const int u = t - 1;   // the tile whose weights the score waves wrote last
+        const char DCP_LDS* tb = lds + (u % kNBuf) * kTileBytes;
+        auto vop = [&](int dt) -> bf16x8 {
+          const int o = offv[dt & 3] + 128 * (dt >> 2);
+          const u32x2 v0 = lds_tr16(tb + o);
+          const u32x2 v1 = lds_tr16(tb + 16 * kRowBytes + o);
+          return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
+        };
+        const bf16x8 pb =
+            *reinterpret_cast<const bf16x8 DCP_LDS*>(psrc + (u & 1) * (kHeadTiles * 1024));
+        const float alpha = asrc[(u & 1) * (kHeadTiles * 16)];
+        bf16x8 va[kAheadV + 1];
+#pragma unroll
+        for (int dt = 0; dt < kAheadV; ++dt) va[dt] = vop(dt);
+        if (__ballot(alpha != 1.f) != 0) {
+          settle_acc();
+#pragma unroll
+          for (int i = 0; i < kDvHalfTiles; ++i) {
+            acc[i] *= alpha;
+            asm volatile("" : "+a"(acc[i]));
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < kDvHalfTiles; ++dt) {
+          if (dt + kAheadV < kDvHalfTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
+          if (dt == 0) mfma_acc<true>(acc[dt], va[dt % (kAheadV + 1)], pb);
+          else mfma_acc<false>(acc[dt], va[dt % (kAheadV + 1)], pb);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    // (2) this wave's copies of tile ti+1 have landed (those of ti+2 may still fly); after
-    // the barrier every wave's have, and every wave is done with tile ti-1, whose buffer
-    // tile ti+3 now takes.  A bare barrier: the fence of __syncthreads would also wait for
-    // the copies still in flight.
-    if (kFast && ti + 2 < ntiles) wait_vmcnt<kDmaPerWave>();
-    else wait_vmcnt<0>();
     asm volatile("s_barrier" ::: "memory");
-    vm3 = ti + 3 < ntiles ? issue_tile(ti + 3) : 0ull;
-    const char DCP_LDS* bq = lds + ((ti + 1) % kNBuf) * kTileBytes;
-    const char DCP_LDS* bv = lds + (ti % kNBuf) * kTileBytes;
-
-    // (3) scores of tile ti+1; weights of tile ti
-    f4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = {0.f, 0.f, 0.f, 0.f};
-    float p[8];
-    bf16x8 pb;
-    {
-      bf16x8 kop[kAhead + 1][2];
+    // ---- finalize: lane holds dims 256 half + 16 dt + 4 g + [0, 4) of its head
+    const float inv = ((const float DCP_LDS*)(smem + kFOff))[ht * 16 + i16];
+    settle_acc();
+    float* dst = (single ? a.o_out + ((size_t)b * kHeads + head) * kDv
+                         : a.po + ((size_t)item * kHeads + head) * kDv) +
+                 half * 256;
 #pragma unroll
-      for (int ks = 0; ks < kAhead; ++ks) kread(bq, ks, kop[ks]);
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        if (ks + kAhead < kKSteps) kread(bq, ks + kAhead, kop[(ks + kAhead) % (kAhead + 1)]);
-        n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][0], qreg[ks], n0,
-                                                     0, 0, 0);
-        n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAhead + 1)][1], qreg[ks], n1,
-                                                     0, 0, 0);
-        if (ks < 8) p[ks] = __builtin_amdgcn_exp2f(fmaf(x[ks], a.sl2, negm));
-        if (ks == 9)
-          pb = __builtin_bit_cast(
-              bf16x8, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-        if (ks == 10) ls += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        __builtin_amdgcn_sched_barrier(0);   // one scheduling region per k-step
-      }
+    for (int dt = 0; dt < kDvHalfTiles; ++dt) {
+      const f4 v = acc[dt] * inv;
+      *reinterpret_cast<f4*>(dst + 16 * dt + 4 * g) = v;
     }
-
-    // (4) O^T += V^T P^T of tile ti (V^T operands read kAhead dim tiles ahead); masking and
-    // max of tile ti+1
-    {
-      float xn[8];
-      float tn = 0.f;
-      bf16x8 va[kAhead + 1];
-#pragma unroll
-      for (int dt = 0; dt < kAhead; ++dt) va[dt] = vop(bv, dt);
-#pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt) {
-        if (dt + kAhead < kDvTiles) va[(dt + kAhead) % (kAhead + 1)] = vop(bv, dt + kAhead);
-        if (dt == 0) mfma_acc<true>(acc[dt], va[dt % (kAhead + 1)], pb);
-        else mfma_acc<false>(acc[dt], va[dt % (kAhead + 1)], pb);
-        if (dt == 1) mask_scores(n0, n1, vm1, xn);
-        if (dt == 3) tn = lane_max(xn);
-        if (dt == 5) tn = row_max(tn);
-        if (dt == 7) tn *= a.sl2;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = xn[i];
-      tmax = tn;
-    }
-    vm0 = vm1;
-    vm1 = vm2;
-    vm2 = vm3;
-  }
-
-  // ---- finalize: lane holds dims 16 dt + 4 g + [0, 4) of its head
-  settle_acc();
-  float lt = ls + __shfl_xor(ls, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : neg_inf();
-  float* dst = single ? a.o_out + ((size_t)b * kHeads + head) * kDv
-                      : a.po + ((size_t)item * kHeads + head) * kDv;
-#pragma unroll
-  for (int dt = 0; dt < kDvTiles; ++dt) {
-    const f4 v = acc[dt] * inv;
-    *reinterpret_cast<f4*>(dst + 16 * dt + 4 * g) = v;
-  }
-  if (g == 0) {
-    if (single) a.lse_out[(size_t)b * kHeads + head] = lse;
-    else a.plse[(size_t)item * kHeads + head] = lse;
   }
 }
 
