@@ -67,22 +67,27 @@ constexpr int kKSteps = kDk / 32;            // 18
 constexpr int kDvTiles = kDv / 16;           // 32
 constexpr int kHeadTiles = 4;                // 16-head tiles per workgroup (64 heads)
 constexpr int kGroups = kHeads / (16 * kHeadTiles);      // head groups (workgroups) per item
-constexpr int kQkWaves = kHeadTiles;         // score waves: one per head tile
-constexpr int kPvWaves = 2 * kHeadTiles;     // output waves: one per (head tile, dv half)
+constexpr int kQkWaves = 4;                  // score waves: (head pair, half of the 576 dims)
+constexpr int kPvWaves = 8;                  // output waves: (head pair, quarter of the 512 dims)
 constexpr int kWaves = kQkWaves + kPvWaves;  // 12 waves, three per SIMD
-constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 16-B copies per lane per tile
-constexpr int kDvHalfTiles = kDvTiles / 2;   // dv tiles of one output wave
+constexpr int kHalfSteps = kKSteps / 2;      // 9 k-steps of 32 dims per score wave
+constexpr int kQuarterTiles = kDvTiles / 4;  // 8 dv tiles of 16 dims per output wave
+constexpr int kSlotsHi = 5;                  // 1-KiB tile copies per tile: output waves 0..3
+constexpr int kSlotsLo = 4;                  // output waves 4..7 (4 x 5 + 4 x 4 = 36 slots)
+constexpr int kPhase1Tiles = 2;              // dv tiles of an output wave before the mid barrier
 constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kRescaleSlack = 8.f;          // see the online softmax below
 constexpr int kAheadK = 4;                   // K operand prefetch distance (k-steps)
-constexpr int kAheadV = 6;                   // V^T operand prefetch distance (dv tiles)
-// LDS: the tile ring, then the weight exchange (two slots: tile parity), the rescale
-// factors, and the final per-head normalisation
+constexpr int kAheadV = 3;                   // V^T operand prefetch distance (dv tiles)
+// LDS: the tile ring; the partial-score exchange [pair][head tile][lane][8 floats]; the
+// weights P [head tile][lane][16 B]; the rescale factors and the final normalisation
+// [head tile][16] floats
 constexpr int kRingBytes = kNBuf * kTileBytes;                  // 147456
-constexpr int kPOff = kRingBytes;                               // [2][4][64 lanes][16 B]
-constexpr int kAOff = kPOff + 2 * kHeadTiles * 1024;            // [2][4][16] float
-constexpr int kFOff = kAOff + 2 * kHeadTiles * 16 * 4;          // [4][16] float
-constexpr int kLdsBytes = kFOff + kHeadTiles * 16 * 4;          // 156416
+constexpr int kXOff = kRingBytes;
+constexpr int kPOff = kXOff + kHeadTiles * 64 * 32;             // + 8192
+constexpr int kAOff = kPOff + kHeadTiles * 1024;                // + 4096
+constexpr int kFOff = kAOff + kHeadTiles * 16 * 4;              // + 256
+constexpr int kLdsBytes = kFOff + kHeadTiles * 16 * 4;          // 160256
 
 struct MlaKArgs {
   const uint16_t* q;
@@ -157,17 +162,23 @@ __device__ __forceinline__ void wait_lgkm0() {
 // kFast: the interleave and the block size are multiples of the tile, so the 32 tokens of a
 // tile are consecutive slots of one cache page.
 //
-// Warp-specialised workgroup of 12 waves for 64 heads (four 16-head tiles):
-//   * score waves 0..3 (one per head tile) hold the head tile's query and compute, for tile
-//     t, S^T = K Q^T, the online-softmax state and the bf16 weights P, which they hand over
-//     through LDS together with the factor that rescales the output accumulated so far;
-//   * output waves 4..11 (one per head tile and half of the 512 value dims) hold O^T in
-//     AGPRs and, one tile behind, accumulate O^T += V^T P^T.
-// Waves are dealt round-robin over the SIMDs, so each SIMD runs one score wave and two
-// output waves (68 MFMAs per tile), and every wave issues only 33-36 LDS reads per tile.
-// One barrier per tile: at barrier t, tile t has landed (copies paced by each wave's own
-// vector-memory counter), the weights of tile t-1 are in LDS, and every read of tile t-2
-// is done, so its buffer takes the copy of tile t+2.
+// Warp-specialised workgroup of 12 waves for 64 heads (two pairs of 16-head tiles).  Every
+// K / V operand read from LDS feeds two MFMAs (both head tiles of a pair):
+//   * score waves 0..3 = (head pair hp = w / 2, half kh = w % 2 of the 576 dims): for tile
+//     t, the partial S^T = K Q^T of both head tiles of the pair over their 288 dims
+//     (18 K reads, 36 MFMAs).  The two halves swap the partial scores of one head tile
+//     through LDS, so each finishes the online softmax of one head tile: running max,
+//     bf16 weights P and the factor that rescales the output accumulated so far, handed
+//     to the output waves through LDS;
+//   * output waves 4..11 = (head pair hp = (w - 4) / 4, quarter dq of the 512 value dims):
+//     O^T in AGPRs (both head tiles, 128 dims), one tile behind the score waves,
+//     O^T += V^T P^T (16 transposed V reads, 16 MFMAs per tile).
+// Waves are dealt round-robin over the SIMDs: each SIMD runs one score wave and two output
+// waves (68 MFMAs per tile).  Two barriers per tile: at barrier A of iteration t, tile t
+// has landed (copies paced by each wave's own vector-memory counter), P of tile t-1 is in
+// LDS and every read of tile t-2 is done, so its buffer takes the copy of tile t+2; at
+// barrier B the partial scores of tile t have been swapped.  The output waves split their
+// MFMAs over both phases, so the matrix cores stay busy while the softmax runs.
 template <bool kFast>
 __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -194,139 +205,161 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
       reinterpret_cast<uintptr_t>(btb));
   const char DCP_LDS* lds = (const char DCP_LDS*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  const bool is_qk = w < kQkWaves;
+  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
 
-  // Per-lane copy slots (loop invariant): 16-B slot (w * kDmaPerWave + k) * 64 + lane of a
-  // tile holds chunk (s mod 72) ^ (row & 7) of tile row s / 72.
-  uint32_t slot_off[kDmaPerWave], slot_col[kDmaPerWave];
-  int slot_row[kDmaPerWave];
-#pragma unroll
-  for (int k = 0; k < kDmaPerWave; ++k) {
-    const int sl = (w * kDmaPerWave + k) * 64 + lane;
-    const int r = sl / kRowChunks;
-    slot_row[k] = r;
-    slot_col[k] = (uint32_t)(((sl - r * kRowChunks) ^ (r & 7)) * 16);
-    slot_off[k] = (uint32_t)r * kRowBytes + slot_col[k];
-  }
-
-  // ---- one tile's HBM -> LDS copy (kDmaPerWave copies of 1 KiB per wave); returns the
-  // mask of valid rows.  Chunk c of row r lands at byte 16 * (72 r + (c ^ (r & 7))).
-  auto issue_tile = [&](int ti) -> uint64_t {
-    const int tj = j0 + ti * kTile;
-    const uint32_t dst = lds_addr + (uint32_t)((ti % kNBuf) * kTileBytes + w * kDmaPerWave * 1024);
+  // Page-contiguous tiles: a per-wave table of tile sources, lane k holding the first cache
+  // row of tile 64 * window + k (or ~0 for a bad page).  It is built by a lane-parallel walk
+  // and one gather of block-table entries, once per 64 tiles (the gather's vector-memory
+  // wait then drains the copies in flight, once per window), so locating a tile is one
+  // readlane: no scalar memory load inside the tile loop, whose counter the LDS operand
+  // waits share.
+  struct TileSrc {
+    const char* base;   // global address of the tile's first row
+    uint32_t lim;       // bytes of valid rows (slots past them re-read row 0, masked)
+    bool full;          // all 32 rows valid
+  };
+  uint32_t row_tab = 0;
+  auto build_table = [&](int win) {
+    const int tt = win * 64 + lane;
+    bool bad = false;
+    uint32_t row = ~0u;
+    if (tt < ntiles) {
+      const uint32_t t = dcp_walk_global_pos((uint32_t)(j0 + tt * kTile), a.rank, a.cp,
+                                             a.interleave);
+      const uint32_t lp = t / B;
+      const int32_t pg = btb[lp];
+      if (pg < 0 || (uint32_t)pg >= a.num_blocks) bad = true;
+      else row = (uint32_t)pg * B + (t - lp * B);
+    }
+    if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
+    row_tab = row;
+  };
+  if constexpr (kFast) build_table(0);
+  uint64_t vm_new = 0;
+  // source of tile ti
+  auto tile_src = [&](int ti) -> TileSrc {
+    if ((ti & 63) == 0 && ti > 0) build_table(ti >> 6);
+    const int nvalid = min(kTile, j1 - (j0 + ti * kTile));
+    const uint32_t row0 = __builtin_amdgcn_readlane(row_tab, ti & 63);
+    const bool ok = row0 != ~0u;
+    TileSrc ts;
+    ts.base = a.lat + (size_t)(ok ? row0 : 0u) * kRowBytes;
+    ts.full = ok && nvalid == kTile;
+    ts.lim = ok ? (uint32_t)nvalid * kRowBytes : 0u;
+    vm_new = ts.full ? 0xffffffffull : (ok ? ((1ull << nvalid) - 1) : 0ull);
+    return ts;
+  };
+  // mask of valid rows of tile ti (page-contiguous tiles: from the source table)
+  auto tile_mask = [&](int ti) -> uint64_t {
     if constexpr (kFast) {
-      const uint32_t t0 = dcp_walk_global_pos((uint32_t)tj, a.rank, a.cp, a.interleave);
-      const uint32_t lp = t0 / B;
-      const int32_t pg = btc[lp];
-      const int nvalid = min(kTile, j1 - tj);
-      const bool ok = pg >= 0 && (uint32_t)pg < a.num_blocks;
-      if (!ok && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
-      const uint32_t row0 = ok ? (uint32_t)pg * B + (t0 - lp * B) : 0u;
-      const char* base = a.lat + (size_t)row0 * kRowBytes;
-      if (ok && nvalid == kTile) {
-#pragma unroll
-        for (int k = 0; k < kDmaPerWave; ++k) copy16_sbase(dst + k * 1024, slot_off[k], base);
-        return 0xffffffffull;
-      }
-      // partial (last) tile or a bad page: slots of rows past the valid prefix re-read row
-      // 0 of the tile (their scores are masked)
-      const uint32_t lim = ok ? (uint32_t)nvalid * kRowBytes : 0u;
-#pragma unroll
-      for (int k = 0; k < kDmaPerWave; ++k)
-        copy16_sbase(dst + k * 1024, slot_off[k] < lim ? slot_off[k] : slot_col[k], base);
-      return ok ? ((1ull << nvalid) - 1) : 0ull;
+      (void)tile_src(ti);
+      return vm_new;
     } else {
-      const int j = tj + lane;
+      const int j = j0 + ti * kTile + lane;
       bool ok = lane < kTile && j < j1;
-      bool bad = false;
-      uint32_t lrow = 0;
       if (ok) {
         const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-        const uint32_t lp = t / B;
-        const int32_t pg = btb[lp];
-        if (pg < 0 || (uint32_t)pg >= a.num_blocks) {
-          ok = false;
-          bad = true;
-        } else {
-          lrow = (uint32_t)pg * B + (t - lp * B);
-        }
-      }
-      if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
-#pragma unroll
-      for (int k = 0; k < kDmaPerWave; ++k) {
-        const uint32_t rr = __shfl(lrow, slot_row[k], 64);
-        copy16_vaddr(dst + k * 1024, a.lat + (size_t)rr * kRowBytes + slot_col[k]);
+        const int32_t pg = btb[t / B];
+        ok = pg >= 0 && (uint32_t)pg < a.num_blocks;
       }
       return __ballot(ok);
     }
   };
 
-  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  // prologue: tiles 0 and 1 in flight
-  uint64_t vm0 = issue_tile(0);
-  uint64_t vm1 = ntiles > 1 ? issue_tile(1) : 0ull;
-  uint64_t vm2 = 0ull;
+  if (is_qk) {
+    // ================= score wave: head pair hp, dims 288 kh .. + 288 =================
+    const int hp = w >> 1, kh = w & 1;
+    const int own = 2 * hp + kh;   // local head tile whose softmax this wave finishes
+    // Barrier A of iteration t (both roles run ntiles + 1 iterations; the output waves'
+    // copies of tile t have landed).  Bare barriers: the fence of __syncthreads would also
+    // wait for the copies still in flight.
+    uint64_t vm0 = tile_mask(0);
+    uint64_t vm1 = ntiles > 1 ? tile_mask(1) : 0ull;
+    uint64_t vm2 = 0ull;
+    auto barrier_a = [&](int t) {
+      asm volatile("s_barrier" ::: "memory");
+      vm2 = t + 2 < ntiles ? tile_mask(t + 2) : 0ull;
+    };
 
-  // Iteration t of the tile loop, common part: tile t has landed for every wave, tile t+2
-  // starts.  Both roles run exactly ntiles + 1 of these.
-  auto sync_tile = [&](int t) {
-    if (t < ntiles) {
-      if (kFast && t + 1 < ntiles) wait_vmcnt<kDmaPerWave>();
-      else wait_vmcnt<0>();
-    }
-    asm volatile("s_barrier" ::: "memory");
-    vm2 = t + 2 < ntiles ? issue_tile(t + 2) : 0ull;
-  };
-
-  if (w < kQkWaves) {
-    // ================= score wave: head tile w =================
-    const int head = 16 * (kHeadTiles * hg + w) + i16;
-    // query (B operand of S^T = K Q^T): dims 32 ks + 8 g .. + 8
-    bf16x8 qreg[kKSteps];
-    {
-      const uint16_t* qrow = a.q + ((size_t)b * kHeads + head) * kDk + 8 * g;
+    const int head_p = 16 * (kHeadTiles * hg + 2 * hp) + i16;   // lane's head, tile 2 hp
+    // query (B operand of S^T = K Q^T): qreg[hh][j] = dims 32 (9 kh + j) + 8 g .. + 8 of
+    // head tile 2 hp + hh
+    bf16x8 qreg[2][kHalfSteps];
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks)
-        qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint16_t* qrow =
+          a.q + ((size_t)b * kHeads + head_p + 16 * hh) * kDk + 8 * g + 32 * kHalfSteps * kh;
+#pragma unroll
+      for (int j = 0; j < kHalfSteps; ++j)
+        qreg[hh][j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j);
     }
     // the query must have landed before the copy ring is paced by the counter alone
     wait_vmcnt<0>();
     // The query lives in AGPRs (the MFMAs read their B operand from there), leaving the
     // VGPRs to the operand ring: both roles then fit three waves per SIMD.
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+a"(qreg[ks]));
-    float m = neg_inf();   // running max (log2 units) of this lane's head
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int j = 0; j < kHalfSteps; ++j) asm volatile("" : "+a"(qreg[hh][j]));
+    float m = neg_inf();   // running max (log2 units) of this lane's head of tile `own`
     float negm = 0.f;      // -m, or 0 while m is -inf
     float ls = 0.f;        // this lane's share of the running sum of weights
     const int xk = i16 & 7;
     const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
     const int offk1 = i16 * kRowBytes + 16 * ((4 + g) ^ xk);
-    char DCP_LDS* pdst = (char DCP_LDS*)smem + kPOff + w * 1024 + lane * 16;
-    float DCP_LDS* adst = (float DCP_LDS*)(smem + kAOff) + w * 16 + i16;
+    // partial scores: written for the partner's head tile, read for the own one
+    f4 DCP_LDS* xdst = (f4 DCP_LDS*)(smem + kXOff) + ((2 * hp + 1 - kh) * 64 + lane) * 2;
+    const f4 DCP_LDS* xsrc = (const f4 DCP_LDS*)(smem + kXOff) + (own * 64 + lane) * 2;
+    u32x4 DCP_LDS* pdst = (u32x4 DCP_LDS*)(smem + kPOff) + own * 64 + lane;
+    float DCP_LDS* adst = (float DCP_LDS*)(smem + kAOff) + own * 16 + i16;
 
+    // Iteration t: phase 1 = tile t's partial scores (MFMAs) and the swap; phase 2 (after
+    // barrier B) = the online softmax of the own head tile and the hand-over of P.
     for (int t = 0; t <= ntiles; ++t) {
       wait_lgkm0();   // the previous tile's weights are in LDS before the barrier
-      sync_tile(t);
+      barrier_a(t);
+      f4 sm0 = {0.f, 0.f, 0.f, 0.f}, sm1 = {0.f, 0.f, 0.f, 0.f};   // own head tile
       if (t < ntiles) {
         const char DCP_LDS* tb = lds + (t % kNBuf) * kTileBytes;
-        f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        // s[tt][hh]: token half tt, head tile 2 hp + hh (four independent MFMA chains)
+        f4 s[2][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) s[tt][hh] = f4{0.f, 0.f, 0.f, 0.f};
         bf16x8 kop[kAheadK + 1][2];
-        auto kread = [&](int ks) {
+        auto kread = [&](int j) {
+          const int ks = kHalfSteps * kh + j;
           const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
-          kop[ks % (kAheadK + 1)][0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + o);
-          kop[ks % (kAheadK + 1)][1] =
+          kop[j % (kAheadK + 1)][0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + o);
+          kop[j % (kAheadK + 1)][1] =
               *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + 16 * kRowBytes + o);
         };
 #pragma unroll
-        for (int ks = 0; ks < kAheadK; ++ks) kread(ks);
+        for (int j = 0; j < kAheadK; ++j) kread(j);
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          if (ks + kAheadK < kKSteps) kread(ks + kAheadK);
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAheadK + 1)][0], qreg[ks], s0,
-                                                       0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks % (kAheadK + 1)][1], qreg[ks], s1,
-                                                       0, 0, 0);
+        for (int j = 0; j < kHalfSteps; ++j) {
+          if (j + kAheadK < kHalfSteps) kread(j + kAheadK);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              s[tt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (kAheadK + 1)][tt],
+                                                                  qreg[hh][j], s[tt][hh], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
+        // hand the partner's head tile over; keep the own one
+        xdst[0] = kh ? s[0][0] : s[0][1];
+        xdst[1] = kh ? s[1][0] : s[1][1];
+        sm0 = kh ? s[0][1] : s[0][0];
+        sm1 = kh ? s[1][1] : s[1][0];
+      }
+      wait_lgkm0();   // the partial scores are in LDS before the mid barrier
+      asm volatile("s_barrier" ::: "memory");   // barrier B
+      if (t < ntiles) {
+        const f4 s0 = sm0 + xsrc[0];
+        const f4 s1 = sm1 + xsrc[1];
         // scores: x[i] is token 4 g + i, x[4 + i] token 16 + 4 g + i; masked rows -> -inf
         float x[8];
         {
@@ -361,16 +394,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
           m = tmax;
           negm = -tmax;
         }
-        float p[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], a.sl2, negm));
-        ls = ls * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(x[i], a.sl2, negm));
+        ls = ls * alpha + (((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7])));
         // B operand of O^T += V^T P^T: k slots 8 g .. 8 g + 7 = tokens 4 g + [0, 4) and
-        // 16 + 4 g + [0, 4); the output lane with the same index reads these 16 bytes
-        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        *reinterpret_cast<u32x4 DCP_LDS*>(pdst + (t & 1) * (kHeadTiles * 1024)) = pw;
-        if (g == 0) adst[(t & 1) * (kHeadTiles * 16)] = alpha;
+        // 16 + 4 g + [0, 4); the output lanes with the same index read these 16 bytes
+        *pdst = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        if (g == 0) *adst = alpha;
       }
       vm0 = vm1;
       vm1 = vm2;
@@ -388,93 +419,198 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : neg_inf();
     if (g == 0) {
-      ((float DCP_LDS*)(smem + kFOff))[w * 16 + i16] = inv;
+      const int head = head_p + 16 * kh;
+      ((float DCP_LDS*)(smem + kFOff))[own * 16 + i16] = inv;
       if (single) a.lse_out[(size_t)b * kHeads + head] = lse;
       else a.plse[(size_t)item * kHeads + head] = lse;
     }
     wait_lgkm0();
     asm volatile("s_barrier" ::: "memory");
   } else {
-    // ================= output wave: head tile ht, value dims 256 half .. + 256 ==========
+    // ============ output wave: head pair hp, value dims 128 dq .. + 128 ============
     const int pv = w - kQkWaves;
-    const int ht = pv >> 1;
-    const int half = pv & 1;
-    const int head = 16 * (kHeadTiles * hg + ht) + i16;
+    const int hp = pv >> 2, dq = pv & 3;
+    // ---- HBM -> LDS tile copies, all issued by the output waves.  A tile is 36 slots of
+    // 1 KiB (64 lanes x 16 B); slot s, lane l holds chunk (q mod 72) ^ (row & 7) of tile row
+    // q / 72, q = 64 s + l.  Output wave p copies 5 slots from 5p (p < 4) or 4 slots from
+    // 20 + 4 (p - 4).
+    const int pvw = w - kQkWaves;
+    const int slot0 = pvw < 4 ? kSlotsHi * pvw : 4 * kSlotsHi + kSlotsLo * (pvw - 4);
+    const int nslots = is_qk ? 0 : (pvw < 4 ? kSlotsHi : kSlotsLo);
+    uint32_t slot_off[kSlotsHi], slot_col[kSlotsHi];
+    int slot_row[kSlotsHi];
+#pragma unroll
+    for (int k = 0; k < kSlotsHi; ++k) {
+      const int sl = max(slot0 + k, 0) * 64 + lane;
+      const int r = min(sl / kRowChunks, kTile - 1);   // slots a wave does not copy: unused
+      slot_row[k] = r;
+      slot_col[k] = (uint32_t)(((sl - r * kRowChunks) ^ (r & 7)) * 16);
+      slot_off[k] = (uint32_t)r * kRowBytes + slot_col[k];
+    }
+    // all of this wave's copies of tile ti; returns the mask of valid rows
+    auto issue_tile = [&](int ti) -> uint64_t {
+      const uint32_t dst = lds_addr + (uint32_t)((ti % kNBuf) * kTileBytes + slot0 * 1024);
+      if constexpr (kFast) {
+        const TileSrc ts = tile_src(ti);
+#pragma unroll
+        for (int k = 0; k < kSlotsHi; ++k) {
+          if (k < nslots) {
+            const uint32_t voff =
+                ts.full ? slot_off[k] : (slot_off[k] < ts.lim ? slot_off[k] : slot_col[k]);
+            copy16_sbase(dst + k * 1024, voff, ts.base);
+          }
+        }
+        return vm_new;
+      } else {
+        // general tiles: each lane walks one token
+        const int j = j0 + ti * kTile + lane;
+        bool ok = lane < kTile && j < j1;
+        bool bad = false;
+        uint32_t lrow = 0;
+        if (ok) {
+          const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
+          const uint32_t lp = t / B;
+          const int32_t pg = btb[lp];
+          if (pg < 0 || (uint32_t)pg >= a.num_blocks) {
+            ok = false;
+            bad = true;
+          } else {
+            lrow = (uint32_t)pg * B + (t - lp * B);
+          }
+        }
+        if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
+#pragma unroll
+        for (int k = 0; k < kSlotsHi; ++k) {
+          if (k < nslots) {
+            const uint32_t rr = __shfl(lrow, slot_row[k], 64);
+            copy16_vaddr(dst + k * 1024, a.lat + (size_t)rr * kRowBytes + slot_col[k]);
+          }
+        }
+        return __ballot(ok);
+      }
+    };
+
+    // prologue: tiles 0 and 1 in flight
+    (void)issue_tile(0);
+    if (ntiles > 1) (void)issue_tile(1);
+
+    // Barrier A of iteration t: this wave's copies of tile t have landed (those of tile t+1
+    // may still fly), then every wave's have; tile t+2 starts.  Bare barriers: the fence of __syncthreads would also wait for the copies
+    // still in flight.
+    auto barrier_a = [&](int t) {
+      if (t < ntiles) {
+        if (kFast && t + 1 < ntiles) {
+          if (nslots == kSlotsHi) wait_vmcnt<kSlotsHi>();
+          else wait_vmcnt<kSlotsLo>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      }
+      asm volatile("s_barrier" ::: "memory");
+      if (t + 2 < ntiles) (void)issue_tile(t + 2);
+    };
+
+
+    const int head_p = 16 * (kHeadTiles * hg + 2 * hp) + i16;   // lane's head, tile 2 hp
     // Every definition of an accumulator comes out of an AGPR-constrained asm statement,
     // so the register allocator keeps the loop-carried accumulators in AGPRs.
-    f4 acc[kDvHalfTiles];
+    f4 acc[2][kQuarterTiles];
 #pragma unroll
-    for (int i = 0; i < kDvHalfTiles; ++i) {
-      acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-      asm volatile("" : "+a"(acc[i]));
-    }
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < kQuarterTiles; ++i) {
+        acc[hh][i] = f4{0.f, 0.f, 0.f, 0.f};
+        asm volatile("" : "+a"(acc[hh][i]));
+      }
     // Wait states between the last accumulator MFMAs and VALU reads of the accumulators;
     // every accumulator passes through an AGPR-constrained statement here, so the reads
     // cannot be hoisted above it.
     auto settle_acc = [&]() {
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                   : "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]),
-                     "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
+                   : "+a"(acc[0][4]), "+a"(acc[0][5]), "+a"(acc[0][6]), "+a"(acc[0][7]),
+                     "+a"(acc[1][4]), "+a"(acc[1][5]), "+a"(acc[1][6]), "+a"(acc[1][7]));
       asm volatile(""
-                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]),
-                     "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]));
+                   : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                     "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
     };
-    // V^T operand (A of O^T = V^T P^T) for value-dim tile dt of this wave's half
+    // V^T operand (A of O^T = V^T P^T) for value-dim tile dt of this wave's quarter
     const int rv = 4 * g + (i16 >> 2);
     const int xv = rv & 7;
     const int qv = (i16 >> 1) & 1;
     int offv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8 + half * 512;
-    const char DCP_LDS* psrc = lds + kPOff + ht * 1024 + lane * 16;
-    const float DCP_LDS* asrc = (const float DCP_LDS*)(smem + kAOff) + ht * 16 + i16;
+      offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8 + dq * 256;
+    const u32x4 DCP_LDS* psrc = (const u32x4 DCP_LDS*)(smem + kPOff) + 2 * hp * 64 + lane;
+    const float DCP_LDS* asrc = (const float DCP_LDS*)(smem + kAOff) + 2 * hp * 16 + i16;
 
+    // Iteration t: phase 1 = P of tile t-1 (written by the score waves in phase 2 of the
+    // previous iteration), the rescale, and the first kPhase1Tiles dv tiles; phase 2 = the
+    // other dv tiles, while the score waves run the softmax.
     for (int t = 0; t <= ntiles; ++t) {
-      sync_tile(t);
+      barrier_a(t);
+      const int u = t - 1;
+      const char DCP_LDS* tb = lds + ((u + kNBuf) % kNBuf) * kTileBytes;
+      auto vop = [&](int dt) -> bf16x8 {
+        const int o = offv[dt & 3] + 128 * (dt >> 2);
+        const u32x2 v0 = lds_tr16(tb + o);
+        const u32x2 v1 = lds_tr16(tb + 16 * kRowBytes + o);
+        return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
+      };
+      bf16x8 pb0, pb1;
+      bf16x8 va[kAheadV + 1];
       if (t >= 1) {
-        const int u = t - 1;   // the tile whose weights the score waves wrote last
-        const char DCP_LDS* tb = lds + (u % kNBuf) * kTileBytes;
-        auto vop = [&](int dt) -> bf16x8 {
-          const int o = offv[dt & 3] + 128 * (dt >> 2);
-          const u32x2 v0 = lds_tr16(tb + o);
-          const u32x2 v1 = lds_tr16(tb + 16 * kRowBytes + o);
-          return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
-        };
-        const bf16x8 pb =
-            *reinterpret_cast<const bf16x8 DCP_LDS*>(psrc + (u & 1) * (kHeadTiles * 1024));
-        const float alpha = asrc[(u & 1) * (kHeadTiles * 16)];
-        bf16x8 va[kAheadV + 1];
+        pb0 = __builtin_bit_cast(bf16x8, psrc[0]);
+        pb1 = __builtin_bit_cast(bf16x8, psrc[64]);
+        const float alpha0 = asrc[0], alpha1 = asrc[16];
 #pragma unroll
         for (int dt = 0; dt < kAheadV; ++dt) va[dt] = vop(dt);
-        if (__ballot(alpha != 1.f) != 0) {
+        if (__ballot(alpha0 != 1.f || alpha1 != 1.f) != 0) {
           settle_acc();
 #pragma unroll
-          for (int i = 0; i < kDvHalfTiles; ++i) {
-            acc[i] *= alpha;
-            asm volatile("" : "+a"(acc[i]));
+          for (int i = 0; i < kQuarterTiles; ++i) {
+            acc[0][i] *= alpha0;
+            acc[1][i] *= alpha1;
+            asm volatile("" : "+a"(acc[0][i]), "+a"(acc[1][i]));
           }
         }
 #pragma unroll
-        for (int dt = 0; dt < kDvHalfTiles; ++dt) {
-          if (dt + kAheadV < kDvHalfTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
-          if (dt == 0) mfma_acc<true>(acc[dt], va[dt % (kAheadV + 1)], pb);
-          else mfma_acc<false>(acc[dt], va[dt % (kAheadV + 1)], pb);
+        for (int dt = 0; dt < kPhase1Tiles; ++dt) {
+          if (dt + kAheadV < kQuarterTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
+          if (dt == 0) mfma_acc<true>(acc[0][dt], va[dt % (kAheadV + 1)], pb0);
+          else mfma_acc<false>(acc[0][dt], va[dt % (kAheadV + 1)], pb0);
+          mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      asm volatile("s_barrier" ::: "memory");   // barrier B
+      if (t >= 1) {
+#pragma unroll
+        for (int dt = kPhase1Tiles; dt < kQuarterTiles; ++dt) {
+          if (dt + kAheadV < kQuarterTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
+          mfma_acc<false>(acc[0][dt], va[dt % (kAheadV + 1)], pb0);
+          mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb1);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
     asm volatile("s_barrier" ::: "memory");
-    // ---- finalize: lane holds dims 256 half + 16 dt + 4 g + [0, 4) of its head
-    const float inv = ((const float DCP_LDS*)(smem + kFOff))[ht * 16 + i16];
+    // ---- finalize: lane holds dims 128 dq + 16 dt + 4 g + [0, 4) of its heads
+    const float inv0 = ((const float DCP_LDS*)(smem + kFOff))[2 * hp * 16 + i16];
+    const float inv1 = ((const float DCP_LDS*)(smem + kFOff))[(2 * hp + 1) * 16 + i16];
     settle_acc();
-    float* dst = (single ? a.o_out + ((size_t)b * kHeads + head) * kDv
-                         : a.po + ((size_t)item * kHeads + head) * kDv) +
-                 half * 256;
 #pragma unroll
-    for (int dt = 0; dt < kDvHalfTiles; ++dt) {
-      const f4 v = acc[dt] * inv;
-      *reinterpret_cast<f4*>(dst + 16 * dt + 4 * g) = v;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int head = head_p + 16 * hh;
+      float* dst = (single ? a.o_out + ((size_t)b * kHeads + head) * kDv
+                           : a.po + ((size_t)item * kHeads + head) * kDv) +
+                   dq * 128;
+      const float inv = hh ? inv1 : inv0;
+#pragma unroll
+      for (int dt = 0; dt < kQuarterTiles; ++dt) {
+        const f4 v = acc[hh][dt] * inv;
+        *reinterpret_cast<f4*>(dst + 16 * dt + 4 * g) = v;
+      }
     }
   }
 }
