@@ -59,15 +59,15 @@ struct Plan {
 };
 
 // Work items: the planner splits the shard's tokens into about `target` items (never more
-// than target + batch), enough to cover every CU a few times (GQA: one 4-wave workgroup per
-// item and KV head; MLA: two 4-wave workgroups, one per half of the heads, per item).
+// than target + batch), about one round of workgroups over the CUs (GQA: one workgroup per
+// item and KV head; MLA: two workgroups, one per half of the heads, per item).
 bool make_plan(const dcp_attn_desc* d, int batch, Plan* p) {
   const int cus = device_cus();
   if (cus <= 0) return false;
   if (d->kind == DCP_GQA) {
     p->tile = dcp::kGqaTile;
-    // two resident 4-wave workgroups per CU, about two rounds of them
-    p->target = std::max<int64_t>(1, (int64_t)cus * 4 / d->num_kv_heads);
+    // two resident workgroups (64 KiB double buffer each) per CU and KV head, one round
+    p->target = std::max<int64_t>(1, (int64_t)cus * 2 / d->num_kv_heads);
     p->min_chunk = 4 * dcp::kGqaTile;
   } else {
     // two head-group workgroups per item, one resident workgroup per CU (144 KiB of LDS)

@@ -8,28 +8,33 @@
 // into exact attention.
 //
 // The work is HBM-bound (per token and KV head: 2 * D * sizeof(T) bytes against
-// 4 * G * D flops), so the design is about streaming K and V at full rate on the vector
-// ALUs:
-//   * One workgroup of NW = min(G, 4) waves per work item (request, KV head, local token
-//     range); wave w owns G / NW of the query heads that share the KV head.
-//   * 64-token tiles of K and V rows are copied HBM -> LDS with global_load_lds_dwordx4
-//     (no register staging), double buffered so that tile i+1 streams in while tile i is
-//     computed.  The block-table walk gives each lane the cache row of one token; when the
-//     64 rows are consecutive in memory (the common case: interleave and block size are
-//     multiples of the tile) the copy addresses are plain offsets, otherwise each row
-//     index comes from the lane that walked it.  The 16-byte chunks of a K row are
-//     XOR-swizzled by (row mod 16) so the transposed reads below are conflict free.
-//   * Scores: lane = token.  The lane pulls its K row from LDS into registers once, and
-//     each query head, being wave-uniform, arrives as whole-row scalar loads used as the
-//     scalar operand of v_dot2_f32_bf16 (bf16) or v_fma_f32 (f32): no cross-lane
-//     reduction.
+// 4 * G * D flops), so the design is about keeping enough K / V bytes in flight and
+// streaming them at full rate on the vector ALUs:
+//   * One workgroup of NW = min(G, 8) waves per work item (request, KV head, local token
+//     range), one workgroup per CU; wave w owns G / NW of the query heads that share the
+//     KV head.
+//   * 64-token tiles of K and V rows are copied HBM -> LDS by global_load_lds_dwordx4 (no
+//     register staging) into a 4-deep ring: three tiles (96 KiB) in flight while one is
+//     computed.  The copies are issued from inline assembly and paced by explicit
+//     vector-memory counter waits plus a bare s_barrier, so the compiler never drains them
+//     before LDS reads of the other buffers.  When the interleave and the block size are
+//     multiples of the tile, a tile is one run of consecutive cache rows: a per-wave table
+//     (lane k = first row of tile 64 * window + k) locates it with one readlane and the
+//     copies are a scalar base plus fixed lane offsets; otherwise each lane walks one
+//     token.  The 16-byte chunks of a K row are XOR-swizzled by (row mod 16) so the
+//     transposed reads below are conflict free.
+//   * Scores: lane = token.  The lane pulls its K row from LDS into registers once; each
+//     query head, being wave-uniform, sits in scalar registers (loaded once when a wave
+//     owns one head, streamed in 16-dword chunks otherwise) and is the scalar operand of
+//     v_dot2_f32_bf16 (bf16) or v_fma_f32 (f32): no cross-lane reduction.
 //   * Online softmax in base 2 (scale * log2 e folded into the scores).  The tile max per
 //     head is a DPP butterfly plus four lane reads (no LDS); running sums stay per lane and
 //     are reduced once per item.
-//   * P.V: lane = one dword of every V row (2 bf16 dims or 1 f32 dim).  For bf16 the V
-//     values of token pairs (2k, 2k+1) are packed with v_perm_b32 and combined with the
-//     bf16-rounded weight pairs by v_dot2_f32_bf16 into fp32 accumulators; the weights are
-//     broadcast through LDS.
+//   * P.V: lane = (token group r = lane / 16, 16-byte chunk c = lane % 16 of the V row), so
+//     one ds_read_b128 brings four V rows.  For bf16 the rows of tokens t and t + 4 are
+//     paired with v_perm_b32 and combined with the bf16-rounded weight pair by
+//     v_dot2_f32_bf16 into fp32 accumulators (8 dims per lane); the four token groups are
+//     summed across rows once per item.
 //   * An item that covers a request's whole shard writes (O, lse) directly; otherwise it
 //     writes a normalized partial that the split combine merges.
 #include "launch.h"
@@ -41,14 +46,16 @@ namespace {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(16))) uint32_t u32x16;
+
 #define DCP_LDS __attribute__((address_space(3)))
 #define DCP_CONST __attribute__((address_space(4)))
 
 constexpr int kTile = kGqaTile;      // tokens per tile (= lanes)
 constexpr int kRowBytes = 256;       // D * sizeof(T) for the supported shapes
 constexpr int kChunks = kRowBytes / 16;
-constexpr int kTileBytes = kTile * kRowBytes;   // 16 KiB
-constexpr int kDmaPerTile = kTileBytes / 1024;  // 1 KiB per copy instruction
+constexpr int kTileBytes = kTile * kRowBytes;   // 16 KiB of K (and of V) per tile
+constexpr int kNBuf = 2;                         // double buffer: one computed, one in flight
+constexpr int kSlots = 2 * kTileBytes / 1024;   // 1-KiB copies per tile (K then V)
 
 struct GqaKArgs {
   const void* q;
@@ -73,7 +80,31 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-constexpr int waves_for(int g) { return g >= 4 ? 4 : g; }
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((kVm & 0xF) | ((kVm >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 16-byte-per-lane HBM -> LDS copy: LDS bytes [lds + 16 lane, + 16) <- global
+// sbase + voff (scalar base, 32-bit lane offset).  M0 carries the LDS address; one wait
+// state separates its write from the copy that reads it.
+__device__ __forceinline__ void copy16_sbase(uint32_t lds, uint32_t voff, const char* sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+// The same from a per-lane 64-bit address.
+__device__ __forceinline__ void copy16_vaddr(uint32_t lds, const char* src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+constexpr int waves_for(int g) { return g >= 8 ? 8 : g; }
+constexpr int kDppRowShl4 = 0x104;   // lane i <- lane i + 4 within each 16-lane row
 
 template <bool kBf16, int G>
 __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArgs a) {
@@ -81,13 +112,13 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
   constexpr int HPW = G / NW;                   // query heads per wave
   constexpr int kElemBytes = kBf16 ? 2 : 4;
   constexpr int D = kRowBytes / kElemBytes;     // head dim
-  constexpr int NA = kBf16 ? 2 : 1;             // accumulators per lane per head
-  constexpr int kDmaPerWave = kDmaPerTile / NW;
-  constexpr int kPWords = kBf16 ? kTile / 2 : kTile;  // weight slots per head per tile
+  constexpr int NA = kBf16 ? 8 : 4;             // dims (accumulators) per lane per head
+  constexpr int kDmaPerWave = kSlots / NW;
+  constexpr int kPWords = kBf16 ? kTile / 2 : kTile;  // weight words per head per tile
 
   // [buffer][K, V][row * 16 + chunk]
-  __shared__ u32x4 kv[2][2][kTile * kChunks];
-  __shared__ uint32_t pbuf[NW][kPWords * HPW];
+  __shared__ u32x4 kv[kNBuf][2][kTile * kChunks];
+  __shared__ uint32_t pbuf[NW][HPW][kPWords];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -104,6 +135,9 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
                                  ((size_t)b * a.hq + head0) * (kRowBytes / 4);
   const int32_t* btb = a.bt + (size_t)b * a.max_blocks;
   const uint32_t B = (uint32_t)a.block_size;
+  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+  const bool fast = (a.interleave % kTile) == 0 && (a.block_size % kTile) == 0;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(const char DCP_LDS*)&kv[0][0][0];
 
   float m[HPW], ls[HPW], acc[HPW][NA];
 #pragma unroll
@@ -114,113 +148,188 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     for (int k = 0; k < NA; ++k) acc[h][k] = 0.f;
   }
 
-  // ---- block-table walk: lane = local token tj + lane
-  auto page_of = [&](int tj) -> int32_t {
-    const int j = tj + lane;
-    if (j >= j1) return 0;
-    const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-    return btb[t / B];
+  // ---- copy slots of this wave: slot s = w * kDmaPerWave + k; s < 16 copies K, s >= 16 V.
+  // 16-byte position q = (s mod 16) * 64 + lane of the tile holds row q / 16, chunk q mod 16
+  // (K: source chunk (q mod 16) ^ (row & 15), V: as it is).
+  uint32_t slot_src[kDmaPerWave];
+  int slot_row[kDmaPerWave];
+#pragma unroll
+  for (int k = 0; k < kDmaPerWave; ++k) {
+    const int sl = w * kDmaPerWave + k;
+    const int q = (sl % 16) * 64 + lane;
+    const int r = q / kChunks, pc = q % kChunks;
+    slot_row[k] = r;
+    slot_src[k] = (uint32_t)((sl < 16 ? (pc ^ (r & 15)) : pc) * 16);
+  }
+
+  // ---- tile sources (contiguous tiles): lane k = first cache row of tile 64 * window + k,
+  // or ~0 for a bad page; rebuilt once per 64 tiles
+  uint32_t row_tab = 0;
+  auto build_table = [&](int win) {
+    const int tt = win * 64 + lane;
+    bool bad = false;
+    uint32_t row = ~0u;
+    if (tt < ntiles) {
+      const uint32_t t = dcp_walk_global_pos((uint32_t)(j0 + tt * kTile), a.rank, a.cp,
+                                             a.interleave);
+      const uint32_t lp = t / B;
+      const int32_t pg = btb[lp];
+      if (pg < 0 || (uint32_t)pg >= a.num_blocks) bad = true;
+      else row = ((uint32_t)pg * a.hkv + kvh) * B + (t - lp * B);
+    }
+    if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
+    row_tab = row;
   };
-  // cache row (page * Hkv + kvh) * B + slot of the lane's token; ballot of valid tokens
-  auto row_of = [&](int tj, int32_t pg, uint32_t& row) -> uint64_t {
-    const int j = tj + lane;
+  if (fast) build_table(0);
+
+  // ---- contiguous tiles: where tile ti comes from (rb = byte offset of its first row;
+  // rows at or past lim re-read row 0, their tokens being masked), and one of this wave's
+  // copies of it
+  struct TileSrc {
+    size_t rb;
+    uint32_t lim;
+    uint32_t dst;
+  };
+  auto locate = [&](int ti, uint64_t& vm) -> TileSrc {
+    if ((ti & 63) == 0 && ti > 0) build_table(ti >> 6);
+    const int nvalid = min(kTile, j1 - (j0 + ti * kTile));
+    const uint32_t row0 = __builtin_amdgcn_readlane(row_tab, ti & 63);
+    const bool ok = row0 != ~0u;
+    vm = ok ? (nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1)) : 0ull;
+    TileSrc ts;
+    ts.rb = (size_t)(ok ? row0 : 0u) * kRowBytes;
+    ts.lim = ok ? (uint32_t)nvalid : 0u;
+    ts.dst = lds_addr + (uint32_t)((ti % kNBuf) * 2 * kTileBytes);
+    return ts;
+  };
+  auto copy_slot = [&](const TileSrc& ts, int k) {
+    const int sl = w * kDmaPerWave + k;
+    const uint32_t voff = (uint32_t)slot_row[k] < ts.lim
+                              ? (uint32_t)slot_row[k] * kRowBytes + slot_src[k]
+                              : slot_src[k];
+    copy16_sbase(ts.dst + (uint32_t)(sl * 1024), voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
+  };
+  // ---- all of this wave's HBM -> LDS copies of tile ti; returns the mask of valid tokens
+  auto issue_tile = [&](int ti) -> uint64_t {
+    const uint32_t dst = lds_addr + (uint32_t)((ti % kNBuf) * 2 * kTileBytes);
+    if (fast) {
+      uint64_t vm;
+      const TileSrc ts = locate(ti, vm);
+#pragma unroll
+      for (int k = 0; k < kDmaPerWave; ++k) copy_slot(ts, k);
+      return vm;
+    }
+    // general tiles: each lane walks one token; the copies take the row of their token
+    const int j = j0 + ti * kTile + lane;
     bool ok = j < j1;
     bool bad = false;
-    row = 0;
+    uint32_t row = 0;
     if (ok) {
+      const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
+      const uint32_t lp = t / B;
+      const int32_t pg = btb[lp];
       if (pg < 0 || (uint32_t)pg >= a.num_blocks) {
         ok = false;
         bad = true;
       } else {
-        const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-        row = ((uint32_t)pg * a.hkv + kvh) * B + t % B;
+        row = ((uint32_t)pg * a.hkv + kvh) * B + (t - lp * B);
       }
     }
     if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
-    return __ballot(ok);
-  };
-  // ---- HBM -> LDS copy of the K and V rows of one tile (this wave's share)
-  char* lds_base = reinterpret_cast<char*>(&kv[0][0][0]);
-  asm volatile("" : "+v"(lds_base));
-  auto issue_tile = [&](int buf, uint32_t row) {
-    const uint32_t row0 = __builtin_amdgcn_readfirstlane(row);
-    const bool contig = __ballot(row == row0 + (uint32_t)lane) == ~0ull;
-    const int pc = lane & (kChunks - 1);
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
-      const int blk = w * kDmaPerWave + k;
-      const int r = blk * (64 / kChunks) + lane / kChunks;  // tile row of this lane's slot
-      const uint32_t rr = contig ? row0 + r : __shfl(row, r, 64);
-      const size_t rb = (size_t)rr * kRowBytes;
-      // K chunks XOR-swizzled (read transposed below), V rows stored as they are (read
-      // row-wise: consecutive lanes hit consecutive banks)
-      // the destination is formed from an opaque byte base so that the compiler does not
-      // treat the copy as aliasing the tile being read (which would make every read wait
-      // for the copy of the next tile); the loop's own wait + barrier order the buffers
-      char* kd = lds_base + ((buf * 2 + 0) * kTileBytes + blk * 1024);
-      char* vd = lds_base + ((buf * 2 + 1) * kTileBytes + blk * 1024);
-      __builtin_amdgcn_global_load_lds(a.kp + rb + ((pc ^ (r & 15)) * 16), (void DCP_LDS*)kd, 16,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds(a.vp + rb + pc * 16, (void DCP_LDS*)vd, 16, 0, 0);
+      const int sl = w * kDmaPerWave + k;
+      const uint32_t rr = __shfl(row, slot_row[k], 64);
+      copy16_vaddr(dst + (uint32_t)(sl * 1024),
+                   (sl < 16 ? a.kp : a.vp) + (size_t)rr * kRowBytes + slot_src[k]);
     }
+    return __ballot(ok);
   };
 
-  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  uint32_t row;
-  uint64_t vm_cur = row_of(j0, page_of(j0), row);
-  issue_tile(0, row);
-  int32_t pg_next = ntiles > 1 ? page_of(j0 + kTile) : 0;
+  // query of a single head per wave: loaded once into scalar registers
+  constexpr bool kQResident = HPW == 1;
+  u32x16 qres[kChunks / 4];
+  if constexpr (kQResident) {
+#pragma unroll
+    for (int c = 0; c < kChunks / 4; ++c)
+      qres[c] = *reinterpret_cast<const u32x16 DCP_CONST*>(qh + 16 * c);
+  }
 
+  // prologue: tile 0 in flight
+  uint64_t vm0 = issue_tile(0);
+
+  const int pr = lane >> 4, pcl = lane & 15;   // P.V lane: token group, row chunk
   for (int ti = 0; ti < ntiles; ++ti) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int tj = j0 + ti * kTile;
-    uint64_t vm_next = 0;
-    if (ti + 1 < ntiles) {
-      vm_next = row_of(tj + kTile, pg_next, row);
-      issue_tile((ti + 1) & 1, row);
-      if (ti + 2 < ntiles) pg_next = page_of(tj + 2 * kTile);
-    }
-    const u32x4* kt = kv[ti & 1][0];
-    const uint32_t* vt = reinterpret_cast<const uint32_t*>(kv[ti & 1][1]);
+    // this wave's copies of tile ti have landed; after the barrier every wave's have, and
+    // tile ti-1 is free for tile ti+1.  A bare barrier: the fence of __syncthreads would
+    // also wait for LDS traffic that needs no ordering here.
+    wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+    const uint64_t vm1 = ti + 1 < ntiles ? issue_tile(ti + 1) : 0ull;
+    const u32x4* kt = kv[ti % kNBuf][0];
+    const u32x4* vt = kv[ti % kNBuf][1];
 
-    // ---- scores: lane = token; the K row moves to registers once
-    u32x4 krow[kChunks];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) krow[c] = kt[lane * kChunks + (c ^ (lane & 15))];
-    // 16 query dwords per scalar load, one load ahead of its use; each step is its own
-    // scheduling region so that no more than two chunks (32 scalar registers) are live
-    constexpr int kQSteps = HPW * (kChunks / 4);
-    auto qload = [&](int st) -> u32x16 {
-      uint64_t qa = reinterpret_cast<uint64_t>(qh + (st / (kChunks / 4)) * (kRowBytes / 4) +
-                                               16 * (st % (kChunks / 4)));
-      asm volatile("" : "+s"(qa));
-      return *reinterpret_cast<const u32x16 DCP_CONST*>(qa);
-    };
+    // ---- scores: lane = token
     float s[HPW];
-    float sacc[HPW][2];
+    if constexpr (kQResident) {
+      // the K row moves to registers in two halves (32 VGPRs each)
+      float s2[2] = {0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < HPW; ++h) sacc[h][0] = sacc[h][1] = 0.f;
-    u32x16 qv[2];
-    qv[0] = qload(0);
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 kr[kChunks / 2];
 #pragma unroll
-    for (int st = 0; st < kQSteps; ++st) {
-      if (st + 1 < kQSteps) qv[(st + 1) & 1] = qload(st + 1);
-      const int h = st / (kChunks / 4), qc = st % (kChunks / 4);
+        for (int c = 0; c < kChunks / 2; ++c) {
+          const int cc = hf * (kChunks / 2) + c;
+          kr[c] = kt[lane * kChunks + (cc ^ (lane & 15))];
+        }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t kd = krow[4 * qc + e / 4][e % 4];
-        float& dst = sacc[h][e & 1];
-        if constexpr (kBf16) dst = dot2_bf16(qv[st & 1][e], kd, dst);
-        else dst = fmaf(__uint_as_float(qv[st & 1][e]), __uint_as_float(kd), dst);
+        for (int c = 0; c < kChunks / 8; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t kd = kr[4 * c + e / 4][e % 4];
+            const uint32_t qd = qres[hf * (kChunks / 8) + c][e];
+            if constexpr (kBf16) s2[e & 1] = dot2_bf16(qd, kd, s2[e & 1]);
+            else s2[e & 1] = fmaf(__uint_as_float(qd), __uint_as_float(kd), s2[e & 1]);
+          }
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      s[0] = s2[0] + s2[1];
+    } else {
+      u32x4 krow[kChunks];
 #pragma unroll
-    for (int h = 0; h < HPW; ++h) s[h] = sacc[h][0] + sacc[h][1];
+      for (int c = 0; c < kChunks; ++c) krow[c] = kt[lane * kChunks + (c ^ (lane & 15))];
+      // 16 query dwords per scalar load, one load ahead of its use; each step is its own
+      // scheduling region so that no more than two chunks (32 scalar registers) are live
+      constexpr int kQSteps = HPW * (kChunks / 4);
+      auto qload = [&](int st) -> u32x16 {
+        uint64_t qa = reinterpret_cast<uint64_t>(qh + (st / (kChunks / 4)) * (kRowBytes / 4) +
+                                                 16 * (st % (kChunks / 4)));
+        asm volatile("" : "+s"(qa));
+        return *reinterpret_cast<const u32x16 DCP_CONST*>(qa);
+      };
+      float sacc[HPW][2];
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) sacc[h][0] = sacc[h][1] = 0.f;
+      u32x16 qv[2];
+      qv[0] = qload(0);
+#pragma unroll
+      for (int st = 0; st < kQSteps; ++st) {
+        if (st + 1 < kQSteps) qv[(st + 1) & 1] = qload(st + 1);
+        const int h = st / (kChunks / 4), qc = st % (kChunks / 4);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t kd = krow[4 * qc + e / 4][e % 4];
+          float& dst = sacc[h][e & 1];
+          if constexpr (kBf16) dst = dot2_bf16(qv[st & 1][e], kd, dst);
+          else dst = fmaf(__uint_as_float(qv[st & 1][e]), __uint_as_float(kd), dst);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) s[h] = sacc[h][0] + sacc[h][1];
+    }
 
-    // ---- online softmax (base 2); weights to LDS for the P.V broadcast
-    const bool valid = (vm_cur >> lane) & 1;
+    // ---- online softmax (base 2); weights to LDS for the P.V lanes
+    const bool valid = (vm0 >> lane) & 1;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
       const float x = valid ? s[h] * a.sl2 : neg_inf();
@@ -235,56 +344,77 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
 #pragma unroll
       for (int k = 0; k < NA; ++k) acc[h][k] *= alpha;
       if constexpr (kBf16) {
-        // pair (2k, 2k+1) as one bf16x2 word, written by the even lane
+        // tokens t and t + 4 (t mod 8 < 4) as one bf16x2 word, written by lane t
         const uint32_t pb = f32_to_bf16_rne(p);
-        const uint32_t pn = (uint32_t)__builtin_amdgcn_update_dpp((int)pb, (int)pb, kDppQuadXor1,
+        const uint32_t pn = (uint32_t)__builtin_amdgcn_update_dpp((int)pb, (int)pb, kDppRowShl4,
                                                                   0xF, 0xF, false);
-        if (!(lane & 1)) pbuf[w][(lane >> 1) * HPW + h] = pb | (pn << 16);
+        if (!(lane & 4)) pbuf[w][h][(lane >> 3) * 4 + (lane & 3)] = pb | (pn << 16);
       } else {
-        pbuf[w][lane * HPW + h] = __float_as_uint(p);
+        pbuf[w][h][lane] = __float_as_uint(p);
       }
     }
 
-    // ---- P.V: lane = one dword of every V row
+    // ---- P.V: lane = (token group pr, 16-byte chunk pcl of the V row)
     if constexpr (kBf16) {
 #pragma unroll
-      for (int k = 0; k < kTile / 2; ++k) {
-        const uint32_t v0 = vt[(2 * k) * (kRowBytes / 4) + lane];
-        const uint32_t v1 = vt[(2 * k + 1) * (kRowBytes / 4) + lane];
-        const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
+      for (int k2 = 0; k2 < kTile / 8; ++k2) {
+        const u32x4 v0 = vt[(8 * k2 + pr) * kChunks + pcl];
+        const u32x4 v1 = vt[(8 * k2 + 4 + pr) * kChunks + pcl];
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
-          const uint32_t pp = pbuf[w][k * HPW + h];
-          acc[h][0] = dot2_bf16(pp, lo, acc[h][0]);
-          acc[h][1] = dot2_bf16(pp, hi, acc[h][1]);
+          const uint32_t pp = pbuf[w][h][k2 * 4 + pr];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[h][2 * i] = dot2_bf16(pp, __builtin_amdgcn_perm(v1[i], v0[i], 0x05040100u),
+                                      acc[h][2 * i]);
+            acc[h][2 * i + 1] = dot2_bf16(pp, __builtin_amdgcn_perm(v1[i], v0[i], 0x07060302u),
+                                          acc[h][2 * i + 1]);
+          }
         }
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < kTile; ++t) {
-        const float v = __uint_as_float(vt[t * (kRowBytes / 4) + lane]);
+      for (int k = 0; k < kTile / 4; ++k) {
+        const u32x4 v = vt[(4 * k + pr) * kChunks + pcl];
 #pragma unroll
-        for (int h = 0; h < HPW; ++h)
-          acc[h][0] = fmaf(__uint_as_float(pbuf[w][t * HPW + h]), v, acc[h][0]);
+        for (int h = 0; h < HPW; ++h) {
+          const float pp = __uint_as_float(pbuf[w][h][4 * k + pr]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(pp, __uint_as_float(v[i]), acc[h][i]);
+        }
       }
     }
-    vm_cur = vm_next;
+    vm0 = vm1;
   }
 
-  // ---- finalize: O = acc / l, lse = (m + log2 l) ln 2
+  // ---- finalize: O = acc / l, lse = (m + log2 l) ln 2; the four token groups of each
+  // row chunk are summed across the 16-lane rows with two swaps
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
     const float lt = wave_sum_dpp(ls[h]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (m[h] + __log2f(lt)) * kLn2 : neg_inf();
+    float o[NA];
+#pragma unroll
+    for (int k = 0; k < NA; ++k) {
+      float v = acc[h][k];
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                         false, false);
+      v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                         false, false);
+      o[k] = (__uint_as_float(r32[0]) + __uint_as_float(r32[1])) * inv;
+    }
     const int head = head0 + h;
     float* dst = single ? a.o_out + ((size_t)b * a.hq + head) * D
                         : a.po + ((size_t)item * a.hq + head) * D;
-    if constexpr (kBf16) {
-      *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(acc[h][0] * inv, acc[h][1] * inv);
-    } else {
-      dst[lane] = acc[h][0] * inv;
+    if (pr == 0) {
+      if constexpr (kBf16) {
+        *reinterpret_cast<float4*>(dst + 8 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(dst + 8 * pcl + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      } else {
+        *reinterpret_cast<float4*>(dst + 4 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
+      }
     }
     if (lane == 0) {
       if (single) a.lse_out[(size_t)b * a.hq + head] = lse;
