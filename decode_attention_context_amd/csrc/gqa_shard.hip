@@ -46,6 +46,8 @@ namespace {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(16))) uint32_t u32x16;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
 #define DCP_LDS __attribute__((address_space(3)))
 #define DCP_CONST __attribute__((address_space(4)))
@@ -80,6 +82,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+__device__ __forceinline__ u32x2 lds_tr16(const char DCP_LDS* p) {
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 DCP_LDS*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// V rows are stored with their 16-byte chunks XOR-swizzled by bits of the row, so that the
+// four rows of a transposed read (bf16) fall in distinct LDS banks.  f32 V rows are read
+// row-wise and stored as they are.
+template <bool kBf16>
+__device__ __forceinline__ int v_swz_t(int r) {
+  return kBf16 ? (((r & 1) << 1) | ((r & 2) << 2)) : 0;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int kVm>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -104,7 +119,6 @@ __device__ __forceinline__ void copy16_vaddr(uint32_t lds, const char* src) {
 }
 
 constexpr int waves_for(int g) { return g >= 8 ? 8 : g; }
-constexpr int kDppRowShl4 = 0x104;   // lane i <- lane i + 4 within each 16-lane row
 
 template <bool kBf16, int G>
 __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArgs a) {
@@ -112,7 +126,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
   constexpr int HPW = G / NW;                   // query heads per wave
   constexpr int kElemBytes = kBf16 ? 2 : 4;
   constexpr int D = kRowBytes / kElemBytes;     // head dim
-  constexpr int NA = kBf16 ? 8 : 4;             // dims (accumulators) per lane per head
+  constexpr int NA = kBf16 ? 2 : 4;             // dims (accumulators) per lane per head
   constexpr int kDmaPerWave = kSlots / NW;
   constexpr int kPWords = kBf16 ? kTile / 2 : kTile;  // weight words per head per tile
 
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     const int q = (sl % 16) * 64 + lane;
     const int r = q / kChunks, pc = q % kChunks;
     slot_row[k] = r;
-    slot_src[k] = (uint32_t)((sl < 16 ? (pc ^ (r & 15)) : pc) * 16);
+    slot_src[k] = (uint32_t)((sl < 16 ? (pc ^ (r & 15)) : (pc ^ v_swz_t<kBf16>(r))) * 16);
   }
 
   // ---- tile sources (contiguous tiles): lane k = first cache row of tile 64 * window + k,
@@ -258,7 +272,8 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
   // prologue: tile 0 in flight
   uint64_t vm0 = issue_tile(0);
 
-  const int pr = lane >> 4, pcl = lane & 15;   // P.V lane: token group, row chunk
+  const int pr = lane >> 4, pcl = lane & 15;   // f32 P.V lane: token group, row chunk
+  auto v_swz = [](int r) { return v_swz_t<kBf16>(r); };
   for (int ti = 0; ti < ntiles; ++ti) {
     // this wave's copies of tile ti have landed; after the barrier every wave's have, and
     // tile ti-1 is free for tile ti+1.  A bare barrier: the fence of __syncthreads would
@@ -344,31 +359,43 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
 #pragma unroll
       for (int k = 0; k < NA; ++k) acc[h][k] *= alpha;
       if constexpr (kBf16) {
-        // tokens t and t + 4 (t mod 8 < 4) as one bf16x2 word, written by lane t
+        // tokens 2k and 2k + 1 as one bf16x2 word, written by the even lane
         const uint32_t pb = f32_to_bf16_rne(p);
-        const uint32_t pn = (uint32_t)__builtin_amdgcn_update_dpp((int)pb, (int)pb, kDppRowShl4,
+        const uint32_t pn = (uint32_t)__builtin_amdgcn_update_dpp((int)pb, (int)pb, kDppQuadXor1,
                                                                   0xF, 0xF, false);
-        if (!(lane & 4)) pbuf[w][h][(lane >> 3) * 4 + (lane & 3)] = pb | (pn << 16);
+        if (!(lane & 1)) pbuf[w][h][lane >> 1] = pb | (pn << 16);
       } else {
         pbuf[w][h][lane] = __float_as_uint(p);
       }
     }
 
-    // ---- P.V: lane = (token group pr, 16-byte chunk pcl of the V row)
+    // ---- P.V
     if constexpr (kBf16) {
+      // lane (16-lane group pg, i16) owns dims 32 pg + i16 and 32 pg + 16 + i16.  One
+      // ds_read_b64_tr_b16 gives it one of those dims of 4 consecutive tokens t0 .. t0 + 3,
+      // i.e. the token pairs (t0, t0 + 1), (t0 + 2, t0 + 3) that v_dot2 takes against the
+      // weight pairs, which arrive wave-uniform, four pairs per LDS read.
+      const char DCP_LDS* vb = (const char DCP_LDS*)vt;
+      const int i16 = lane & 15, pg = lane >> 4;
 #pragma unroll
-      for (int k2 = 0; k2 < kTile / 8; ++k2) {
-        const u32x4 v0 = vt[(8 * k2 + pr) * kChunks + pcl];
-        const u32x4 v1 = vt[(8 * k2 + 4 + pr) * kChunks + pcl];
+      for (int q = 0; q < kTile / 8; ++q) {
+        u32x4 pq[HPW];   // weight pairs of tokens 8 q .. 8 q + 7
 #pragma unroll
-        for (int h = 0; h < HPW; ++h) {
-          const uint32_t pp = pbuf[w][h][k2 * 4 + pr];
+        for (int h = 0; h < HPW; ++h)
+          pq[h] = *reinterpret_cast<const u32x4 DCP_LDS*>(
+              (const char DCP_LDS*)&pbuf[w][h][0] + 16 * q);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[h][2 * i] = dot2_bf16(pp, __builtin_amdgcn_perm(v1[i], v0[i], 0x05040100u),
-                                      acc[h][2 * i]);
-            acc[h][2 * i + 1] = dot2_bf16(pp, __builtin_amdgcn_perm(v1[i], v0[i], 0x07060302u),
-                                          acc[h][2 * i + 1]);
+        for (int half = 0; half < 2; ++half) {
+          const int r = 8 * q + 4 * half + (i16 >> 2);   // tile row this lane addresses
+#pragma unroll
+          for (int dh = 0; dh < 2; ++dh) {
+            const int c = 2 * (2 * pg + dh) + ((i16 >> 1) & 1);   // logical 16-byte chunk
+            const u32x2 v = lds_tr16(vb + r * kRowBytes + 16 * (c ^ v_swz(r)) + (i16 & 1) * 8);
+#pragma unroll
+            for (int h = 0; h < HPW; ++h) {
+              acc[h][dh] = dot2_bf16(pq[h][2 * half], v.x, acc[h][dh]);
+              acc[h][dh] = dot2_bf16(pq[h][2 * half + 1], v.y, acc[h][dh]);
+            }
           }
         }
       }
@@ -387,34 +414,35 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     vm0 = vm1;
   }
 
-  // ---- finalize: O = acc / l, lse = (m + log2 l) ln 2; the four token groups of each
-  // row chunk are summed across the 16-lane rows with two swaps
+  // ---- finalize: O = acc / l, lse = (m + log2 l) ln 2
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
     const float lt = wave_sum_dpp(ls[h]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (m[h] + __log2f(lt)) * kLn2 : neg_inf();
-    float o[NA];
-#pragma unroll
-    for (int k = 0; k < NA; ++k) {
-      float v = acc[h][k];
-      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                         false, false);
-      v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                         false, false);
-      o[k] = (__uint_as_float(r32[0]) + __uint_as_float(r32[1])) * inv;
-    }
     const int head = head0 + h;
     float* dst = single ? a.o_out + ((size_t)b * a.hq + head) * D
                         : a.po + ((size_t)item * a.hq + head) * D;
-    if (pr == 0) {
-      if constexpr (kBf16) {
-        *reinterpret_cast<float4*>(dst + 8 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<float4*>(dst + 8 * pcl + 4) = make_float4(o[4], o[5], o[6], o[7]);
-      } else {
-        *reinterpret_cast<float4*>(dst + 4 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
+    if constexpr (kBf16) {
+      // lane (g, i16): dims 32 g + i16 and 32 g + 16 + i16
+      const int d0 = 32 * (lane >> 4) + (lane & 15);
+      dst[d0] = acc[h][0] * inv;
+      dst[d0 + 16] = acc[h][1] * inv;
+    } else {
+      // the four token groups of each row chunk are summed across the 16-lane rows
+      float o[NA];
+#pragma unroll
+      for (int k = 0; k < NA; ++k) {
+        float v = acc[h][k];
+        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                           false, false);
+        v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                           false, false);
+        o[k] = (__uint_as_float(r32[0]) + __uint_as_float(r32[1])) * inv;
       }
+      if (pr == 0)
+        *reinterpret_cast<float4*>(dst + 4 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
     }
     if (lane == 0) {
       if (single) a.lse_out[(size_t)b * a.hq + head] = lse;
