@@ -9,9 +9,11 @@
 // the split-K partials of one shard call, whose items cover disjoint local token ranges.
 //
 // One wave merges one (request, head) row: the n lse values are loaded one per lane and
-// reduced with DPP (no serial chain of loads), then each lane streams VEC consecutive
-// floats of every partial row, eight partials' loads in flight at a time.  Empty partials
-// (weight 0) are never read.  The kernel is HBM-bound.
+// reduced with DPP (no serial chain of loads).  With at most 8 partials (every cp_size in
+// practice) each lane issues the loads of all its partial-row chunks together with the lse
+// load, so a row costs one memory round trip; weights of empty partials are exactly 0 and
+// their rows (which may hold garbage) are excluded by a select, never multiplied.  More
+// partials are streamed eight at a time, empty ones not read.  The kernel is HBM-bound.
 #include "launch.h"
 
 namespace dcp {
@@ -113,7 +115,110 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
   if (lse_out && lane == 0) *lse_out = (m2 - __log2f(inv)) * kLn2;
 }
 
+// At most 8 partials and 2 chunks of 64 * VEC floats per lane: all loads up front.
+template <int VEC>
+__device__ __forceinline__ void merge_row_small(const float* __restrict__ o_base,
+                                                int64_t o_stride,
+                                                const float* __restrict__ l_base,
+                                                int64_t l_stride, int n, int dv,
+                                                float* __restrict__ out_f32,
+                                                uint16_t* __restrict__ out_bf16,
+                                                float* __restrict__ lse_out, int lane) {
+  using V = typename VecT<VEC>::T;
+  constexpr int kMaxN = 8, kMaxC = 2;
+  const int nc = dv / (64 * VEC);
+  float x = lane < n ? l_base[lane * l_stride] : neg_inf();
+  V v[kMaxN][kMaxC];
+#pragma unroll
+  for (int r = 0; r < kMaxN; ++r)
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c)
+      if (r < n && c < nc)
+        v[r][c] = *reinterpret_cast<const V*>(o_base + (int64_t)r * o_stride +
+                                              (c * 64 + lane) * VEC);
+  x = __builtin_isfinite(x) ? x : neg_inf();
+  const float m = wave_max_dpp(x);
+  if (m == neg_inf()) {
+    // every partial is empty
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c) {
+      if (c < nc) {
+        const int d = (c * 64 + lane) * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          if (out_f32) out_f32[d + i] = 0.f;
+          else out_bf16[d + i] = 0;
+        }
+      }
+    }
+    if (lse_out && lane == 0) *lse_out = neg_inf();
+    return;
+  }
+  const float m2 = m * kLog2e;
+  const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
+  const float inv = 1.f / wave_sum_dpp(wl);
+  float acc[kMaxC][VEC];
+#pragma unroll
+  for (int c = 0; c < kMaxC; ++c)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[c][i] = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxN; ++r) {
+    if (r < n) {
+      const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r));
+#pragma unroll
+      for (int c = 0; c < kMaxC; ++c) {
+        if (c < nc) {
+          const float* pv = reinterpret_cast<const float*>(&v[r][c]);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i)
+            acc[c][i] = wr != 0.f ? fmaf(wr, pv[i], acc[c][i]) : acc[c][i];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kMaxC; ++c) {
+    if (c < nc) {
+      const int d = (c * 64 + lane) * VEC;
+      if (out_f32) {
+        V o;
+        float* po = reinterpret_cast<float*>(&o);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) po[i] = acc[c][i] * inv;
+        *reinterpret_cast<V*>(out_f32 + d) = o;
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+          out_bf16[d + i] = (uint16_t)f32_to_bf16_rne(acc[c][i] * inv);
+      }
+    }
+  }
+  if (lse_out && lane == 0) *lse_out = (m2 - __log2f(inv)) * kLn2;
+}
+
+// whether a row qualifies for merge_row_small
+__host__ __device__ __forceinline__ bool merge_small_ok(int n, int dv, int vec) {
+  return n <= 8 && dv % (64 * vec) == 0 && dv <= 2 * 64 * vec;
+}
+
 constexpr int kRowsPerBlock = 4;
+
+// dcp_merge with at most 8 partials: one row per wave, all loads up front
+template <int VEC>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void merge_small_kernel(
+    const float* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
+    int batch, int heads, int dv, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
+    float* __restrict__ lse_out) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)batch * heads;
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  merge_row_small<VEC>(o_partials + row * dv, rows * dv, lse_partials + row, rows, n, dv,
+                       out_f32 ? out_f32 + row * dv : nullptr,
+                       out_bf16 ? out_bf16 + row * dv : nullptr,
+                       lse_out ? lse_out + row : nullptr, lane);
+}
 
 template <int VEC>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void merge_kernel(
@@ -142,8 +247,14 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
   const int i0 = off[b], n = off[b + 1] - i0;
   if (n == 1) return;
   const int lane = threadIdx.x & 63;
-  merge_row<VEC>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h,
-                 hq, n, dv, o_out + row * dv, nullptr, lse_out + row, lane);
+  if (merge_small_ok(n, dv, VEC))
+    merge_row_small<VEC>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv,
+                         plse + (int64_t)i0 * hq + h, hq, n, dv, o_out + row * dv, nullptr,
+                         lse_out + row, lane);
+  else
+    merge_row<VEC>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv,
+                   plse + (int64_t)i0 * hq + h, hq, n, dv, o_out + row * dv, nullptr,
+                   lse_out + row, lane);
 }
 
 int pick_vec(int dv) {
@@ -161,6 +272,22 @@ hipError_t launch_merge(const float* o_partials, const float* lse_partials, int 
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   float* of = out_bf16 ? nullptr : static_cast<float*>(o_out);
   uint16_t* ob = out_bf16 ? static_cast<uint16_t*>(o_out) : nullptr;
+  if (merge_small_ok(n, dv, pick_vec(dv))) {
+    switch (pick_vec(dv)) {
+      case 4:
+        hipLaunchKernelGGL(merge_small_kernel<4>, grid, dim3(64 * kRowsPerBlock), 0, stream,
+                           o_partials, lse_partials, n, batch, heads, dv, of, ob, lse_out);
+        break;
+      case 2:
+        hipLaunchKernelGGL(merge_small_kernel<2>, grid, dim3(64 * kRowsPerBlock), 0, stream,
+                           o_partials, lse_partials, n, batch, heads, dv, of, ob, lse_out);
+        break;
+      default:
+        hipLaunchKernelGGL(merge_small_kernel<1>, grid, dim3(64 * kRowsPerBlock), 0, stream,
+                           o_partials, lse_partials, n, batch, heads, dv, of, ob, lse_out);
+    }
+    return hipGetLastError();
+  }
   switch (pick_vec(dv)) {
     case 4:
       hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(64 * kRowsPerBlock), 0, stream, o_partials,
