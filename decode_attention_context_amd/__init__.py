@@ -160,7 +160,8 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     MLA: q [b, 128, 576] bf16, kv_pages = latent pages [nb, B, 576], v_pages None.
     block_table int32 [b, max_blocks]; seq_lens int32 [b] (global lengths).
     Returns (O_r float32 [b, Hq, Dv], lse_r float32 [b, Hq], workspace).
-    `events` = (begin, end) torch.cuda.Event pair recorded around the attention kernel."""
+    `events` = (begin, end) torch.cuda.Event pair that takes the attention kernel's own start
+    and end time stamps."""
     lib = load()
     if kind is None:
         kind = MLA if v_pages is None else GQA

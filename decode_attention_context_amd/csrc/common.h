@@ -74,35 +74,89 @@ constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
 constexpr int kDppRowMirror = 0x140;     // lane i <-> 15 - i within each 16 lanes
 
+// Row-local lane permutation (every lane reads a lane of its own 16-lane row, so the
+// bound control never applies); an undefined old value lets the compiler fuse the move
+// into the consuming VALU op (v_max_f32_dpp, v_add_f32_dpp).
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), kCtrl,
-                                                    0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+
+// The same value combined across the four 16-lane rows: lanes i, i+16, i+32, i+48 swap
+// through v_permlane16_swap / v_permlane32_swap (no LDS, no scalar round trip).
+__device__ __forceinline__ float rows_max(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                     false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // Max / sum over all 64 lanes without LDS: a DPP butterfly inside each 16-lane row, then
-// the four row results are read into scalars.  The result is wave-uniform.
+// the row results are combined by lane swaps.  The result is the same in every lane.
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp<kDppQuadXor1>(v));
   v = fmaxf(v, dpp<kDppQuadXor2>(v));
   v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
   v = fmaxf(v, dpp<kDppRowMirror>(v));
-  const int vi = __float_as_int(v);
-  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(vi, 0)),
-                     __int_as_float(__builtin_amdgcn_readlane(vi, 16))),
-               fmaxf(__int_as_float(__builtin_amdgcn_readlane(vi, 32)),
-                     __int_as_float(__builtin_amdgcn_readlane(vi, 48))));
+  return rows_max(v);
 }
 __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += dpp<kDppQuadXor1>(v);
   v += dpp<kDppQuadXor2>(v);
   v += dpp<kDppRowHalfMirror>(v);
   v += dpp<kDppRowMirror>(v);
-  const int vi = __float_as_int(v);
-  return (__int_as_float(__builtin_amdgcn_readlane(vi, 0)) +
-          __int_as_float(__builtin_amdgcn_readlane(vi, 16))) +
-         (__int_as_float(__builtin_amdgcn_readlane(vi, 32)) +
-          __int_as_float(__builtin_amdgcn_readlane(vi, 48)));
+  return rows_sum(v);
+}
+
+// Max over all 64 lanes, returned wave-uniform.  v_max_f32 takes its first operand through
+// DPP: a butterfly inside each 16-lane row, then row_bcast:15 (rows 1 and 3 take the last
+// lane of the row below) and row_bcast:31 (rows 2 and 3 take lane 31), which leaves the
+// maximum of the whole wave in lane 63.  Every DPP step reads the register that the VALU op
+// before it wrote, so two wait states precede it.
+__device__ __forceinline__ float wave_max_bcast(float v) {
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
+      : "+v"(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((kVm & 0xF) | ((kVm >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 16-byte-per-lane HBM -> LDS copy: LDS bytes [lds + 16 lane, + 16) <- global
+// sbase + voff (scalar base, 32-bit lane offset).  M0 carries the LDS address; one wait
+// state separates its write from the copy that reads it.  The copies stream data that is
+// read once per launch, so they carry the non-temporal cache policy (nt): streamed this
+// way the HBM -> LDS rate rises from about 5.9 to 7.1 TB/s on MI355X.
+__device__ __forceinline__ void copy16_sbase(uint32_t lds, uint32_t voff, const char* sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+// The same from a per-lane 64-bit address.
+__device__ __forceinline__ void copy16_vaddr(uint32_t lds, const char* src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
 }
 
 // float -> bf16 bits, round to nearest even (NaN -> quiet NaN).

@@ -101,18 +101,16 @@ int shard_impl(const dcp_attn_desc* d, const void* q, const void* kv, const void
   hipError_t e = dcp::launch_plan(lens, batch, rank, cp, il, len_cap, p.target, p.tile,
                                   p.min_chunk, w, stream);
   if (e != hipSuccess) return DCP_ELAUNCH;
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return DCP_ELAUNCH;
   if (d->kind == DCP_GQA) {
     dcp::GqaArgs a{q, kv, v, bt, d->num_q_heads, d->num_kv_heads, d->head_dim_qk, d->block_size,
                    d->max_blocks_per_seq, d->num_blocks, rank, cp, il, scale, d->dtype};
-    e = dcp::launch_gqa_shard(a, p.max_items, w, o, lse, stream);
+    e = dcp::launch_gqa_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   } else {
     dcp::MlaArgs a{q, kv, bt, d->block_size, d->max_blocks_per_seq, d->num_blocks,
                    rank, cp, il, scale};
-    e = dcp::launch_mla_shard(a, p.max_items, w, o, lse, stream);
+    e = dcp::launch_mla_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   }
   if (e != hipSuccess) return DCP_ELAUNCH;
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return DCP_ELAUNCH;
   e = dcp::launch_split_combine(w, batch, d->num_q_heads, d->head_dim_v, o, lse, stream);
   return e == hipSuccess ? DCP_OK : DCP_ELAUNCH;
 }

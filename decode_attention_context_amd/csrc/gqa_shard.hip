@@ -8,33 +8,36 @@
 // into exact attention.
 //
 // The work is HBM-bound (per token and KV head: 2 * D * sizeof(T) bytes against
-// 4 * G * D flops), so the design is about keeping enough K / V bytes in flight and
-// streaming them at full rate on the vector ALUs:
+// 4 * G * D flops), so the design is about keeping K / V bytes streaming at full rate and
+// the vector-ALU work per byte small:
 //   * One workgroup of NW = min(G, 8) waves per work item (request, KV head, local token
-//     range), one workgroup per CU; wave w owns G / NW of the query heads that share the
+//     range), two workgroups per CU; wave w owns G / NW of the query heads that share the
 //     KV head.
 //   * 64-token tiles of K and V rows are copied HBM -> LDS by global_load_lds_dwordx4 (no
-//     register staging) into a 4-deep ring: three tiles (96 KiB) in flight while one is
-//     computed.  The copies are issued from inline assembly and paced by explicit
+//     register staging) with the non-temporal cache policy into a double buffer: tiles 0
+//     and 1 are issued up front, then each tile's copies leave right after the barrier that
+//     frees its buffer.  The copies are issued from inline assembly and paced by explicit
 //     vector-memory counter waits plus a bare s_barrier, so the compiler never drains them
-//     before LDS reads of the other buffers.  When the interleave and the block size are
-//     multiples of the tile, a tile is one run of consecutive cache rows: a per-wave table
-//     (lane k = first row of tile 64 * window + k) locates it with one readlane and the
-//     copies are a scalar base plus fixed lane offsets; otherwise each lane walks one
-//     token.  The 16-byte chunks of a K row are XOR-swizzled by (row mod 16) so the
-//     transposed reads below are conflict free.
-//   * Scores: lane = token.  The lane pulls its K row from LDS into registers once; each
-//     query head, being wave-uniform, sits in scalar registers (loaded once when a wave
-//     owns one head, streamed in 16-dword chunks otherwise) and is the scalar operand of
+//     before LDS reads.  When the interleave and the block size are multiples of the tile,
+//     a tile is one run of consecutive cache rows: a per-wave table (lane k = first row of
+//     tile 64 * window + k) locates it with one readlane and the copies are a scalar base
+//     plus fixed lane offsets; otherwise each lane walks one token.
+//   * K rows sit in 4-row blocks, chunk-major inside a block, the blocks 1088 bytes apart:
+//     a lane's row is a base address plus immediate offsets, and the rows that one LDS read
+//     serves fall in distinct bank groups.
+//   * Scores: lane = token.  The lane pulls its K row from LDS in two halves; each query
+//     head, being wave-uniform, sits in scalar registers (loaded once when a wave owns one
+//     head, streamed in 16-dword chunks otherwise) and is the scalar operand of
 //     v_dot2_f32_bf16 (bf16) or v_fma_f32 (f32): no cross-lane reduction.
 //   * Online softmax in base 2 (scale * log2 e folded into the scores).  The tile max per
-//     head is a DPP butterfly plus four lane reads (no LDS); running sums stay per lane and
-//     are reduced once per item.
-//   * P.V: lane = (token group r = lane / 16, 16-byte chunk c = lane % 16 of the V row), so
-//     one ds_read_b128 brings four V rows.  For bf16 the rows of tokens t and t + 4 are
-//     paired with v_perm_b32 and combined with the bf16-rounded weight pair by
-//     v_dot2_f32_bf16 into fp32 accumulators (8 dims per lane); the four token groups are
-//     summed across rows once per item.
+//     head is v_max_f32 with DPP operands (row butterfly, then row broadcasts into the last
+//     lane) read into a scalar; running sums stay per lane and are reduced once per item.
+//   * P.V (bf16): lane = (16-lane group, lane in group) owns two head dims; one transposed
+//     LDS read (ds_read_b64_tr_b16) gives it one dim of four consecutive tokens, i.e. two
+//     token pairs that v_dot2_f32_bf16 combines with the bf16-rounded weight pairs, which
+//     arrive wave-uniform, four pairs per LDS read.  V chunks are XOR-swizzled by bits of
+//     the row so that the transposed reads are conflict free.  f32: lane = (token group,
+//     16-byte chunk of the V row), the four token groups summed across rows once per item.
 //   * An item that covers a request's whole shard writes (O, lse) directly; otherwise it
 //     writes a normalized partial that the split combine merges.
 #include "launch.h"
@@ -44,6 +47,7 @@ namespace dcp {
 namespace {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(16))) uint32_t u32x16;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
@@ -58,6 +62,12 @@ constexpr int kChunks = kRowBytes / 16;
 constexpr int kTileBytes = kTile * kRowBytes;   // 16 KiB of K (and of V) per tile
 constexpr int kNBuf = 2;                         // double buffer: one computed, one in flight
 constexpr int kSlots = 2 * kTileBytes / 1024;   // 1-KiB copies per tile (K then V)
+// K rows sit in 4-row blocks, chunk-major inside a block (16-byte unit 4 * chunk + row),
+// with the blocks 1088 bytes apart: row r's chunk c is at a lane base plus the immediate
+// 64 c, and the 16 rows read together fall in 16 distinct 16-byte bank groups.
+constexpr int kKBlock = 1024 + 64;
+constexpr int kKBytes = (kTile / 4) * kKBlock;   // K part of a buffer
+constexpr int kBufBytes = kKBytes + kTileBytes;  // K blocks, then the V rows
 
 struct GqaKArgs {
   const void* q;
@@ -95,28 +105,6 @@ __device__ __forceinline__ int v_swz_t(int r) {
   return kBf16 ? (((r & 1) << 1) | ((r & 2) << 2)) : 0;
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int kVm>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((kVm & 0xF) | ((kVm >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// One 16-byte-per-lane HBM -> LDS copy: LDS bytes [lds + 16 lane, + 16) <- global
-// sbase + voff (scalar base, 32-bit lane offset).  M0 carries the LDS address; one wait
-// state separates its write from the copy that reads it.
-__device__ __forceinline__ void copy16_sbase(uint32_t lds, uint32_t voff, const char* sbase) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-// The same from a per-lane 64-bit address.
-__device__ __forceinline__ void copy16_vaddr(uint32_t lds, const char* src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
 
 constexpr int waves_for(int g) { return g >= 8 ? 8 : g; }
 
@@ -130,8 +118,8 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
   constexpr int kDmaPerWave = kSlots / NW;
   constexpr int kPWords = kBf16 ? kTile / 2 : kTile;  // weight words per head per tile
 
-  // [buffer][K, V][row * 16 + chunk]
-  __shared__ u32x4 kv[kNBuf][2][kTile * kChunks];
+  // [buffer][K blocks | V rows]
+  __shared__ u32x4 kvs[kNBuf * kBufBytes / 16];
   __shared__ uint32_t pbuf[NW][HPW][kPWords];
 
   const int lane = threadIdx.x & 63;
@@ -151,7 +139,8 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
   const uint32_t B = (uint32_t)a.block_size;
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
   const bool fast = (a.interleave % kTile) == 0 && (a.block_size % kTile) == 0;
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)(const char DCP_LDS*)&kv[0][0][0];
+  const char DCP_LDS* kvb = (const char DCP_LDS*)&kvs[0];
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)kvb;
 
   float m[HPW], ls[HPW], acc[HPW][NA];
 #pragma unroll
@@ -162,18 +151,28 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     for (int k = 0; k < NA; ++k) acc[h][k] = 0.f;
   }
 
-  // ---- copy slots of this wave: slot s = w * kDmaPerWave + k; s < 16 copies K, s >= 16 V.
-  // 16-byte position q = (s mod 16) * 64 + lane of the tile holds row q / 16, chunk q mod 16
-  // (K: source chunk (q mod 16) ^ (row & 15), V: as it is).
+  // ---- copy slots of this wave: slot s = w * kDmaPerWave + k, one 1-KiB copy each.
+  // s < 16: the K block of rows 4 s .. 4 s + 3, lane l bringing chunk l / 4 of row
+  // 4 s + l % 4.  s >= 16: V 16-byte positions q = (s - 16) * 64 + lane, row q / 16, holding
+  // chunk (q mod 16) ^ swizzle(row).
   uint32_t slot_src[kDmaPerWave];
   int slot_row[kDmaPerWave];
+  uint32_t slot_dst[kDmaPerWave];   // byte offset in the buffer (wave-uniform)
 #pragma unroll
   for (int k = 0; k < kDmaPerWave; ++k) {
     const int sl = w * kDmaPerWave + k;
-    const int q = (sl % 16) * 64 + lane;
-    const int r = q / kChunks, pc = q % kChunks;
-    slot_row[k] = r;
-    slot_src[k] = (uint32_t)((sl < 16 ? (pc ^ (r & 15)) : (pc ^ v_swz_t<kBf16>(r))) * 16);
+    if (sl < 16) {
+      slot_row[k] = 4 * sl + (lane & 3);
+      slot_src[k] = (uint32_t)(lane >> 2) * 16;
+      slot_dst[k] = (uint32_t)(sl * kKBlock);
+    } else {
+      const int q = (sl - 16) * 64 + lane;
+      const int r = q / kChunks, pc = q % kChunks;
+      slot_row[k] = r;
+      slot_src[k] = (uint32_t)((pc ^ v_swz_t<kBf16>(r)) * 16);
+      slot_dst[k] = (uint32_t)(kKBytes + (sl - 16) * 1024);
+    }
+    slot_dst[k] = __builtin_amdgcn_readfirstlane(slot_dst[k]);   // M0 operand: keep it scalar
   }
 
   // ---- tile sources (contiguous tiles): lane k = first cache row of tile 64 * window + k,
@@ -213,7 +212,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     TileSrc ts;
     ts.rb = (size_t)(ok ? row0 : 0u) * kRowBytes;
     ts.lim = ok ? (uint32_t)nvalid : 0u;
-    ts.dst = lds_addr + (uint32_t)((ti % kNBuf) * 2 * kTileBytes);
+    ts.dst = lds_addr + (uint32_t)((ti % kNBuf) * kBufBytes);
     return ts;
   };
   auto copy_slot = [&](const TileSrc& ts, int k) {
@@ -221,11 +220,11 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     const uint32_t voff = (uint32_t)slot_row[k] < ts.lim
                               ? (uint32_t)slot_row[k] * kRowBytes + slot_src[k]
                               : slot_src[k];
-    copy16_sbase(ts.dst + (uint32_t)(sl * 1024), voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
+    copy16_sbase(ts.dst + slot_dst[k], voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
   };
   // ---- all of this wave's HBM -> LDS copies of tile ti; returns the mask of valid tokens
   auto issue_tile = [&](int ti) -> uint64_t {
-    const uint32_t dst = lds_addr + (uint32_t)((ti % kNBuf) * 2 * kTileBytes);
+    const uint32_t dst = lds_addr + (uint32_t)((ti % kNBuf) * kBufBytes);
     if (fast) {
       uint64_t vm;
       const TileSrc ts = locate(ti, vm);
@@ -254,7 +253,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     for (int k = 0; k < kDmaPerWave; ++k) {
       const int sl = w * kDmaPerWave + k;
       const uint32_t rr = __shfl(row, slot_row[k], 64);
-      copy16_vaddr(dst + (uint32_t)(sl * 1024),
+      copy16_vaddr(dst + slot_dst[k],
                    (sl < 16 ? a.kp : a.vp) + (size_t)rr * kRowBytes + slot_src[k]);
     }
     return __ballot(ok);
@@ -269,20 +268,26 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
       qres[c] = *reinterpret_cast<const u32x16 DCP_CONST*>(qh + 16 * c);
   }
 
-  // prologue: tile 0 in flight
+  // prologue: tiles 0 and 1 in flight (both buffers are free)
   uint64_t vm0 = issue_tile(0);
+  const uint64_t vm_first = ntiles > 1 ? issue_tile(1) : 0ull;
 
   const int pr = lane >> 4, pcl = lane & 15;   // f32 P.V lane: token group, row chunk
   auto v_swz = [](int r) { return v_swz_t<kBf16>(r); };
   for (int ti = 0; ti < ntiles; ++ti) {
-    // this wave's copies of tile ti have landed; after the barrier every wave's have, and
-    // tile ti-1 is free for tile ti+1.  A bare barrier: the fence of __syncthreads would
-    // also wait for LDS traffic that needs no ordering here.
-    wait_vmcnt<0>();
+    // this wave's copies of tile ti have landed (loads complete in issue order, so on the
+    // first tile only tile 1's copies may still be outstanding); after the barrier every
+    // wave's have, and from tile 1 on the buffer of tile ti-1 is free for tile ti+1.  A bare
+    // barrier: the fence of __syncthreads would also wait for LDS traffic that needs no
+    // ordering here.
+    if (ti == 0 && ntiles > 1) wait_vmcnt<kDmaPerWave>();
+    else wait_vmcnt<0>();
     asm volatile("s_barrier" ::: "memory");
-    const uint64_t vm1 = ti + 1 < ntiles ? issue_tile(ti + 1) : 0ull;
-    const u32x4* kt = kv[ti % kNBuf][0];
-    const u32x4* vt = kv[ti % kNBuf][1];
+    const uint64_t vm1 = ti == 0 ? vm_first : (ti + 1 < ntiles ? issue_tile(ti + 1) : 0ull);
+    const char DCP_LDS* kb = kvb + (ti % kNBuf) * kBufBytes +
+                             (lane >> 2) * kKBlock + (lane & 3) * 16;   // this lane's K row
+    const u32x4 DCP_LDS* vt = (const u32x4 DCP_LDS*)(kvb + (ti % kNBuf) * kBufBytes + kKBytes);
+    auto kchunk = [&](int c) { return *(const u32x4 DCP_LDS*)(kb + 64 * c); };
 
     // ---- scores: lane = token
     float s[HPW];
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
 #pragma unroll
         for (int c = 0; c < kChunks / 2; ++c) {
           const int cc = hf * (kChunks / 2) + c;
-          kr[c] = kt[lane * kChunks + (cc ^ (lane & 15))];
+          kr[c] = kchunk(cc);
         }
 #pragma unroll
         for (int c = 0; c < kChunks / 8; ++c)
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     } else {
       u32x4 krow[kChunks];
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) krow[c] = kt[lane * kChunks + (c ^ (lane & 15))];
+      for (int c = 0; c < kChunks; ++c) krow[c] = kchunk(c);
       // 16 query dwords per scalar load, one load ahead of its use; each step is its own
       // scheduling region so that no more than two chunks (32 scalar registers) are live
       constexpr int kQSteps = HPW * (kChunks / 4);
@@ -344,11 +349,12 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     }
 
     // ---- online softmax (base 2); weights to LDS for the P.V lanes
-    const bool valid = (vm0 >> lane) & 1;
+    const bool full = vm0 == ~0ull;   // uniform: mask only partial tiles
+    const bool valid = full || ((vm0 >> lane) & 1);
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
       const float x = valid ? s[h] * a.sl2 : neg_inf();
-      const float mn = fmaxf(m[h], wave_max_dpp(x));
+      const float mn = fmaxf(m[h], wave_max_bcast(x));
       float alpha = 1.f, p = 0.f;
       if (mn != neg_inf()) {
         alpha = __builtin_amdgcn_exp2f(m[h] - mn);
@@ -359,11 +365,12 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
 #pragma unroll
       for (int k = 0; k < NA; ++k) acc[h][k] *= alpha;
       if constexpr (kBf16) {
-        // tokens 2k and 2k + 1 as one bf16x2 word, written by the even lane
-        const uint32_t pb = f32_to_bf16_rne(p);
-        const uint32_t pn = (uint32_t)__builtin_amdgcn_update_dpp((int)pb, (int)pb, kDppQuadXor1,
-                                                                  0xF, 0xF, false);
-        if (!(lane & 1)) pbuf[w][h][lane >> 1] = pb | (pn << 16);
+        // tokens 2k and 2k + 1 as one bf16x2 word (round to nearest even), written by the
+        // even lane
+        const float pn = dpp<kDppQuadXor1>(p);
+        const f2 pp = {p, pn};
+        if (!(lane & 1))
+          pbuf[w][h][lane >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
       } else {
         pbuf[w][h][lane] = __float_as_uint(p);
       }
@@ -452,13 +459,14 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
 }
 
 template <bool kBf16>
-hipError_t launch_g(const GqaKArgs& k, int group, dim3 grid, hipStream_t s) {
+hipError_t launch_g(const GqaKArgs& k, int group, dim3 grid, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1) {
   switch (group) {
-    case 1: hipLaunchKernelGGL((gqa_shard_kernel<kBf16, 1>), grid, dim3(64 * waves_for(1)), 0, s, k); break;
-    case 2: hipLaunchKernelGGL((gqa_shard_kernel<kBf16, 2>), grid, dim3(64 * waves_for(2)), 0, s, k); break;
-    case 4: hipLaunchKernelGGL((gqa_shard_kernel<kBf16, 4>), grid, dim3(64 * waves_for(4)), 0, s, k); break;
-    case 8: hipLaunchKernelGGL((gqa_shard_kernel<kBf16, 8>), grid, dim3(64 * waves_for(8)), 0, s, k); break;
-    case 16: hipLaunchKernelGGL((gqa_shard_kernel<kBf16, 16>), grid, dim3(64 * waves_for(16)), 0, s, k); break;
+    case 1: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 1>), grid, dim3(64 * waves_for(1)), 0, s, e0, e1, 0, k); break;
+    case 2: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 2>), grid, dim3(64 * waves_for(2)), 0, s, e0, e1, 0, k); break;
+    case 4: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 4>), grid, dim3(64 * waves_for(4)), 0, s, e0, e1, 0, k); break;
+    case 8: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 8>), grid, dim3(64 * waves_for(8)), 0, s, e0, e1, 0, k); break;
+    case 16: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 16>), grid, dim3(64 * waves_for(16)), 0, s, e0, e1, 0, k); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -473,7 +481,8 @@ bool gqa_supported(int dtype, int head_dim, int group) {
 }
 
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream) {
+                            float* o_out, float* lse_out, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1) {
   GqaKArgs k;
   k.q = a.q;
   k.kp = static_cast<const char*>(a.k_pages);
@@ -497,8 +506,8 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
   k.po = ws.po;
   const dim3 grid((unsigned)max_items, (unsigned)a.hkv);
   const int group = a.hq / a.hkv;
-  return a.dtype == 1 ? launch_g<true>(k, group, grid, stream)
-                      : launch_g<false>(k, group, grid, stream);
+  return a.dtype == 1 ? launch_g<true>(k, group, grid, stream, ev0, ev1)
+                      : launch_g<false>(k, group, grid, stream, ev0, ev1);
 }
 
 }  // namespace dcp

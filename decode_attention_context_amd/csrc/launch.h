@@ -1,6 +1,7 @@
 // launch.h — host-side launchers of the gfx950 kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,8 +35,10 @@ struct GqaArgs {
   float scale;
   int dtype;  // 0 f32, 1 bf16
 };
+// ev0 / ev1 (nullable): events stamped with the attention kernel's own start and end.
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream);
+                            float* o_out, float* lse_out, hipStream_t stream,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 bool gqa_supported(int dtype, int head_dim, int group);
 
 struct MlaArgs {
@@ -48,7 +51,8 @@ struct MlaArgs {
   float scale;
 };
 hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream);
+                            float* o_out, float* lse_out, hipStream_t stream,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_shard_slots(const int32_t* block_table, const int32_t* seq_lens, int batch,
                               int max_blocks, int block_size, int64_t num_blocks, int rank,

@@ -25,9 +25,20 @@ struct VecT;
 template <>
 struct VecT<1> { using T = float; };
 template <>
-struct VecT<2> { using T = float2; };
+struct VecT<2> { using T = __attribute__((ext_vector_type(2))) float; };
 template <>
-struct VecT<4> { using T = float4; };
+struct VecT<4> { using T = __attribute__((ext_vector_type(4))) float; };
+
+// Partials are read once and outputs written once: both stream with the non-temporal cache
+// policy.
+template <typename T>
+__device__ __forceinline__ T ld_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
+template <typename T>
+__device__ __forceinline__ void st_nt(float* p, T v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+}
 
 template <int VEC>
 __device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename VecT<VEC>::T& v) {
@@ -48,7 +59,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
   using V = typename VecT<VEC>::T;
   auto lse_at = [&](int r) -> float {
     if (r >= n) return neg_inf();
-    const float x = l_base[r * l_stride];
+    const float x = ld_nt<float>(l_base + r * l_stride);
     return __builtin_isfinite(x) ? x : neg_inf();
   };
   float m = neg_inf();
@@ -89,7 +100,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
         for (int u = 0; u < 8; ++u) {
           wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r + u));
           if (wv[u] != 0.f)
-            v[u] = *reinterpret_cast<const V*>(o_base + (int64_t)(r0 + r + u) * o_stride + d);
+            v[u] = ld_nt<V>(o_base + (int64_t)(r0 + r + u) * o_stride + d);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -98,7 +109,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
       for (; r < nr; ++r) {
         const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r));
         if (wr != 0.f)
-          vfma<VEC>(acc, wr, *reinterpret_cast<const V*>(o_base + (int64_t)(r0 + r) * o_stride + d));
+          vfma<VEC>(acc, wr, ld_nt<V>(o_base + (int64_t)(r0 + r) * o_stride + d));
       }
     }
     if (out_f32) {
@@ -106,7 +117,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
       float* po = reinterpret_cast<float*>(&o);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) po[i] = acc[i] * inv;
-      *reinterpret_cast<V*>(out_f32 + d) = o;
+      st_nt<V>(out_f32 + d, o);
     } else {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) out_bf16[d + i] = (uint16_t)f32_to_bf16_rne(acc[i] * inv);
@@ -127,15 +138,14 @@ __device__ __forceinline__ void merge_row_small(const float* __restrict__ o_base
   using V = typename VecT<VEC>::T;
   constexpr int kMaxN = 8, kMaxC = 2;
   const int nc = dv / (64 * VEC);
-  float x = lane < n ? l_base[lane * l_stride] : neg_inf();
+  float x = lane < n ? ld_nt<float>(l_base + lane * l_stride) : neg_inf();
   V v[kMaxN][kMaxC];
 #pragma unroll
   for (int r = 0; r < kMaxN; ++r)
 #pragma unroll
     for (int c = 0; c < kMaxC; ++c)
       if (r < n && c < nc)
-        v[r][c] = *reinterpret_cast<const V*>(o_base + (int64_t)r * o_stride +
-                                              (c * 64 + lane) * VEC);
+        v[r][c] = ld_nt<V>(o_base + (int64_t)r * o_stride + (c * 64 + lane) * VEC);
   x = __builtin_isfinite(x) ? x : neg_inf();
   const float m = wave_max_dpp(x);
   if (m == neg_inf()) {
@@ -186,7 +196,7 @@ __device__ __forceinline__ void merge_row_small(const float* __restrict__ o_base
         float* po = reinterpret_cast<float*>(&o);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) po[i] = acc[c][i] * inv;
-        *reinterpret_cast<V*>(out_f32 + d) = o;
+        st_nt<V>(out_f32 + d, o);
       } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i)

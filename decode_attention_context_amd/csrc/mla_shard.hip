@@ -117,28 +117,6 @@ __device__ __forceinline__ u32x2 lds_tr16(const char DCP_LDS* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int kVm>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((kVm & 0xF) | ((kVm >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// One 16-byte-per-lane HBM -> LDS copy: LDS bytes [lds + 16 lane, + 16) <- global
-// sbase + voff (scalar base, 32-bit lane offset).  M0 carries the LDS address; one wait
-// state separates its write from the copy that reads it.
-__device__ __forceinline__ void copy16_sbase(uint32_t lds, uint32_t voff, const char* sbase) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-// The same from a per-lane 64-bit address.
-__device__ __forceinline__ void copy16_vaddr(uint32_t lds, const char* src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
 
 // O^T tile += V^T P^T with the accumulator pinned to AGPRs.  kNop inserts wait states
 // first, for an operand written by a VALU op just before (the weights, or a rescaled
@@ -618,7 +596,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 }  // namespace
 
 hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream) {
+                            float* o_out, float* lse_out, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1) {
   MlaKArgs k;
   k.q = static_cast<const uint16_t*>(a.q);
   k.lat = static_cast<const char*>(a.latent);
@@ -641,9 +620,11 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   const dim3 grid((unsigned)(groups8 * kXcds * kGroups));
   const bool fast = (a.interleave % kTile) == 0 && (a.block_size % kTile) == 0;
   if (fast)
-    hipLaunchKernelGGL(mla_shard_kernel<true>, grid, dim3(kWaves * 64), 0, stream, k);
+    hipExtLaunchKernelGGL(mla_shard_kernel<true>, grid, dim3(kWaves * 64), 0, stream, ev0, ev1, 0,
+                          k);
   else
-    hipLaunchKernelGGL(mla_shard_kernel<false>, grid, dim3(kWaves * 64), 0, stream, k);
+    hipExtLaunchKernelGGL(mla_shard_kernel<false>, grid, dim3(kWaves * 64), 0, stream, ev0, ev1,
+                          0, k);
   return hipGetLastError();
 }
 

@@ -118,10 +118,11 @@ int dcp_attn_shard(const dcp_attn_desc* desc, const void* q, const void* kv_page
                    float scale, float* o_partial, float* lse, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
-/* dcp_attn_shard with instrumentation: when non-null, `ev_begin` and `ev_end` are
- * recorded on `stream` immediately before and after the shard's attention kernel (the
- * planning and split-combine launches fall outside them), so a caller can time that
- * kernel alone.  Same arguments, results and errors as dcp_attn_shard. */
+/* dcp_attn_shard with instrumentation: when non-null, `ev_begin` and `ev_end` (created by
+ * the caller with timing enabled) take the start and end time stamps of the shard's
+ * attention kernel itself (launched through hipExtLaunchKernel; the planning and
+ * split-combine launches fall outside them), so hipEventElapsedTime gives that kernel's
+ * duration alone.  Same arguments, results and errors as dcp_attn_shard. */
 int dcp_attn_shard_timed(const dcp_attn_desc* desc, const void* q, const void* kv_pages,
                          const void* v_pages, const int32_t* block_table,
                          const int32_t* seq_lens, int batch, int64_t max_seq_len, int rank,
