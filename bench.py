@@ -161,13 +161,11 @@ def run_step_fns(dca, w, inp, kind):
             dca.shard(q, kv, v, inp["block_table"], inp["seq_lens"], r, C, w.interleave,
                       w.scale, kind=kind, max_seq_len=inp["max_seq_len"], out=o_parts[r],
                       lse=l_parts[r], workspace=ws, events=ev)
+        ev = None
         if record:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            ev[0].record()
-        dca.merge(o_parts, l_parts, out=o, lse_out=lse)
-        if record:
-            ev[1].record()
             merge_events.append(ev)
+        dca.merge(o_parts, l_parts, out=o, lse_out=lse, events=ev)
 
     return step, shard_events, merge_events, ws
 

@@ -62,6 +62,7 @@ _SIGS = {
     "dcp_attn_shard_timed": (_I, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I,
                                   _F, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
     "dcp_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
+    "dcp_merge_timed": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "dcp_shard_slots": (_I, [_P, _P, _I, _I, _I, _I64, _I, _I, _I, _P, _P, _P, _P]),
     "dcp_local_len": (_I64, [_I64, _I, _I, _I]),
     "dcp_check_parallel": (_I, [_I, _I, _I, _I]),
@@ -219,8 +220,10 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
 
 
 def merge(o_partials, lse_partials, *, out_dtype=torch.float32, out=None, lse_out=None,
-          want_lse=True, stream=None):
-    """LSE merge of o_partials [C, b, H, Dv] / lse_partials [C, b, H] -> (O, lse)."""
+          want_lse=True, stream=None, events=None):
+    """LSE merge of o_partials [C, b, H, Dv] / lse_partials [C, b, H] -> (O, lse).
+    `events` = (begin, end) torch.cuda.Event pair that takes the merge kernel's own start and
+    end time stamps."""
     lib = load()
     _need(o_partials, "o_partials", dtype=torch.float32, dim=4)
     _need(lse_partials, "lse_partials", dtype=torch.float32, dim=3)
@@ -232,9 +235,19 @@ def merge(o_partials, lse_partials, *, out_dtype=torch.float32, out=None, lse_ou
     _need(out, "out", dtype=out_dtype)
     if want_lse and lse_out is None:
         lse_out = torch.empty(b, h, dtype=torch.float32, device=o_partials.device)
-    st = lib.dcp_merge(_ptr(o_partials), _ptr(lse_partials), c, b, h, dv, _ptr(out),
-                       _dtype_code(out_dtype), _ptr(lse_out), _stream(stream))
-    _check("dcp_merge", st)
+    if events is None:
+        st = lib.dcp_merge(_ptr(o_partials), _ptr(lse_partials), c, b, h, dv, _ptr(out),
+                           _dtype_code(out_dtype), _ptr(lse_out), _stream(stream))
+        _check("dcp_merge", st)
+    else:
+        ev0, ev1 = events
+        for ev in (ev0, ev1):
+            if not ev.cuda_event:       # torch creates the HIP event on its first record
+                ev.record(stream)
+        st = lib.dcp_merge_timed(_ptr(o_partials), _ptr(lse_partials), c, b, h, dv, _ptr(out),
+                                 _dtype_code(out_dtype), _ptr(lse_out), _stream(stream),
+                                 ctypes.c_void_p(ev0.cuda_event), ctypes.c_void_p(ev1.cuda_event))
+        _check("dcp_merge_timed", st)
     return out, lse_out
 
 

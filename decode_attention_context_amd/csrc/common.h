@@ -134,6 +134,24 @@ __device__ __forceinline__ float wave_max_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Max / sum over lanes 0..7 (DPP steps inside each 8-lane group), returned wave-uniform
+// from lane 0.  Each DPP step reads the register the VALU op before it wrote, so two wait
+// states precede it.
+__device__ __forceinline__ float lanes8_max(float v) {
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+}
+__device__ __forceinline__ float lanes8_sum(float v) {
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int kVm>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -148,9 +148,9 @@ int dcp_attn_shard_timed(const dcp_attn_desc* desc, const void* q, const void* k
                     stream, ev_begin, ev_end);
 }
 
-int dcp_merge(const float* o_partials, const float* lse_partials, int cp_size, int batch,
-              int num_heads, int head_dim_v, void* o_out, int out_dtype, float* lse_out,
-              hipStream_t stream) {
+int dcp_merge_timed(const float* o_partials, const float* lse_partials, int cp_size, int batch,
+                    int num_heads, int head_dim_v, void* o_out, int out_dtype, float* lse_out,
+                    hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (cp_size < 1 || batch < 0 || num_heads < 1 || head_dim_v < 1) return DCP_EINVAL;
   if (out_dtype != DCP_F32 && out_dtype != DCP_BF16) return DCP_EINVAL;
   if ((int64_t)batch * num_heads * head_dim_v * cp_size > ((int64_t)1 << 40)) return DCP_EUNSUPPORTED;
@@ -158,8 +158,16 @@ int dcp_merge(const float* o_partials, const float* lse_partials, int cp_size, i
   if (!o_partials || !lse_partials || !o_out) return DCP_EINVAL;
   if (!aligned(o_partials, 16) || !aligned(o_out, 16)) return DCP_EINVAL;
   const hipError_t e = dcp::launch_merge(o_partials, lse_partials, cp_size, batch, num_heads,
-                                         head_dim_v, o_out, out_dtype == DCP_BF16, lse_out, stream);
+                                         head_dim_v, o_out, out_dtype == DCP_BF16, lse_out, stream,
+                                         ev_begin, ev_end);
   return e == hipSuccess ? DCP_OK : DCP_ELAUNCH;
+}
+
+int dcp_merge(const float* o_partials, const float* lse_partials, int cp_size, int batch,
+              int num_heads, int head_dim_v, void* o_out, int out_dtype, float* lse_out,
+              hipStream_t stream) {
+  return dcp_merge_timed(o_partials, lse_partials, cp_size, batch, num_heads, head_dim_v, o_out,
+                         out_dtype, lse_out, stream, nullptr, nullptr);
 }
 
 int dcp_shard_slots(const int32_t* block_table, const int32_t* seq_lens, int batch,

@@ -15,10 +15,11 @@ hipError_t launch_plan(const int32_t* seq_lens, int batch, int rank, int cp, int
                        int64_t len_cap, int64_t target_items, int tile, int min_chunk,
                        const WsPtrs& ws, hipStream_t stream);
 
-// LSE merge of `n` partials per row (rows = batch * heads).
+// LSE merge of `n` partials per row (rows = batch * heads); ev0 / ev1 (nullable) take the
+// merge kernel's own start and end time stamps.
 hipError_t launch_merge(const float* o_partials, const float* lse_partials, int n, int batch,
                         int heads, int dv, void* o_out, int out_bf16, float* lse_out,
-                        hipStream_t stream);
+                        hipStream_t stream, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Combine of the split partials of each request into the shard output.
 hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, float* o_out,

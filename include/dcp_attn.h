@@ -146,6 +146,14 @@ int dcp_merge(const float* o_partials, const float* lse_partials, int cp_size, i
               int num_heads, int head_dim_v, void* o_out, int out_dtype, float* lse_out,
               hipStream_t stream);
 
+/* dcp_merge with instrumentation: when non-null, `ev_begin` and `ev_end` (created by the
+ * caller with timing enabled) take the start and end time stamps of the merge kernel itself
+ * (launched through hipExtLaunchKernel), so hipEventElapsedTime gives its duration alone.
+ * Same arguments, results and errors as dcp_merge. */
+int dcp_merge_timed(const float* o_partials, const float* lse_partials, int cp_size, int batch,
+                    int num_heads, int head_dim_v, void* o_out, int out_dtype, float* lse_out,
+                    hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+
 /* Physical slots (page * block_size + t % block_size, int64) of the tokens a rank stores,
  * in ascending global position t: the library's block-table walk made visible.
  * out_offsets  int64 [batch]: where request b's slots start in slots_out; request b
