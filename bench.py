@@ -167,6 +167,7 @@ def run_step_fns(dca, w, inp, kind):
             merge_events.append(ev)
         dca.merge(o_parts, l_parts, out=o, lse_out=lse, events=ev)
 
+    step.bufs = (o_parts, l_parts, o, lse)
     return step, shard_events, merge_events, ws
 
 
@@ -306,7 +307,26 @@ def secondary_mla(dca, wl, torch, steps=20):
     flops = sum(c[1] for c in costs) / C
     merge_us = sum(a.elapsed_time(b) for a, b in merge_ev) / len(merge_ev) * 1e3
     merge_bytes = (C + 1) * w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
-    del inp
+    # The same merge with its 134 MB of partials evicted from L2 and the 256 MB MALL by a
+    # 1 GiB read before each launch (HBM rate), and with them just read by the previous
+    # merge (cached rate).  In the step above the partials of the later ranks may still be
+    # cached, those of the first ranks are not.
+    o_parts, l_parts, o, lse = step.bufs
+    flush = torch.ones(1 << 28, device="cuda")
+
+    def merge_median(prep, reps=12):
+        ms = []
+        for _ in range(reps):
+            prep()
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            dca.merge(o_parts, l_parts, out=o, lse_out=lse, events=ev)
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        return sorted(ms)[len(ms) // 2]
+
+    merge_hbm_us = merge_median(lambda: flush.sum())
+    merge_cached_us = merge_median(lambda: None)
+    del inp, flush
     torch.cuda.empty_cache()
     return {"workload": w.name, "mla_shard_avg_us": round(dur * 1e6, 2),
             "mla_mfma_util": round(flops / dur / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -316,7 +336,11 @@ def secondary_mla(dca, wl, torch, steps=20):
             "mla_traffic": load_counters("mla_shard", "mla_shard.hip", w.name),
             "mla_kv_tokens_per_s": round(sum(c[2] for c in costs) / C / dur, 1),
             "merge8_us": round(merge_us, 2),
-            "merge8_gbs": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1)}
+            "merge8_gbs": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1),
+            "merge8_hbm_us": round(merge_hbm_us, 2),
+            "merge8_hbm_gbs": round(merge_bytes / (merge_hbm_us * 1e-6) / 1e9, 1),
+            "merge8_cached_us": round(merge_cached_us, 2),
+            "merge8_cached_gbs": round(merge_bytes / (merge_cached_us * 1e-6) / 1e9, 1)}
 
 
 if __name__ == "__main__":

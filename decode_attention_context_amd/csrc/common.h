@@ -160,21 +160,36 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One 16-byte-per-lane HBM -> LDS copy: LDS bytes [lds + 16 lane, + 16) <- global
 // sbase + voff (scalar base, 32-bit lane offset).  M0 carries the LDS address; one wait
-// state separates its write from the copy that reads it.  The copies stream data that is
-// read once per launch, so they carry the non-temporal cache policy (nt): streamed this
-// way the HBM -> LDS rate rises from about 5.9 to 7.1 TB/s on MI355X.
+// state separates its write from the copy that reads it.  kNt selects the non-temporal
+// cache policy (nt): a plain stream of HBM -> LDS copies runs at about 7.1 TB/s with it
+// against 5.9 TB/s without on MI355X, which the HBM-bound GQA kernel takes; the MLA kernel,
+// bound by its matrix work, runs about 5% slower with it and copies without.
+template <bool kNt>
 __device__ __forceinline__ void copy16_sbase(uint32_t lds, uint32_t voff, const char* sbase) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-               :
-               : "s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
+  if constexpr (kNt)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
 }
 // The same from a per-lane 64-bit address.
+template <bool kNt>
 __device__ __forceinline__ void copy16_vaddr(uint32_t lds, const char* src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
+  if constexpr (kNt)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "memory", "m0");
 }
 
 // float -> bf16 bits, round to nearest even (NaN -> quiet NaN).

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     const uint32_t voff = (uint32_t)slot_row[k] < ts.lim
                               ? (uint32_t)slot_row[k] * kRowBytes + slot_src[k]
                               : slot_src[k];
-    copy16_sbase(ts.dst + slot_dst[k], voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
+    copy16_sbase<true>(ts.dst + slot_dst[k], voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
   };
   // ---- all of this wave's HBM -> LDS copies of tile ti; returns the mask of valid tokens
   auto issue_tile = [&](int ti) -> uint64_t {
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     for (int k = 0; k < kDmaPerWave; ++k) {
       const int sl = w * kDmaPerWave + k;
       const uint32_t rr = __shfl(row, slot_row[k], 64);
-      copy16_vaddr(dst + slot_dst[k],
+      copy16_vaddr<true>(dst + slot_dst[k],
                    (sl < 16 ? a.kp : a.vp) + (size_t)rr * kRowBytes + slot_src[k]);
     }
     return __ballot(ok);

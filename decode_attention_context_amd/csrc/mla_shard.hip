@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
           if (k < nslots) {
             const uint32_t voff =
                 ts.full ? slot_off[k] : (slot_off[k] < ts.lim ? slot_off[k] : slot_col[k]);
-            copy16_sbase(dst + k * 1024, voff, ts.base);
+            copy16_sbase<false>(dst + k * 1024, voff, ts.base);
           }
         }
         return vm_new;
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
         for (int k = 0; k < kSlotsHi; ++k) {
           if (k < nslots) {
             const uint32_t rr = __shfl(lrow, slot_row[k], 64);
-            copy16_vaddr(dst + k * 1024, a.lat + (size_t)rr * kRowBytes + slot_col[k]);
+            copy16_vaddr<false>(dst + k * 1024, a.lat + (size_t)rr * kRowBytes + slot_col[k]);
           }
         }
         return __ballot(ok);
