@@ -28,9 +28,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
 def _src_hash(name):
-    p = os.path.join(ROOT, "decode_attention_context_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of a kernel source together with the headers every kernel includes."""
+    h = hashlib.sha256()
+    for n in (name, "common.h", "launch.h"):
+        with open(os.path.join(ROOT, "decode_attention_context_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def owned_tokens_count(L, rank, cp, il):
@@ -340,7 +343,8 @@ def secondary_mla(dca, wl, torch, steps=20):
             "merge8_hbm_us": round(merge_hbm_us, 2),
             "merge8_hbm_gbs": round(merge_bytes / (merge_hbm_us * 1e-6) / 1e9, 1),
             "merge8_cached_us": round(merge_cached_us, 2),
-            "merge8_cached_gbs": round(merge_bytes / (merge_cached_us * 1e-6) / 1e9, 1)}
+            "merge8_cached_gbs": round(merge_bytes / (merge_cached_us * 1e-6) / 1e9, 1),
+            "merge8_traffic": load_counters("merge_small", "merge.hip", w.name)}
 
 
 if __name__ == "__main__":
