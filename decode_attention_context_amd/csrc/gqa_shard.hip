@@ -68,6 +68,7 @@ constexpr int kSlots = 2 * kTileBytes / 1024;   // 1-KiB copies per tile (K then
 constexpr int kKBlock = 1024 + 64;
 constexpr int kKBytes = (kTile / 4) * kKBlock;   // K part of a buffer
 constexpr int kBufBytes = kKBytes + kTileBytes;  // K blocks, then the V rows
+constexpr float kRescaleSlack = 8.f;             // see the online softmax below
 
 struct GqaKArgs {
   const void* q;
@@ -142,10 +143,12 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
   const char DCP_LDS* kvb = (const char DCP_LDS*)&kvs[0];
   const uint32_t lds_addr = (uint32_t)(uintptr_t)kvb;
 
-  float m[HPW], ls[HPW], acc[HPW][NA];
+  // running max (log2 units), -m (0 while m is -inf), per-lane share of the running sum
+  float m[HPW], negm[HPW], ls[HPW], acc[HPW][NA];
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
     m[h] = neg_inf();
+    negm[h] = 0.f;
     ls[h] = 0.f;
 #pragma unroll
     for (int k = 0; k < NA; ++k) acc[h][k] = 0.f;
@@ -292,26 +295,20 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     // ---- scores: lane = token
     float s[HPW];
     if constexpr (kQResident) {
-      // the K row moves to registers in two halves (32 VGPRs each)
+      // the whole K row moves to registers at once (64 VGPRs): all 16 reads in flight
       float s2[2] = {0.f, 0.f};
+      u32x4 kr[kChunks];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 kr[kChunks / 2];
+      for (int c = 0; c < kChunks; ++c) kr[c] = kchunk(c);
 #pragma unroll
-        for (int c = 0; c < kChunks / 2; ++c) {
-          const int cc = hf * (kChunks / 2) + c;
-          kr[c] = kchunk(cc);
+      for (int c = 0; c < kChunks / 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t kd = kr[4 * c + e / 4][e % 4];
+          const uint32_t qd = qres[c][e];
+          if constexpr (kBf16) s2[e & 1] = dot2_bf16(qd, kd, s2[e & 1]);
+          else s2[e & 1] = fmaf(__uint_as_float(qd), __uint_as_float(kd), s2[e & 1]);
         }
-#pragma unroll
-        for (int c = 0; c < kChunks / 8; ++c)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t kd = kr[4 * c + e / 4][e % 4];
-            const uint32_t qd = qres[hf * (kChunks / 8) + c][e];
-            if constexpr (kBf16) s2[e & 1] = dot2_bf16(qd, kd, s2[e & 1]);
-            else s2[e & 1] = fmaf(__uint_as_float(qd), __uint_as_float(kd), s2[e & 1]);
-          }
-      }
       s[0] = s2[0] + s2[1];
     } else {
       u32x4 krow[kChunks];
@@ -348,22 +345,29 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
       for (int h = 0; h < HPW; ++h) s[h] = sacc[h][0] + sacc[h][1];
     }
 
-    // ---- online softmax (base 2); weights to LDS for the P.V lanes
-    const bool full = vm0 == ~0ull;   // uniform: mask only partial tiles
-    const bool valid = full || ((vm0 >> lane) & 1);
+    // ---- online softmax (base 2); weights to LDS for the P.V lanes.  The running max m
+    // only moves when a tile's max exceeds it by more than kRescaleSlack (always on the
+    // first tile with a valid token); in between the weights stay below 2^kRescaleSlack and
+    // the accumulators are not touched.  The final normalisation by the running sum makes
+    // the result exact for any reference m.
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-      const float x = valid ? s[h] * a.sl2 : neg_inf();
-      const float mn = fmaxf(m[h], wave_max_bcast(x));
-      float alpha = 1.f, p = 0.f;
-      if (mn != neg_inf()) {
-        alpha = __builtin_amdgcn_exp2f(m[h] - mn);
-        p = __builtin_amdgcn_exp2f(x - mn);
+      float x = s[h] * a.sl2;
+      if (vm0 != ~0ull) {   // partial tile (uniform); the empty asm keeps this a branch
+        asm volatile("");
+        x = ((vm0 >> lane) & 1) ? x : neg_inf();
       }
-      m[h] = mn;
-      ls[h] = fmaf(ls[h], alpha, p);
+      const float tmax = wave_max_bcast(x);
+      if (tmax > m[h] + kRescaleSlack) {   // uniform branch; m = -inf: any valid tile
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);   // m = -inf -> 0
+        m[h] = tmax;
+        negm[h] = -tmax;
+        ls[h] *= alpha;
 #pragma unroll
-      for (int k = 0; k < NA; ++k) acc[h][k] *= alpha;
+        for (int k = 0; k < NA; ++k) acc[h][k] *= alpha;
+      }
+      const float p = __builtin_amdgcn_exp2f(x + negm[h]);   // masked: 0
+      ls[h] += p;
       if constexpr (kBf16) {
         // tokens 2k and 2k + 1 as one bf16x2 word (round to nearest even), written by the
         // even lane
