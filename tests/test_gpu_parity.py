@@ -19,11 +19,14 @@ from parity_helpers import check_requests, run_shards, scale_of
 pytestmark = pytest.mark.gpu
 
 
-def _run_and_check(w, requests=None, label=None):
+def _run_and_check(w, requests=None, label=None, q_scale=None):
     torch.cuda.synchronize()
     print(f"[parity] {label or w.name}: batch={w.batch} C={w.cp_size} I={w.interleave} "
-          f"B={w.block_size}", flush=True)
+          f"B={w.block_size} q_scale={q_scale}", flush=True)
     inp = wl.make_inputs(w, device="cuda")
+    if q_scale is not None:
+        # the oracle reads the same (rescaled, re-rounded) query back from the device
+        inp["q"] = (inp["q"].float() * q_scale).to(inp["q"].dtype)
     kind = dca.GQA if w.kind == "gqa" else dca.MLA
     o_parts, l_parts = run_shards(inp, kind, w.cp_size, w.interleave, w.scale)
     o_m, l_m = dca.merge(o_parts, l_parts)
@@ -70,6 +73,17 @@ def test_gqa_small(gpu_lib, w):
 @pytest.mark.parametrize("w", SMALL_MLA, ids=[w.name for w in SMALL_MLA])
 def test_mla_small(gpu_lib, w):
     _run_and_check(w)
+
+
+# Queries scaled by 30: score spreads of tens of log2 units, so the running max of every
+# head jumps by more than the kernels' rescale slack many times per request and the
+# softmax is nearly one-hot (the lazy-rescale and near-overflow paths).
+LARGE_Q = [SMALL_GQA[1], SMALL_GQA[3], SMALL_GQA[4], SMALL_MLA[0], SMALL_MLA[3]]
+
+
+@pytest.mark.parametrize("w", LARGE_Q, ids=[w.name + "_q30" for w in LARGE_Q])
+def test_large_scores(gpu_lib, w):
+    _run_and_check(w, label=w.name + "_q30", q_scale=30.0)
 
 
 def test_gqa_full_share(gpu_lib):
