@@ -74,6 +74,14 @@ constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
 constexpr int kDppRowMirror = 0x140;     // lane i <-> 15 - i within each 16 lanes
 
+// Max of two floats as v_maximum3_f32 computes it: no quieting of the operands first (which
+// fmaxf implies and costs an instruction per operand that the compiler cannot prove
+// canonical).  It differs from fmaxf only for NaN operands; the kernels compare finite
+// values and -inf.
+__device__ __forceinline__ float max_f(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Row-local lane permutation (every lane reads a lane of its own 16-lane row, so the
 // bound control never applies); an undefined old value lets the compiler fuse the move
 // into the consuming VALU op (v_max_f32_dpp, v_add_f32_dpp).

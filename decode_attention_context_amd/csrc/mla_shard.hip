@@ -340,26 +340,32 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
         const f4 s1 = sm1 + xsrc[1];
         // scores: x[i] is token 4 g + i, x[4 + i] token 16 + 4 g + i; masked rows -> -inf
         float x[8];
-        {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = s0[i];
+          x[4 + i] = s1[i];
+        }
+        if ((uint32_t)vm0 != 0xffffffffu) {   // partial tile (uniform); the empty asm keeps
+          asm volatile("");                   // the masking a branch
           const uint32_t lo = (uint32_t)(vm0 >> (4 * g)) & 0xFu;
           const uint32_t hi = (uint32_t)(vm0 >> (16 + 4 * g)) & 0xFu;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            x[i] = ((lo >> i) & 1u) ? s0[i] : neg_inf();
-            x[4 + i] = ((hi >> i) & 1u) ? s1[i] : neg_inf();
+            x[i] = ((lo >> i) & 1u) ? x[i] : neg_inf();
+            x[4 + i] = ((hi >> i) & 1u) ? x[4 + i] : neg_inf();
           }
         }
         // tile max of this lane's head: within the lane, then across the four 16-lane
         // rows (which hold the same head) with two swaps
-        float tm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        float tm = max_f(max_f(max_f(x[0], x[1]), max_f(x[2], x[3])),
+                         max_f(max_f(x[4], x[5]), max_f(x[6], x[7])));
         {
           const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tm),
                                                              __float_as_uint(tm), false, false);
-          tm = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+          tm = max_f(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
           const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm),
                                                              __float_as_uint(tm), false, false);
-          tm = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+          tm = max_f(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
         }
         const float tmax = tm * a.sl2;
         // The running max only moves when a head's tile max exceeds it by more than
