@@ -11,34 +11,32 @@
 // contraction (about 242 flop/byte), so both products run on v_mfma_f32_16x16x32_bf16.
 //
 // Design:
-//   * Two workgroups of 4 waves per work item (request, local token range), each owning 64
-//     of the 128 heads; wave w of a group owns 16 heads.  A wave keeps its heads' query
-//     (18 k-steps x 8 bf16 per lane) and the fp32 output accumulator (32 tiles of 16 dims x
-//     16 heads, in AGPRs) in registers.  The two groups of an item get workgroup ids
-//     congruent mod 8, so they run on the same XCD and read each latent tile from HBM once
-//     between them (the second read hits that XCD's L2).
+//   * Two workgroups of 12 waves per work item (request, local token range), each owning 64
+//     of the 128 heads (two pairs of 16-head tiles).  The two groups of an item get
+//     workgroup ids congruent mod 8, so they run on the same XCD and read each latent tile
+//     from HBM once between them (the second read hits that XCD's L2).
+//   * Warp specialisation.  Four score waves = (head pair, half of the 576 dims) compute the
+//     partial S^T = K . Q^T of both 16-head tiles of their pair (M = 16 tokens, N = 16
+//     heads, K = 32 latent dims per MFMA; every K operand read feeds two MFMAs), swap the
+//     partial scores of one head tile through LDS and finish the online softmax of the
+//     other.  Eight output waves = (head pair, quarter of the 512 value dims) keep O^T in
+//     AGPRs and, one tile behind, accumulate O^T += V^T . P^T (M = 16 value dims, N = 16
+//     heads, K = 32 tokens), the V^T operand read with ds_read_b64_tr_b16 in the token
+//     order of the score registers.  In both products every lane's results belong to one
+//     head, so the softmax max needs two cross-lane steps and the weights never move
+//     between lanes.
 //   * 32-token tiles of latent rows are copied HBM -> LDS by global_load_lds_dwordx4 (no
-//     register staging) into a 4-deep ring: three tiles in flight while one is computed.
-//     The copies are issued from inline assembly and paced by explicit vector-memory
-//     counter waits plus a bare s_barrier; the compiler, which does not see them, then has
-//     no reason to drain them before LDS reads of the other ring buffers.  The 16-byte
-//     chunks of a row are XOR-swizzled by (row mod 8) so that operand reads spread over
-//     the LDS banks.
+//     register staging) into a 4-deep ring: two tiles in flight while the score waves work
+//     on one and the output waves on the previous one.  The copies are issued from inline
+//     assembly and paced by explicit vector-memory counter waits plus a bare s_barrier;
+//     the compiler, which does not see them, then has no reason to drain them before LDS
+//     reads.  The 16-byte chunks of a row are XOR-swizzled by (row mod 8), which spreads
+//     the operand reads over the LDS banks.
 //   * When the interleave and the block size are multiples of 32, every tile is one run of
-//     consecutive slots in one page: one scalar block-table read locates it and each lane
-//     copies from precomputed offsets off that base.  Otherwise each lane walks its own
-//     token (the general kernel).
-//   * Scores as S^T = K . Q^T (M = 16 tokens, N = 16 heads, K = 32 latent dims): every
-//     lane's results belong to ONE head, so the online-softmax max needs only two
-//     cross-lane steps and the weights never move between lanes.
-//   * Output as O^T = V^T . P^T (M = 16 value dims, N = 16 heads, K = 32 tokens).  The
-//     weight operand is the scores' exponentials rounded to bf16; the V^T operand is read
-//     with ds_read_b64_tr_b16, which transposes 16-bit elements across each 16-lane group,
-//     in the same token order as the score registers.  Accumulator lanes again hold one
-//     head, so the online-softmax rescale is lane-local.
-//   * The running max only moves when a tile's max exceeds it by more than 8 (log2
-//     units).  That rare event leaves the steady tile loop, rescales the accumulator and
-//     re-enters it, so inside the loop the accumulator is only ever touched by MFMAs.
+//     consecutive slots in one page, located by one readlane from a per-wave table of tile
+//     sources; otherwise each lane walks its own token (the general kernel).
+//   * The running max only moves when a tile's max exceeds it by more than 8 (log2 units);
+//     the output waves rescale their accumulators only on such tiles.
 #include "launch.h"
 
 namespace dcp {
