@@ -282,11 +282,26 @@ def main():
                     "merge_us": round(merge_us, 2),
                     "merge_gbs": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1)},
     }
+    line["kernels"][f"{kernel_name}_interleave1_us"] = fine_interleave_us(dca, torch, w, inp, kind)
     if not args.no_secondary and kind == dca.GQA:
         line["secondary"] = secondary_mla(dca, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)
+
+
+def fine_interleave_us(dca, torch, w, inp, kind, steps=10):
+    """Median shard-kernel time of the same workload and inputs with interleave 1 (every
+    token owned round-robin: the token-granular path instead of page-contiguous tiles)."""
+    step, shard_ev, _, _ = run_step_fns(dca, w.with_(interleave=1), inp, kind)
+    for _ in range(3):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in shard_ev)
+    return round(ms[len(ms) // 2] * 1e3, 2)
 
 
 def secondary_mla(dca, wl, torch, steps=20):
@@ -327,6 +342,7 @@ def secondary_mla(dca, wl, torch, steps=20):
             ms.append(ev[0].elapsed_time(ev[1]) * 1e3)
         return sorted(ms)[len(ms) // 2]
 
+    mla_i1_us = fine_interleave_us(dca, torch, w, inp, dca.MLA)
     merge_hbm_us = merge_median(lambda: flush.sum())
     merge_cached_us = merge_median(lambda: None)
     del inp, flush
@@ -344,7 +360,8 @@ def secondary_mla(dca, wl, torch, steps=20):
             "merge8_hbm_gbs": round(merge_bytes / (merge_hbm_us * 1e-6) / 1e9, 1),
             "merge8_cached_us": round(merge_cached_us, 2),
             "merge8_cached_gbs": round(merge_bytes / (merge_cached_us * 1e-6) / 1e9, 1),
-            "merge8_traffic": load_counters("merge_small", "merge.hip", w.name)}
+            "merge8_traffic": load_counters("merge_small", "merge.hip", w.name),
+            "mla_interleave1_shard_us": mla_i1_us}
 
 
 if __name__ == "__main__":

@@ -34,7 +34,10 @@
 //     the operand reads over the LDS banks.
 //   * When the interleave and the block size are multiples of 32, every tile is one run of
 //     consecutive slots in one page, located by one readlane from a per-wave table of tile
-//     sources; otherwise each lane walks its own token (the general kernel).
+//     sources.  Otherwise (the general kernel, down to interleave 1) the cache row of every
+//     token of a window of 12 tiles sits in an LDS table that the score waves, which have
+//     no copies in flight, build a few tiles ahead; the output waves' copies then read their
+//     rows from LDS and stay paced exactly as for page-contiguous tiles.
 //   * The running max only moves when a tile's max exceeds it by more than 8 (log2 units);
 //     the output waves rescale their accumulators only on such tiles.
 #include "launch.h"
@@ -85,7 +88,10 @@ constexpr int kXOff = kRingBytes;
 constexpr int kPOff = kXOff + kHeadTiles * 64 * 32;             // + 8192
 constexpr int kAOff = kPOff + kHeadTiles * 1024;                // + 4096
 constexpr int kFOff = kAOff + kHeadTiles * 16 * 4;              // + 256
-constexpr int kLdsBytes = kFOff + kHeadTiles * 16 * 4;          // 160256
+constexpr int kTOff = kFOff + kHeadTiles * 16 * 4;              // + 256
+// general tiles: the cache rows of the tokens of kTWin tiles, built ahead by the score waves
+constexpr int kTWin = 12;
+constexpr int kLdsBytes = kTOff + kTWin * kTile * 4;            // + 1536 = 161792
 
 struct MlaKArgs {
   const uint16_t* q;
@@ -227,21 +233,65 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     return ts;
   };
   // mask of valid rows of tile ti (page-contiguous tiles: from the source table)
+  // General tiles: the cache row of every token of a window of kTWin tiles sits in LDS
+  // (~0 for no token or a bad page).  The score waves, which have no copies in flight,
+  // walk the tokens and load the block-table entries (gen_load) and store the rows
+  // (gen_store) a few tiles before the window is first used, so no block-table load ever
+  // waits inside the output waves, whose copies stay paced by the counter alone.
+  uint32_t DCP_LDS* const rowtab = (uint32_t DCP_LDS*)(smem + kTOff);
+  uint32_t gen_t[2];
+  int32_t gen_pg[2];
+  bool gen_ok[2];
+  auto gen_load = [&](int win) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int e = pass * (kQkWaves * 64) + w * 64 + lane;   // entry of the window
+      const int j = j0 + win * kTWin * kTile + e;
+      gen_ok[pass] = e < kTWin * kTile && j < j1;
+      gen_t[pass] = 0;
+      gen_pg[pass] = 0;
+      if (gen_ok[pass]) {
+        gen_t[pass] = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
+        gen_pg[pass] = btb[gen_t[pass] / B];
+      }
+    }
+  };
+  auto gen_store = [&]() {
+    bool bad = false;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int e = pass * (kQkWaves * 64) + w * 64 + lane;
+      if (e < kTWin * kTile) {
+        uint32_t row = ~0u;
+        if (gen_ok[pass]) {
+          const uint32_t lp = gen_t[pass] / B;
+          if (gen_pg[pass] < 0 || (uint32_t)gen_pg[pass] >= a.num_blocks) bad = true;
+          else row = (uint32_t)gen_pg[pass] * B + (gen_t[pass] - lp * B);
+        }
+        rowtab[e] = row;
+      }
+    }
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(&a.header[0], kErrBlockId);
+  };
+  // mask of valid rows of tile ti
   auto tile_mask = [&](int ti) -> uint64_t {
     if constexpr (kFast) {
       (void)tile_src(ti);
       return vm_new;
     } else {
-      const int j = j0 + ti * kTile + lane;
-      bool ok = lane < kTile && j < j1;
-      if (ok) {
-        const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-        const int32_t pg = btb[t / B];
-        ok = pg >= 0 && (uint32_t)pg < a.num_blocks;
-      }
+      const bool ok = lane < kTile && rowtab[(ti % kTWin) * kTile + (lane & (kTile - 1))] != ~0u;
       return __ballot(ok);
     }
   };
+  if constexpr (!kFast) {
+    // window 0 before any copy
+    if (is_qk) {
+      gen_load(0);
+      gen_store();
+    }
+    wait_lgkm0();
+    asm volatile("s_barrier" ::: "memory");
+  }
 
   if (is_qk) {
     // ================= score wave: head pair hp, dims 288 kh .. + 288 =================
@@ -295,6 +345,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     for (int t = 0; t <= ntiles; ++t) {
       wait_lgkm0();   // the previous tile's weights are in LDS before the barrier
       barrier_a(t);
+      // general tiles: the window of tiles t+3 .. is built in this iteration (its first
+      // tile is first read at barrier A of the next one)
+      const bool gen_now = !kFast && (t + 3) % kTWin == 0 && t + 3 < ntiles;
+      if (gen_now) gen_load((t + 3) / kTWin);
       f4 sm0 = {0.f, 0.f, 0.f, 0.f}, sm1 = {0.f, 0.f, 0.f, 0.f};   // own head tile
       if (t < ntiles) {
         const char DCP_LDS* tb = lds + (t % kNBuf) * kTileBytes;
@@ -333,6 +387,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
       }
       wait_lgkm0();   // the partial scores are in LDS before the mid barrier
       asm volatile("s_barrier" ::: "memory");   // barrier B
+      // every wave has read the table entries of tile t+2 (at barrier A): the old window is
+      // done with
+      if (gen_now) gen_store();
       if (t < ntiles) {
         const f4 s0 = sm0 + xsrc[0];
         const f4 s1 = sm1 + xsrc[1];
@@ -444,31 +501,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
         }
         return vm_new;
       } else {
-        // general tiles: each lane walks one token
-        const int j = j0 + ti * kTile + lane;
-        bool ok = lane < kTile && j < j1;
-        bool bad = false;
-        uint32_t lrow = 0;
-        if (ok) {
-          const uint32_t t = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-          const uint32_t lp = t / B;
-          const int32_t pg = btb[lp];
-          if (pg < 0 || (uint32_t)pg >= a.num_blocks) {
-            ok = false;
-            bad = true;
-          } else {
-            lrow = (uint32_t)pg * B + (t - lp * B);
-          }
-        }
-        if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
+        // general tiles: each copy takes the row of its token from the LDS table (rows
+        // without a valid token re-read row 0; their tokens are masked)
+        const uint32_t DCP_LDS* tr = rowtab + (ti % kTWin) * kTile;
 #pragma unroll
         for (int k = 0; k < kSlotsHi; ++k) {
           if (k < nslots) {
-            const uint32_t rr = __shfl(lrow, slot_row[k], 64);
+            const uint32_t r = tr[slot_row[k]];
+            const uint32_t rr = r == ~0u ? 0u : r;
             copy16_vaddr<false>(dst + k * 1024, a.lat + (size_t)rr * kRowBytes + slot_col[k]);
           }
         }
-        return __ballot(ok);
+        return 0ull;
       }
     };
 
@@ -477,11 +521,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     if (ntiles > 1) (void)issue_tile(1);
 
     // Barrier A of iteration t: this wave's copies of tile t have landed (those of tile t+1
-    // may still fly), then every wave's have; tile t+2 starts.  Bare barriers: the fence of __syncthreads would also wait for the copies
-    // still in flight.
+    // may still fly), then every wave's have; tile t+2 starts.  Bare barriers: the fence of
+    // __syncthreads would also wait for the copies still in flight.
     auto barrier_a = [&](int t) {
       if (t < ntiles) {
-        if (kFast && t + 1 < ntiles) {
+        if (t + 1 < ntiles) {
           if (nslots == kSlotsHi) wait_vmcnt<kSlotsHi>();
           else wait_vmcnt<kSlotsLo>();
         } else {
