@@ -30,6 +30,12 @@ Readings taken where the pages are silent (also listed in the design notes):
   R6  GQA query head h reads KV head h // (Hq / Hkv).
   R7  MLA: one latent row per token serves as the key (all 576 columns) and its first 512
       columns serve as the value.
+  R8  multi-token decode (speculative decoding / multi-token prediction combined with DCP,
+      a pairing the guide lists as supported and the blog's roadmap names): a request
+      carries q_len query rows whose keys and values are already the last q_len tokens of
+      its cache; row i sits at position seq_len - q_len + i and attends every position up
+      to and including its own (a causal mask among the draft tokens, aligned to the end
+      of the sequence).  A row whose position is negative attends nothing.
 """
 
 import math
@@ -185,6 +191,61 @@ def mla_full(q_b, latent_pages, block_table_row, seq_len, scale, block_size, dv=
     t = np.arange(int(seq_len), dtype=np.int64)
     rows = _mla_rows(latent_pages, block_table_row, t, block_size)
     return attend(q_b, rows[:, None, :], rows[:, None, :dv], scale)
+
+
+# ----------------------------------------------------------------------------------------
+# Multi-token decode (reading R8; [Guide] "Overview", the speculative-decoding + DCP entry of
+# the feature table; [Blog] "Roadmap")
+# ----------------------------------------------------------------------------------------
+
+def query_positions(seq_len, q_len):
+    """Global position of each of the q_len query rows: seq_len - q_len + i."""
+    return int(seq_len) - int(q_len) + np.arange(int(q_len), dtype=np.int64)
+
+
+def _attend_rows(q_rows, tokens, keys, values, seq_len, scale):
+    """Row i attends the listed tokens at positions <= its own (R8)."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    pos = query_positions(seq_len, q_rows.shape[0])
+    outs, lses = [], []
+    for i in range(q_rows.shape[0]):
+        sel = tokens <= pos[i]
+        o, l = attend(q_rows[i], keys[sel], values[sel], scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+def gqa_shard_mq(q_rows, k_pages, v_pages, block_table_row, seq_len, rank, cp_size,
+                 interleave, scale, block_size):
+    """Partial (O_r [q_len, Hq, Dv], lse_r [q_len, Hq]) of one request's q_len query rows
+    ([q_len, Hq, D]) over the tokens `rank` stores, each row causally masked (R8)."""
+    t = owned_tokens(seq_len, rank, cp_size, interleave)
+    k = _gqa_rows(k_pages, block_table_row, t, block_size)
+    v = _gqa_rows(v_pages, block_table_row, t, block_size)
+    return _attend_rows(q_rows, t, k, v, seq_len, scale)
+
+
+def gqa_full_mq(q_rows, k_pages, v_pages, block_table_row, seq_len, scale, block_size):
+    """Unsharded multi-token attention: every row over all positions up to its own."""
+    t = np.arange(int(seq_len), dtype=np.int64)
+    k = _gqa_rows(k_pages, block_table_row, t, block_size)
+    v = _gqa_rows(v_pages, block_table_row, t, block_size)
+    return _attend_rows(q_rows, t, k, v, seq_len, scale)
+
+
+def mla_shard_mq(q_rows, latent_pages, block_table_row, seq_len, rank, cp_size, interleave,
+                 scale, block_size, dv=MLA_DV):
+    """MLA partial of q_len query rows ([q_len, 128, 576]) over a rank's tokens (R7, R8)."""
+    t = owned_tokens(seq_len, rank, cp_size, interleave)
+    rows = _mla_rows(latent_pages, block_table_row, t, block_size)
+    return _attend_rows(q_rows, t, rows[:, None, :], rows[:, None, :dv], seq_len, scale)
+
+
+def mla_full_mq(q_rows, latent_pages, block_table_row, seq_len, scale, block_size, dv=MLA_DV):
+    t = np.arange(int(seq_len), dtype=np.int64)
+    rows = _mla_rows(latent_pages, block_table_row, t, block_size)
+    return _attend_rows(q_rows, t, rows[:, None, :], rows[:, None, :dv], seq_len, scale)
 
 
 # ----------------------------------------------------------------------------------------
