@@ -222,9 +222,22 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    # eager pass: every launch stamped by its own kernel's start / end (kernel durations)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
+    torch.cuda.synchronize()
+    elapsed_eager = time.perf_counter() - t0
+    assert dca.read_device_errors(ws) == 0
+    # timed pass: the same step (every shard launch + the merge) captured once in a HIP
+    # graph and replayed, so the launches follow each other without host dispatch gaps
+    graph = capture_step(torch, step)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert dca.read_device_errors(ws) == 0
@@ -270,7 +283,9 @@ def main():
     line = {
         "metric": "shard decode attn: HBM GB/s (% peak), KV tokens/s; MLA MFMA util; merge GB/s",
         "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_eager": round(elapsed_eager * 1e3 / args.steps, 4),
+        "step_launch": "hip_graph_replay", "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": int(max(lens)),
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
@@ -285,9 +300,24 @@ def main():
     line["kernels"][f"{kernel_name}_interleave1_us"] = fine_interleave_us(dca, torch, w, inp, kind)
     if not args.no_secondary and kind == dca.GQA:
         line["secondary"] = secondary_mla(dca, wl, torch)
+        line["secondary_ragged"] = secondary_ragged(dca, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)
+
+
+def capture_step(torch, step):
+    """A HIP graph of one step (all launches recorded once on a side stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(False)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(False)
+    return g
 
 
 def fine_interleave_us(dca, torch, w, inp, kind, steps=10):
@@ -362,6 +392,54 @@ def secondary_mla(dca, wl, torch, steps=20):
             "merge8_cached_gbs": round(merge_bytes / (merge_cached_us * 1e-6) / 1e9, 1),
             "merge8_traffic": load_counters("merge_small", "merge.hip", w.name),
             "mla_interleave1_shard_us": mla_i1_us}
+
+
+def secondary_ragged(dca, wl, torch, steps=5):
+    """Ragged MLA batch (512 requests, lognormal lengths around 67000 plus injected edge
+    lengths, C = 8, I = 64): all 8 shard kernels (sum of their durations, MFMA utilisation,
+    HBM rate) and the merge of 8 partials per (request, head) row, the largest merge of the
+    workloads (1.21 GB).  Also the whole step replayed as a HIP graph."""
+    w = wl.MLA_RAGGED
+    inp = wl.make_inputs(w, device="cuda")
+    lens = w.seq_lens()
+    step, shard_ev, merge_ev, ws = run_step_fns(dca, w, inp, dca.MLA)
+    for _ in range(2):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    assert dca.read_device_errors(ws) == 0
+    C = w.cp_size
+    shard_ms = [a.elapsed_time(b) for a, b in shard_ev]
+    shards_s = sum(shard_ms) / steps / 1e3            # all C shard kernels of one step
+    costs = [mla_launch_cost(w, lens, r) for r in range(C)]
+    byts = sum(c[0] for c in costs)
+    flops = sum(c[1] for c in costs)
+    merge_s = sorted(a.elapsed_time(b) for a, b in merge_ev)[len(merge_ev) // 2] / 1e3
+    merge_bytes = (C + 1) * w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
+    graph = capture_step(torch, step)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    empty = sum(1 for L in lens for r in range(C)
+                if owned_tokens_count(int(L), r, C, w.interleave) == 0)
+    del inp, graph
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "kv_tokens": int(lens.sum()), "empty_shards": empty,
+            "mla_shards_us": round(shards_s * 1e6, 1),
+            "mla_mfma_util": round(flops / shards_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mla_hbm_gbs": round(byts / shards_s / 1e9, 1),
+            "merge8_us": round(merge_s * 1e6, 2),
+            "merge8_bytes": merge_bytes,
+            "merge8_gbs": round(merge_bytes / merge_s / 1e9, 1),
+            "merge8_hbm_frac": round(merge_bytes / merge_s / 1e9 / HBM_PEAK_GBS, 4),
+            "step_ms": round(step_s * 1e3, 3),
+            "kv_tokens_per_s": round(int(lens.sum()) / step_s, 1)}
 
 
 if __name__ == "__main__":

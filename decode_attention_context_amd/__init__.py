@@ -57,6 +57,11 @@ _F = ctypes.c_float
 
 _SIGS = {
     "dcp_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Desc), _I, _I64, _I, _I]),
+    "dcp_workspace_size_mq": (ctypes.c_size_t, [ctypes.POINTER(Desc), _I, _I, _I64, _I, _I]),
+    "dcp_attn_shard_mq": (_I, [ctypes.POINTER(Desc), _I, _P, _P, _P, _P, _P, _I, _I64, _I, _I,
+                               _I, _F, _P, _P, _P, ctypes.c_size_t, _P]),
+    "dcp_attn_shard_mq_timed": (_I, [ctypes.POINTER(Desc), _I, _P, _P, _P, _P, _P, _I, _I64, _I,
+                                     _I, _I, _F, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
     "dcp_attn_shard": (_I, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F,
                             _P, _P, _P, ctypes.c_size_t, _P]),
     "dcp_attn_shard_timed": (_I, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I,
@@ -128,27 +133,30 @@ def _need(t, name, dtype=None, dim=None):
 
 
 def make_desc(kind, q, kv_pages, block_table):
-    """Descriptor from the query, the cache pages and the block table.
+    """Descriptor from the query ([b, Hq, D], or [b, q_len, Hq, D] for multi-token decode),
+    the cache pages and the block table.
     GQA kv_pages: [num_blocks, Hkv, B, D]; MLA kv_pages: [num_blocks, B, Dk]."""
     dtype = _dtype_code(q.dtype)
+    hq = q.shape[-2]
     if kind == GQA:
         nb, hkv, bs, d = kv_pages.shape
-        return Desc(GQA, dtype, q.shape[1], hkv, d, d, bs, block_table.shape[1], nb)
+        return Desc(GQA, dtype, hq, hkv, d, d, bs, block_table.shape[1], nb)
     if kind == MLA:
         nb, bs, dk = kv_pages.shape
-        return Desc(MLA, dtype, q.shape[1], 1, dk, 512, bs, block_table.shape[1], nb)
+        return Desc(MLA, dtype, hq, 1, dk, 512, bs, block_table.shape[1], nb)
     raise ValueError("kind must be GQA or MLA")
 
 
-def workspace_size(desc, batch, max_seq_len, cp_size, interleave):
-    n = load().dcp_workspace_size(ctypes.byref(desc), batch, max_seq_len, cp_size, interleave)
+def workspace_size(desc, batch, max_seq_len, cp_size, interleave, q_len=1):
+    n = load().dcp_workspace_size_mq(ctypes.byref(desc), q_len, batch, max_seq_len, cp_size,
+                                     interleave)
     if n == 0:
-        raise DCPError("dcp_workspace_size", -1)
+        raise DCPError("dcp_workspace_size_mq", -1)
     return int(n)
 
 
-def alloc_workspace(desc, batch, max_seq_len, cp_size, interleave, device=None):
-    n = workspace_size(desc, batch, max_seq_len, cp_size, interleave)
+def alloc_workspace(desc, batch, max_seq_len, cp_size, interleave, device=None, q_len=1):
+    n = workspace_size(desc, batch, max_seq_len, cp_size, interleave, q_len)
     return torch.empty(n, dtype=torch.uint8, device=device or torch.device("cuda"))
 
 
@@ -159,14 +167,20 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
 
     GQA: q [b, Hq, D], kv_pages = K pages [nb, Hkv, B, D], v_pages = V pages (same shape).
     MLA: q [b, 128, 576] bf16, kv_pages = latent pages [nb, B, 576], v_pages None.
+    Multi-token decode: q [b, q_len, Hq, D] (q_len <= 4), query position i of request b at
+    global position seq_len - q_len + i, causally masked (dcp_attn_shard_mq).
     block_table int32 [b, max_blocks]; seq_lens int32 [b] (global lengths).
-    Returns (O_r float32 [b, Hq, Dv], lse_r float32 [b, Hq], workspace).
+    Returns (O_r float32 [b, Hq, Dv] or [b, q_len, Hq, Dv], lse_r float32 [b, Hq] or
+    [b, q_len, Hq], workspace).
     `events` = (begin, end) torch.cuda.Event pair that takes the attention kernel's own start
     and end time stamps."""
     lib = load()
     if kind is None:
         kind = MLA if v_pages is None else GQA
-    _need(q, "q", dim=3)
+    _need(q, "q")
+    if q.dim() not in (3, 4):
+        raise ValueError(f"q must be [b, Hq, D] or [b, q_len, Hq, D], got {tuple(q.shape)}")
+    q_len = q.shape[1] if q.dim() == 4 else 1
     _need(kv_pages, "kv_pages", dtype=q.dtype)
     if kind == GQA:
         _need(v_pages, "v_pages", dtype=q.dtype)
@@ -180,61 +194,71 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     if block_table.shape[0] != batch or seq_lens.shape[0] != batch:
         raise ValueError("q, block_table and seq_lens disagree on the batch size")
     desc = make_desc(kind, q, kv_pages, block_table)
-    if kind == GQA and (q.shape[2] != desc.head_dim_qk):
+    if q.shape[-1] != desc.head_dim_qk:
         raise ValueError("q head dim does not match the cache")
-    if kind == MLA and q.shape[2] != desc.head_dim_qk:
-        raise ValueError("q head dim does not match the latent cache")
     if max_seq_len is None:
         max_seq_len = desc.max_blocks_per_seq * desc.block_size
     dv = desc.head_dim_v
+    rows = (batch,) + ((q_len,) if q.dim() == 4 else ()) + (desc.num_q_heads,)
     if out is None:
-        out = torch.empty(batch, desc.num_q_heads, dv, dtype=torch.float32, device=q.device)
+        out = torch.empty(rows + (dv,), dtype=torch.float32, device=q.device)
     if lse is None:
-        lse = torch.empty(batch, desc.num_q_heads, dtype=torch.float32, device=q.device)
+        lse = torch.empty(rows, dtype=torch.float32, device=q.device)
     _need(out, "out", dtype=torch.float32)
     _need(lse, "lse", dtype=torch.float32)
-    if tuple(out.shape) != (batch, desc.num_q_heads, dv) or tuple(lse.shape) != (batch, desc.num_q_heads):
+    if tuple(out.shape) != rows + (dv,) or tuple(lse.shape) != rows:
         raise ValueError("out / lse have the wrong shape")
-    need = workspace_size(desc, batch, max_seq_len, cp_size, interleave)
+    need = workspace_size(desc, batch, max_seq_len, cp_size, interleave, q_len)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args = (_ptr(q), _ptr(kv_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), batch,
+            int(max_seq_len), rank, cp_size, interleave, float(scale), _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(stream))
     if events is None:
-        st = lib.dcp_attn_shard(ctypes.byref(desc), _ptr(q), _ptr(kv_pages), _ptr(v_pages),
-                                _ptr(block_table), _ptr(seq_lens), batch, int(max_seq_len),
-                                rank, cp_size, interleave, float(scale), _ptr(out), _ptr(lse),
-                                _ptr(workspace), workspace.numel(), _stream(stream))
-        _check("dcp_attn_shard", st)
+        if q.dim() == 3:
+            _check("dcp_attn_shard", lib.dcp_attn_shard(ctypes.byref(desc), *args))
+        else:
+            _check("dcp_attn_shard_mq", lib.dcp_attn_shard_mq(ctypes.byref(desc), q_len, *args))
     else:
         ev0, ev1 = events
         for ev in (ev0, ev1):
             if not ev.cuda_event:       # torch creates the HIP event on its first record
                 ev.record(stream)
-        st = lib.dcp_attn_shard_timed(ctypes.byref(desc), _ptr(q), _ptr(kv_pages),
-                                      _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), batch,
-                                      int(max_seq_len), rank, cp_size, interleave, float(scale),
-                                      _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-                                      _stream(stream), ctypes.c_void_p(ev0.cuda_event),
-                                      ctypes.c_void_p(ev1.cuda_event))
-        _check("dcp_attn_shard_timed", st)
+        evs = (ctypes.c_void_p(ev0.cuda_event), ctypes.c_void_p(ev1.cuda_event))
+        if q.dim() == 3:
+            _check("dcp_attn_shard_timed",
+                   lib.dcp_attn_shard_timed(ctypes.byref(desc), *args, *evs))
+        else:
+            _check("dcp_attn_shard_mq_timed",
+                   lib.dcp_attn_shard_mq_timed(ctypes.byref(desc), q_len, *args, *evs))
     return out, lse, workspace
 
 
 def merge(o_partials, lse_partials, *, out_dtype=torch.float32, out=None, lse_out=None,
           want_lse=True, stream=None, events=None):
-    """LSE merge of o_partials [C, b, H, Dv] / lse_partials [C, b, H] -> (O, lse).
-    `events` = (begin, end) torch.cuda.Event pair that takes the merge kernel's own start and
-    end time stamps."""
+    """LSE merge of o_partials [C, b, H, Dv] / lse_partials [C, b, H] -> (O, lse).  Partials
+    of multi-token decode, [C, b, q_len, H, Dv] / [C, b, q_len, H], merge the same way (rows
+    b x q_len*H).  `events` = (begin, end) torch.cuda.Event pair that takes the merge
+    kernel's own start and end time stamps."""
     lib = load()
-    _need(o_partials, "o_partials", dtype=torch.float32, dim=4)
-    _need(lse_partials, "lse_partials", dtype=torch.float32, dim=3)
-    c, b, h, dv = o_partials.shape
-    if tuple(lse_partials.shape) != (c, b, h):
+    _need(o_partials, "o_partials", dtype=torch.float32)
+    _need(lse_partials, "lse_partials", dtype=torch.float32)
+    if o_partials.dim() not in (4, 5) or lse_partials.dim() != o_partials.dim() - 1:
+        raise ValueError("o_partials must be [C, b, H, Dv] or [C, b, q_len, H, Dv]")
+    if tuple(lse_partials.shape) != tuple(o_partials.shape[:-1]):
         raise ValueError("lse_partials shape does not match o_partials")
+    c, b, dv = o_partials.shape[0], o_partials.shape[1], o_partials.shape[-1]
+    rows_shape = tuple(o_partials.shape[1:-1])
+    h = 1
+    for n in rows_shape[1:]:
+        h *= n
     if out is None:
-        out = torch.empty(b, h, dv, dtype=out_dtype, device=o_partials.device)
+        out = torch.empty(rows_shape + (dv,), dtype=out_dtype, device=o_partials.device)
     _need(out, "out", dtype=out_dtype)
+    if tuple(out.shape) != rows_shape + (dv,):
+        raise ValueError("out has the wrong shape")
     if want_lse and lse_out is None:
-        lse_out = torch.empty(b, h, dtype=torch.float32, device=o_partials.device)
+        lse_out = torch.empty(rows_shape, dtype=torch.float32, device=o_partials.device)
     if events is None:
         st = lib.dcp_merge(_ptr(o_partials), _ptr(lse_partials), c, b, h, dv, _ptr(out),
                            _dtype_code(out_dtype), _ptr(lse_out), _stream(stream))

@@ -56,6 +56,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Local end of the shard's tokens that query row `qi` of a q_len-row request sees: the
+// rank's tokens of the first seq_len - q_len + 1 + qi positions (seq_len clamped to the
+// block table as the planner clamps it).
+__device__ __forceinline__ int row_local_end(const int32_t* seq_lens, int b, int64_t len_cap,
+                                             int q_len, int qi, int rank, int cp, int il) {
+  int64_t L = seq_lens[b];
+  L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
+  return (int)dcp_walk_local_count(L - q_len + 1 + qi, rank, cp, il);
+}
+
 // Butterfly reductions across the 64 lanes of a wave.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

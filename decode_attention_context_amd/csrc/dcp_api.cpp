@@ -26,8 +26,11 @@ int device_cus() {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Shape checks shared by the size query and the shard call.
-int check_desc(const dcp_attn_desc* d, int batch, int64_t max_seq_len, int cp, int il) {
+int check_desc(const dcp_attn_desc* d, int q_len, int batch, int64_t max_seq_len, int cp,
+               int il) {
   if (!d || batch < 0 || max_seq_len < 0 || max_seq_len > kMaxI32) return DCP_EINVAL;
+  if (q_len < 1) return DCP_EINVAL;
+  if (q_len > dcp::kMaxQLen) return DCP_EUNSUPPORTED;
   if (cp < 1 || il < 1 || (int64_t)cp * il > kMaxI32) return DCP_EINVAL;
   if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads) return DCP_EINVAL;
   if (d->head_dim_qk < 1 || d->head_dim_v < 1 || d->block_size < 1 || d->max_blocks_per_seq < 1 ||
@@ -38,7 +41,7 @@ int check_desc(const dcp_attn_desc* d, int batch, int64_t max_seq_len, int cp, i
   if (d->dtype != DCP_F32 && d->dtype != DCP_BF16) return DCP_EINVAL;
   if (d->kind == DCP_GQA) {
     if (d->head_dim_qk != d->head_dim_v) return DCP_EUNSUPPORTED;
-    if (!dcp::gqa_supported(d->dtype, d->head_dim_qk, d->num_q_heads / d->num_kv_heads))
+    if (!dcp::gqa_supported(d->dtype, d->head_dim_qk, d->num_q_heads / d->num_kv_heads, q_len))
       return DCP_EUNSUPPORTED;
   } else if (d->kind == DCP_MLA) {
     if (d->dtype != DCP_BF16 || d->num_q_heads != 128 || d->num_kv_heads != 1 ||
@@ -60,8 +63,9 @@ struct Plan {
 
 // Work items: the planner splits the shard's tokens into about `target` items (never more
 // than target + batch), about one round of workgroups over the CUs (GQA: one workgroup per
-// item and KV head; MLA: two workgroups, one per half of the heads, per item).
-bool make_plan(const dcp_attn_desc* d, int batch, Plan* p) {
+// item and KV head; MLA: two workgroups, one per half of the heads, per item and query
+// position).  Partials are kept per query row: q_len * num_q_heads rows per item.
+bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
   const int cus = device_cus();
   if (cus <= 0) return false;
   if (d->kind == DCP_GQA) {
@@ -72,19 +76,19 @@ bool make_plan(const dcp_attn_desc* d, int batch, Plan* p) {
   } else {
     // two head-group workgroups per item, one resident workgroup per CU (144 KiB of LDS)
     p->tile = dcp::kMlaTile;
-    p->target = std::max<int64_t>(1, (int64_t)cus / 2);
+    p->target = std::max<int64_t>(1, (int64_t)cus / (2 * q_len));
     p->min_chunk = 4 * dcp::kMlaTile;
   }
   p->max_items = (int64_t)batch + p->target;
-  p->lay = dcp::ws_layout(batch, p->max_items, d->num_q_heads, d->head_dim_v);
+  p->lay = dcp::ws_layout(batch, p->max_items, q_len * d->num_q_heads, d->head_dim_v);
   return true;
 }
 
-int shard_impl(const dcp_attn_desc* d, const void* q, const void* kv, const void* v,
-               const int32_t* bt, const int32_t* lens, int batch, int64_t max_seq_len, int rank,
-               int cp, int il, float scale, float* o, float* lse, void* ws, size_t ws_bytes,
-               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  int st = check_desc(d, batch, max_seq_len, cp, il);
+int shard_impl(const dcp_attn_desc* d, int q_len, const void* q, const void* kv,
+               const void* v, const int32_t* bt, const int32_t* lens, int batch,
+               int64_t max_seq_len, int rank, int cp, int il, float scale, float* o, float* lse,
+               void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  int st = check_desc(d, q_len, batch, max_seq_len, cp, il);
   if (st != DCP_OK) return st;
   if (rank < 0 || rank >= cp || !std::isfinite(scale)) return DCP_EINVAL;
   if (batch == 0) return DCP_OK;
@@ -93,25 +97,27 @@ int shard_impl(const dcp_attn_desc* d, const void* q, const void* kv, const void
   if (!aligned(q, 16) || !aligned(kv, 16) || (v && !aligned(v, 16)) || !aligned(o, 16))
     return DCP_EINVAL;
   Plan p;
-  if (!make_plan(d, batch, &p)) return DCP_ELAUNCH;
+  if (!make_plan(d, q_len, batch, &p)) return DCP_ELAUNCH;
   if (!ws || !aligned(ws, 256) || ws_bytes < p.lay.total) return DCP_EWORKSPACE;
   const dcp::WsPtrs w = dcp::ws_ptrs(ws, p.lay);
   const int64_t len_cap = (int64_t)d->max_blocks_per_seq * d->block_size;
+  const dcp::RowArgs rows{lens, len_cap, q_len};
 
   hipError_t e = dcp::launch_plan(lens, batch, rank, cp, il, len_cap, p.target, p.tile,
                                   p.min_chunk, w, stream);
   if (e != hipSuccess) return DCP_ELAUNCH;
   if (d->kind == DCP_GQA) {
     dcp::GqaArgs a{q, kv, v, bt, d->num_q_heads, d->num_kv_heads, d->head_dim_qk, d->block_size,
-                   d->max_blocks_per_seq, d->num_blocks, rank, cp, il, scale, d->dtype};
+                   d->max_blocks_per_seq, d->num_blocks, rank, cp, il, scale, d->dtype, rows};
     e = dcp::launch_gqa_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   } else {
     dcp::MlaArgs a{q, kv, bt, d->block_size, d->max_blocks_per_seq, d->num_blocks,
-                   rank, cp, il, scale};
+                   rank, cp, il, scale, rows};
     e = dcp::launch_mla_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   }
   if (e != hipSuccess) return DCP_ELAUNCH;
-  e = dcp::launch_split_combine(w, batch, d->num_q_heads, d->head_dim_v, o, lse, stream);
+  e = dcp::launch_split_combine(w, batch, q_len * d->num_q_heads, d->head_dim_v, o, lse,
+                                stream);
   return e == hipSuccess ? DCP_OK : DCP_ELAUNCH;
 }
 
@@ -119,12 +125,17 @@ int shard_impl(const dcp_attn_desc* d, const void* q, const void* kv, const void
 
 extern "C" {
 
+size_t dcp_workspace_size_mq(const dcp_attn_desc* desc, int q_len, int batch,
+                             int64_t max_seq_len, int cp_size, int interleave) {
+  if (check_desc(desc, q_len, batch, max_seq_len, cp_size, interleave) != DCP_OK) return 0;
+  Plan p;
+  if (!make_plan(desc, q_len, batch, &p)) return 0;
+  return p.lay.total;
+}
+
 size_t dcp_workspace_size(const dcp_attn_desc* desc, int batch, int64_t max_seq_len,
                           int cp_size, int interleave) {
-  if (check_desc(desc, batch, max_seq_len, cp_size, interleave) != DCP_OK) return 0;
-  Plan p;
-  if (!make_plan(desc, batch, &p)) return 0;
-  return p.lay.total;
+  return dcp_workspace_size_mq(desc, 1, batch, max_seq_len, cp_size, interleave);
 }
 
 int dcp_attn_shard(const dcp_attn_desc* desc, const void* q, const void* kv_pages,
@@ -132,9 +143,31 @@ int dcp_attn_shard(const dcp_attn_desc* desc, const void* q, const void* kv_page
                    int batch, int64_t max_seq_len, int rank, int cp_size, int interleave,
                    float scale, float* o_partial, float* lse, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
-  return shard_impl(desc, q, kv_pages, v_pages, block_table, seq_lens, batch, max_seq_len, rank,
-                    cp_size, interleave, scale, o_partial, lse, workspace, workspace_bytes,
-                    stream, nullptr, nullptr);
+  return shard_impl(desc, 1, q, kv_pages, v_pages, block_table, seq_lens, batch, max_seq_len,
+                    rank, cp_size, interleave, scale, o_partial, lse, workspace,
+                    workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dcp_attn_shard_mq(const dcp_attn_desc* desc, int q_len, const void* q, const void* kv_pages,
+                      const void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                      int batch, int64_t max_seq_len, int rank, int cp_size, int interleave,
+                      float scale, float* o_partial, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return shard_impl(desc, q_len, q, kv_pages, v_pages, block_table, seq_lens, batch,
+                    max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
+                    workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dcp_attn_shard_mq_timed(const dcp_attn_desc* desc, int q_len, const void* q,
+                            const void* kv_pages, const void* v_pages,
+                            const int32_t* block_table, const int32_t* seq_lens, int batch,
+                            int64_t max_seq_len, int rank, int cp_size, int interleave,
+                            float scale, float* o_partial, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
+                            hipEvent_t ev_end) {
+  return shard_impl(desc, q_len, q, kv_pages, v_pages, block_table, seq_lens, batch,
+                    max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
+                    workspace_bytes, stream, ev_begin, ev_end);
 }
 
 int dcp_attn_shard_timed(const dcp_attn_desc* desc, const void* q, const void* kv_pages,
@@ -143,9 +176,9 @@ int dcp_attn_shard_timed(const dcp_attn_desc* desc, const void* q, const void* k
                          int cp_size, int interleave, float scale, float* o_partial,
                          float* lse, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  return shard_impl(desc, q, kv_pages, v_pages, block_table, seq_lens, batch, max_seq_len, rank,
-                    cp_size, interleave, scale, o_partial, lse, workspace, workspace_bytes,
-                    stream, ev_begin, ev_end);
+  return shard_impl(desc, 1, q, kv_pages, v_pages, block_table, seq_lens, batch, max_seq_len,
+                    rank, cp_size, interleave, scale, o_partial, lse, workspace,
+                    workspace_bytes, stream, ev_begin, ev_end);
 }
 
 int dcp_merge_timed(const float* o_partials, const float* lse_partials, int cp_size, int batch,

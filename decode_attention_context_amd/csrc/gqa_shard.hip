@@ -10,9 +10,9 @@
 // The work is HBM-bound (per token and KV head: 2 * D * sizeof(T) bytes against
 // 4 * G * D flops), so the design is about keeping K / V bytes streaming at full rate and
 // the vector-ALU work per byte small:
-//   * One workgroup of NW = min(G, 8) waves per work item (request, KV head, local token
-//     range), two workgroups per CU; wave w owns G / NW of the query heads that share the
-//     KV head.
+//   * One workgroup of NW <= 8 waves per work item (request, KV head, local token range),
+//     two workgroups per CU; wave w owns HPW of the R = q_len * G query rows that share the
+//     KV head (q_len query positions per request, see below).
 //   * 64-token tiles of K and V rows are copied HBM -> LDS by global_load_lds_dwordx4 (no
 //     register staging) with the non-temporal cache policy into a double buffer: tiles 0
 //     and 1 are issued up front, then each tile's copies leave right after the barrier that
@@ -40,6 +40,11 @@
 //     16-byte chunk of the V row), the four token groups summed across rows once per item.
 //   * An item that covers a request's whole shard writes (O, lse) directly; otherwise it
 //     writes a normalized partial that the split combine merges.
+//   * Multi-token decode (q_len > 1: speculative decoding or multi-token prediction, the
+//     last q_len cache tokens being the request's own draft tokens): query row i sits at
+//     position seq_len - q_len + i and sees the positions up to its own, i.e. a prefix of
+//     the shard's local tokens.  Every row of the KV head reads each K / V tile once; a
+//     row's causal limit only masks tokens of the last tile or two of a request.
 #include "launch.h"
 
 namespace dcp {
@@ -79,6 +84,9 @@ struct GqaKArgs {
   uint32_t num_blocks;
   int rank, cp, interleave;
   float sl2;  // scale * log2(e)
+  const int32_t* seq_lens;
+  int64_t len_cap;
+  int q_len;
   float* o_out;
   float* lse_out;
   int32_t* header;
@@ -107,12 +115,13 @@ __device__ __forceinline__ int v_swz_t(int r) {
 }
 
 
-constexpr int waves_for(int g) { return g >= 8 ? 8 : g; }
+// Waves and rows per wave for R query rows per KV head: up to 8 waves, rows dealt evenly;
+// rows past R (when the waves do not divide R) repeat the last row and are not written.
+constexpr int waves_for(int r) { return r >= 8 ? 8 : (r > 4 ? 8 : (r > 2 ? 4 : r)); }
+constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r); }
 
-template <bool kBf16, int G>
-__global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArgs a) {
-  constexpr int NW = waves_for(G);
-  constexpr int HPW = G / NW;                   // query heads per wave
+template <bool kBf16, int NW, int HPW>
+__global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
   constexpr int kElemBytes = kBf16 ? 2 : 4;
   constexpr int D = kRowBytes / kElemBytes;     // head dim
   constexpr int NA = kBf16 ? 2 : 4;             // dims (accumulators) per lane per head
@@ -131,11 +140,32 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
   const int b = it.x, j0 = it.y, j1 = it.z;
   const int kvh = blockIdx.y;
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
-  const int head0 = kvh * G + w * HPW;          // first query head of this wave
-  // the wave's query heads: wave-uniform, read-only -> scalar loads
-  const uint32_t DCP_CONST* qh = reinterpret_cast<const uint32_t DCP_CONST*>(
-                                     reinterpret_cast<uintptr_t>(a.q)) +
-                                 ((size_t)b * a.hq + head0) * (kRowBytes / 4);
+  // The wave's query rows (wave-uniform): row rho = w * HPW + h of the R = q_len * G rows
+  // of this KV head is query position qi = rho / G, head kvh * G + rho % G, request row
+  // qi * hq + head.  lim[h] = local end of the tokens the row sees in this item.
+  const int G = a.hq / a.hkv;
+  const int R = a.q_len * G;
+  const int RQ = a.q_len * a.hq;               // rows per request
+  int rrow[HPW], lim[HPW];
+  bool live[HPW];
+  int lim_min = j1;
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    int rho = w * HPW + h;
+    live[h] = rho < R;
+    rho = min(rho, R - 1);
+    const int qi = rho / G;
+    rrow[h] = qi * a.hq + kvh * G + (rho - qi * G);
+    lim[h] = a.q_len == 1 ? j1
+                          : min(j1, row_local_end(a.seq_lens, b, a.len_cap, a.q_len, qi,
+                                                  a.rank, a.cp, a.interleave));
+    lim_min = min(lim_min, lim[h]);
+  }
+  // the query rows: wave-uniform, read-only -> scalar loads
+  const uint32_t DCP_CONST* qbase = reinterpret_cast<const uint32_t DCP_CONST*>(
+                                        reinterpret_cast<uintptr_t>(a.q)) +
+                                    (size_t)b * RQ * (kRowBytes / 4);
+  const uint32_t DCP_CONST* qh = qbase + (size_t)rrow[0] * (kRowBytes / 4);
   const int32_t* btb = a.bt + (size_t)b * a.max_blocks;
   const uint32_t B = (uint32_t)a.block_size;
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
@@ -318,8 +348,8 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
       // scheduling region so that no more than two chunks (32 scalar registers) are live
       constexpr int kQSteps = HPW * (kChunks / 4);
       auto qload = [&](int st) -> u32x16 {
-        uint64_t qa = reinterpret_cast<uint64_t>(qh + (st / (kChunks / 4)) * (kRowBytes / 4) +
-                                                 16 * (st % (kChunks / 4)));
+        uint64_t qa = reinterpret_cast<uint64_t>(
+            qbase + (size_t)rrow[st / (kChunks / 4)] * (kRowBytes / 4) + 16 * (st % (kChunks / 4)));
         asm volatile("" : "+s"(qa));
         return *reinterpret_cast<const u32x16 DCP_CONST*>(qa);
       };
@@ -350,12 +380,13 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     // first tile with a valid token); in between the weights stay below 2^kRescaleSlack and
     // the accumulators are not touched.  The final normalisation by the running sum makes
     // the result exact for any reference m.
+    const int jt = j0 + ti * kTile;   // local index of the tile's first token
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
       float x = s[h] * a.sl2;
-      if (vm0 != ~0ull) {   // partial tile (uniform); the empty asm keeps this a branch
-        asm volatile("");
-        x = ((vm0 >> lane) & 1) ? x : neg_inf();
+      if (vm0 != ~0ull || jt + kTile > lim_min) {   // partial tile (uniform); the empty asm
+        asm volatile("");                            // keeps this a branch
+        x = (((vm0 >> lane) & 1) && jt + lane < lim[h]) ? x : neg_inf();
       }
       const float tmax = wave_max_bcast(x);
       if (tmax > m[h] + kRescaleSlack) {   // uniform branch; m = -inf: any valid tile
@@ -431,9 +462,10 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
     const float lt = wave_sum_dpp(ls[h]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (m[h] + __log2f(lt)) * kLn2 : neg_inf();
-    const int head = head0 + h;
-    float* dst = single ? a.o_out + ((size_t)b * a.hq + head) * D
-                        : a.po + ((size_t)item * a.hq + head) * D;
+    if (!live[h]) continue;   // a repeated row (uniform)
+    const int row = rrow[h];
+    float* dst = single ? a.o_out + ((size_t)b * RQ + row) * D
+                        : a.po + ((size_t)item * RQ + row) * D;
     if constexpr (kBf16) {
       // lane (g, i16): dims 32 g + i16 and 32 g + 16 + i16
       const int d0 = 32 * (lane >> 4) + (lane & 15);
@@ -456,21 +488,34 @@ __global__ __launch_bounds__(64 * waves_for(G), 2) void gqa_shard_kernel(GqaKArg
         *reinterpret_cast<float4*>(dst + 4 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
     }
     if (lane == 0) {
-      if (single) a.lse_out[(size_t)b * a.hq + head] = lse;
-      else a.plse[(size_t)item * a.hq + head] = lse;
+      if (single) a.lse_out[(size_t)b * RQ + row] = lse;
+      else a.plse[(size_t)item * RQ + row] = lse;
     }
   }
 }
 
+template <bool kBf16, int R>
+void launch_r(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  constexpr int NW = waves_for(R), HPW = rows_per_wave(R);
+  hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, NW, HPW>), grid, dim3(64 * NW), 0, s, e0, e1,
+                        0, k);
+}
+
+// R = q_len * G query rows per KV head; rows sharing a (waves, rows per wave) shape share
+// the kernel.
 template <bool kBf16>
-hipError_t launch_g(const GqaKArgs& k, int group, dim3 grid, hipStream_t s, hipEvent_t e0,
+hipError_t launch_g(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
                     hipEvent_t e1) {
-  switch (group) {
-    case 1: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 1>), grid, dim3(64 * waves_for(1)), 0, s, e0, e1, 0, k); break;
-    case 2: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 2>), grid, dim3(64 * waves_for(2)), 0, s, e0, e1, 0, k); break;
-    case 4: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 4>), grid, dim3(64 * waves_for(4)), 0, s, e0, e1, 0, k); break;
-    case 8: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 8>), grid, dim3(64 * waves_for(8)), 0, s, e0, e1, 0, k); break;
-    case 16: hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, 16>), grid, dim3(64 * waves_for(16)), 0, s, e0, e1, 0, k); break;
+  switch (rows) {
+    case 1: launch_r<kBf16, 1>(k, grid, s, e0, e1); break;
+    case 2: launch_r<kBf16, 2>(k, grid, s, e0, e1); break;
+    case 3: case 4: launch_r<kBf16, 4>(k, grid, s, e0, e1); break;
+    case 6: case 8: launch_r<kBf16, 8>(k, grid, s, e0, e1); break;
+    case 12: case 16: launch_r<kBf16, 16>(k, grid, s, e0, e1); break;
+    case 24: launch_r<kBf16, 24>(k, grid, s, e0, e1); break;
+    case 32: launch_r<kBf16, 32>(k, grid, s, e0, e1); break;
+    case 48: launch_r<kBf16, 48>(k, grid, s, e0, e1); break;
+    case 64: launch_r<kBf16, 64>(k, grid, s, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -478,9 +523,10 @@ hipError_t launch_g(const GqaKArgs& k, int group, dim3 grid, hipStream_t s, hipE
 
 }  // namespace
 
-bool gqa_supported(int dtype, int head_dim, int group) {
+bool gqa_supported(int dtype, int head_dim, int group, int q_len) {
   const int elem = dtype == 1 ? 2 : 4;
   if (head_dim * elem != kRowBytes) return false;
+  if (q_len < 1 || q_len > kMaxQLen) return false;
   return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
 }
 
@@ -501,6 +547,9 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
   k.cp = a.cp;
   k.interleave = a.interleave;
   k.sl2 = a.scale * kLog2e;
+  k.seq_lens = a.rows.seq_lens;
+  k.len_cap = a.rows.len_cap;
+  k.q_len = a.rows.q_len;
   k.o_out = o_out;
   k.lse_out = lse_out;
   k.header = ws.header;
@@ -509,9 +558,9 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
   k.plse = ws.plse;
   k.po = ws.po;
   const dim3 grid((unsigned)max_items, (unsigned)a.hkv);
-  const int group = a.hq / a.hkv;
-  return a.dtype == 1 ? launch_g<true>(k, group, grid, stream, ev0, ev1)
-                      : launch_g<false>(k, group, grid, stream, ev0, ev1);
+  const int rows = a.rows.q_len * (a.hq / a.hkv);
+  return a.dtype == 1 ? launch_g<true>(k, rows, grid, stream, ev0, ev1)
+                      : launch_g<false>(k, rows, grid, stream, ev0, ev1);
 }
 
 }  // namespace dcp

@@ -25,6 +25,16 @@ hipError_t launch_merge(const float* o_partials, const float* lse_partials, int 
 hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, float* o_out,
                                 float* lse_out, hipStream_t stream);
 
+// Query rows of a request: q_len positions x the query heads.  Row i of a multi-token
+// request sits at position seq_len - q_len + i and sees the positions up to its own, so it
+// reads the shard's local tokens j < (tokens of a (seq_len - q_len + 1 + i)-token sequence
+// the rank stores).  With q_len = 1 every row sees all of the shard's tokens.
+struct RowArgs {
+  const int32_t* seq_lens;
+  int64_t len_cap;   // block-table capacity in tokens (seq_len is clamped to it)
+  int q_len;
+};
+
 struct GqaArgs {
   const void* q;
   const void* k_pages;
@@ -35,12 +45,13 @@ struct GqaArgs {
   int rank, cp, interleave;
   float scale;
   int dtype;  // 0 f32, 1 bf16
+  RowArgs rows;
 };
 // ev0 / ev1 (nullable): events stamped with the attention kernel's own start and end.
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
                             float* o_out, float* lse_out, hipStream_t stream,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-bool gqa_supported(int dtype, int head_dim, int group);
+bool gqa_supported(int dtype, int head_dim, int group, int q_len);
 
 struct MlaArgs {
   const void* q;
@@ -50,6 +61,7 @@ struct MlaArgs {
   int64_t num_blocks;
   int rank, cp, interleave;
   float scale;
+  RowArgs rows;
 };
 hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& ws,
                             float* o_out, float* lse_out, hipStream_t stream,
@@ -63,5 +75,7 @@ hipError_t launch_shard_slots(const int32_t* block_table, const int32_t* seq_len
 // Tokens per tile of each shard kernel (work items are whole multiples of it).
 constexpr int kGqaTile = 64;
 constexpr int kMlaTile = 32;
+// Most query positions per request (multi-token decode).
+constexpr int kMaxQLen = 4;
 
 }  // namespace dcp

@@ -40,6 +40,11 @@
 //     rows from LDS and stay paced exactly as for page-contiguous tiles.
 //   * The running max only moves when a tile's max exceeds it by more than 8 (log2 units);
 //     the output waves rescale their accumulators only on such tiles.
+//   * Multi-token decode (q_len query positions per request, the last q_len cache tokens
+//     being the request's own draft tokens): each work item gets two workgroups per query
+//     position, all on one XCD.  Position i sees the positions up to seq_len - q_len + i,
+//     a prefix of the shard's local tokens, so its workgroups simply end the item there
+//     (possibly before its first tile: an empty partial, lse = -inf).
 #include "launch.h"
 
 namespace dcp {
@@ -101,6 +106,9 @@ struct MlaKArgs {
   uint32_t num_blocks;
   int rank, cp, interleave;
   float sl2;
+  const int32_t* seq_lens;
+  int64_t len_cap;
+  int q_len;
   float* o_out;
   float* lse_out;
   int32_t* header;
@@ -165,15 +173,24 @@ template <bool kFast>
 __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
-  // Workgroup ids: the kGroups head groups of one work item are congruent mod 8 (same XCD)
-  // and adjacent in dispatch order.
+  // Workgroup ids: the q_len * kGroups (query position, head group) workgroups of one work
+  // item are congruent mod 8 (same XCD) and adjacent in dispatch order.
   const int blk = blockIdx.x;
-  const int hg = (blk / kXcds) % kGroups;
-  const int item = (blk / (kXcds * kGroups)) * kXcds + blk % kXcds;
+  const int ngroups = kGroups * a.q_len;
+  const int hgq = (blk / kXcds) % ngroups;
+  const int qi = hgq / kGroups, hg = hgq - qi * kGroups;
+  const int item = (blk / (kXcds * ngroups)) * kXcds + blk % kXcds;
   if (item >= a.header[1]) return;
   const int4 it = a.items[item];
-  const int b = it.x, j0 = it.y, j1 = it.z;
+  const int b = it.x, j0 = it.y;
+  // query position qi sees a prefix of the shard's tokens
+  const int j1 = a.q_len == 1 ? it.z
+                              : min(it.z, row_local_end(a.seq_lens, b, a.len_cap, a.q_len, qi,
+                                                        a.rank, a.cp, a.interleave));
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
+  // rows of (request b, position qi) and of (item, position qi) in the outputs
+  const size_t orow = ((size_t)b * a.q_len + qi) * kHeads;
+  const size_t prow = ((size_t)item * a.q_len + qi) * kHeads;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -188,7 +205,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const char DCP_LDS* lds = (const char DCP_LDS*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
   const bool is_qk = w < kQkWaves;
-  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
 
   // Page-contiguous tiles: a per-wave table of tile sources, lane k holding the first cache
   // row of tile 64 * window + k (or ~0 for a bad page).  It is built by a lane-parallel walk
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const uint16_t* qrow =
-          a.q + ((size_t)b * kHeads + head_p + 16 * hh) * kDk + 8 * g + 32 * kHalfSteps * kh;
+          a.q + (orow + head_p + 16 * hh) * kDk + 8 * g + 32 * kHalfSteps * kh;
 #pragma unroll
       for (int j = 0; j < kHalfSteps; ++j)
         qreg[hh][j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j);
@@ -460,8 +477,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     if (g == 0) {
       const int head = head_p + 16 * kh;
       ((float DCP_LDS*)(smem + kFOff))[own * 16 + i16] = inv;
-      if (single) a.lse_out[(size_t)b * kHeads + head] = lse;
-      else a.plse[(size_t)item * kHeads + head] = lse;
+      if (single) a.lse_out[orow + head] = lse;
+      else a.plse[prow + head] = lse;
     }
     wait_lgkm0();
     asm volatile("s_barrier" ::: "memory");
@@ -517,7 +534,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     };
 
     // prologue: tiles 0 and 1 in flight
-    (void)issue_tile(0);
+    if (ntiles > 0) (void)issue_tile(0);
     if (ntiles > 1) (void)issue_tile(1);
 
     // Barrier A of iteration t: this wave's copies of tile t have landed (those of tile t+1
@@ -628,8 +645,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int head = head_p + 16 * hh;
-      float* dst = (single ? a.o_out + ((size_t)b * kHeads + head) * kDv
-                           : a.po + ((size_t)item * kHeads + head) * kDv) +
+      float* dst = (single ? a.o_out + (orow + head) * kDv : a.po + (prow + head) * kDv) +
                    dq * 128;
       const float inv = hh ? inv1 : inv0;
 #pragma unroll
@@ -657,6 +673,9 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   k.cp = a.cp;
   k.interleave = a.interleave;
   k.sl2 = a.scale * kLog2e;
+  k.seq_lens = a.rows.seq_lens;
+  k.len_cap = a.rows.len_cap;
+  k.q_len = a.rows.q_len;
   k.o_out = o_out;
   k.lse_out = lse_out;
   k.header = ws.header;
@@ -665,7 +684,7 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   k.plse = ws.plse;
   k.po = ws.po;
   const int64_t groups8 = (max_items + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(groups8 * kXcds * kGroups));
+  const dim3 grid((unsigned)(groups8 * kXcds * kGroups * a.rows.q_len));
   const bool fast = (a.interleave % kTile) == 0 && (a.block_size % kTile) == 0;
   if (fast)
     hipExtLaunchKernelGGL(mla_shard_kernel<true>, grid, dim3(kWaves * 64), 0, stream, ev0, ev1, 0,

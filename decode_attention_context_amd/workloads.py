@@ -10,6 +10,8 @@ GQA per-GPU share shaped like Qwen3-235B, MLA decode shaped like DeepSeek-V3 / K
 ragged batch whose lengths are lognormal around the agentic trace's median of about 67k
 input tokens.  The trace itself is not available; the lognormal lengths stand in for it.
 
+Queries: [batch][Hq][Dk], or [batch][q_len][Hq][Dk] for multi-token decode (q_len > 1:
+the request's last q_len cache tokens are its draft tokens, each verified by one query row).
 Cache layouts:
   GQA  k_pages, v_pages: [num_blocks][Hkv][block_size][D]   (fp32 or bf16)
   MLA  latent_pages:     [num_blocks][block_size][576]      (bf16)
@@ -53,6 +55,7 @@ class Workload:
     seq_len: int = 0          # fixed length for every request (0: use `lengths`)
     lengths: tuple = field(default=())
     ragged: dict = field(default=None)   # lognormal recipe, see ragged_lengths()
+    q_len: int = 1            # query positions per request (multi-token decode when > 1)
 
     def seq_lens(self):
         if self.ragged is not None:
@@ -141,15 +144,14 @@ def make_inputs(w, device="cpu", seed=None):
                seq_lens=torch.from_numpy(lens.astype(np.int32)).to(device),
                num_blocks=num_blocks, max_blocks_per_seq=max_blocks,
                max_seq_len=int(lens.max()) if len(lens) else 0)
+    qshape = (w.batch,) + ((w.q_len,) if w.q_len > 1 else ()) + (w.num_q_heads, w.head_dim_qk)
     if w.kind == "gqa":
-        out["q"] = _fill_normal(torch.empty(w.batch, w.num_q_heads, w.head_dim_qk, dtype=dt,
-                                            device=device), gen)
+        out["q"] = _fill_normal(torch.empty(qshape, dtype=dt, device=device), gen)
         shape = (num_blocks, w.num_kv_heads, bsz, w.head_dim_qk)
         out["k_pages"] = _fill_normal(torch.empty(shape, dtype=dt, device=device), gen)
         out["v_pages"] = _fill_normal(torch.empty(shape, dtype=dt, device=device), gen)
     else:
-        out["q"] = _fill_normal(torch.empty(w.batch, w.num_q_heads, w.head_dim_qk, dtype=dt,
-                                            device=device), gen)
+        out["q"] = _fill_normal(torch.empty(qshape, dtype=dt, device=device), gen)
         out["latent_pages"] = _fill_normal(
             torch.empty(num_blocks, bsz, w.head_dim_qk, dtype=dt, device=device), gen)
     return out

@@ -130,6 +130,39 @@ int dcp_attn_shard_timed(const dcp_attn_desc* desc, const void* q, const void* k
                          float* lse, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
 
+/* Multi-token decode: dcp_attn_shard for q_len query positions per request (speculative
+ * decoding or multi-token prediction verifying draft tokens under DCP; the "Context Parallel
+ * Guide" lists speculative decoding among the features that work with DCP, and the blog's
+ * "Roadmap" section names it).  The request's last q_len cache tokens are its draft tokens:
+ * query position i (0 <= i < q_len) sits at global position seq_len - q_len + i and attends
+ * every position up to and including its own, a causal mask aligned to the end of the
+ * sequence.  On a shard that is the rank's tokens among the first seq_len - q_len + 1 + i
+ * positions; a position with none of them (or a negative position, seq_len < q_len) gets
+ * lse = -inf and O = 0.  Each K / V (latent) row is read from HBM once for all positions.
+ *   q          [batch][q_len][num_q_heads][head_dim_qk] (dtype)
+ *   o_partial  out float32 [batch][q_len][num_q_heads][head_dim_v]
+ *   lse        out float32 [batch][q_len][num_q_heads]
+ *   q_len      host: 1 .. 4; 1 is exactly dcp_attn_shard.  More returns DCP_EUNSUPPORTED.
+ *   workspace  at least dcp_workspace_size_mq() bytes.
+ * Every other argument, the merge of the partials (dcp_merge with num_heads =
+ * q_len * num_q_heads), the errors and the ownership are as for dcp_attn_shard. */
+size_t dcp_workspace_size_mq(const dcp_attn_desc* desc, int q_len, int batch,
+                             int64_t max_seq_len, int cp_size, int interleave);
+int dcp_attn_shard_mq(const dcp_attn_desc* desc, int q_len, const void* q, const void* kv_pages,
+                      const void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                      int batch, int64_t max_seq_len, int rank, int cp_size, int interleave,
+                      float scale, float* o_partial, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+/* dcp_attn_shard_mq with the attention kernel's own start / end stamped into the caller's
+ * events, as dcp_attn_shard_timed. */
+int dcp_attn_shard_mq_timed(const dcp_attn_desc* desc, int q_len, const void* q,
+                            const void* kv_pages, const void* v_pages,
+                            const int32_t* block_table, const int32_t* seq_lens, int batch,
+                            int64_t max_seq_len, int rank, int cp_size, int interleave,
+                            float scale, float* o_partial, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
+                            hipEvent_t ev_end);
+
 /* LSE-weighted merge of cp_size partials into attention over the union of their tokens
  * (blog, "DCP execution flow", step 3: the LSE values reweight the partial results with
  * the online-softmax trick).  With m = max of the finite lse_r:
