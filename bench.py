@@ -301,6 +301,7 @@ def main():
     if not args.no_secondary and kind == dca.GQA:
         line["secondary"] = secondary_mla(dca, wl, torch)
         line["secondary_ragged"] = secondary_ragged(dca, wl, torch)
+        line["secondary_multi_token"] = secondary_multi_token(dca, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)
@@ -392,6 +393,56 @@ def secondary_mla(dca, wl, torch, steps=20):
             "merge8_cached_gbs": round(merge_bytes / (merge_cached_us * 1e-6) / 1e9, 1),
             "merge8_traffic": load_counters("merge_small", "merge.hip", w.name),
             "mla_interleave1_shard_us": mla_i1_us}
+
+
+def shard_kernel_us(dca, torch, w, inp, kind, steps=10):
+    """Median duration of the rank-0 shard kernel (its own start / end stamps)."""
+    kv = inp["k_pages"] if kind == dca.GQA else inp["latent_pages"]
+    v = inp["v_pages"] if kind == dca.GQA else None
+    ws = None
+    ms = []
+    for i in range(steps + 3):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        _, _, ws = dca.shard(inp["q"], kv, v, inp["block_table"], inp["seq_lens"], 0, w.cp_size,
+                             w.interleave, w.scale, kind=kind, max_seq_len=inp["max_seq_len"],
+                             workspace=ws, events=ev)
+        torch.cuda.synchronize()
+        if i >= 3:
+            ms.append(ev[0].elapsed_time(ev[1]))
+    assert dca.read_device_errors(ws) == 0
+    return sorted(ms)[len(ms) // 2] * 1e3
+
+
+def secondary_multi_token(dca, wl, torch):
+    """Multi-token decode (q_len query positions per request, e.g. speculative decoding):
+    the rank-0 shard kernel of the GQA share at q_len 2 and 4 (HBM rate; every K / V row is
+    read once for all positions) and of the MLA decode workload at q_len 2 (MFMA
+    utilisation)."""
+    res = {}
+    for nq in (2, 4):
+        w = wl.GQA_SHARE.with_(q_len=nq)
+        inp = wl.make_inputs(w, device="cuda")
+        us = shard_kernel_us(dca, torch, w, inp, dca.GQA)
+        byts, tok = gqa_launch_bytes(w, w.seq_lens(), 0)
+        byts += (nq - 1) * w.batch * w.num_q_heads * (w.head_dim_qk * 2 + (w.head_dim_v + 1) * 4)
+        flops = tok * 4 * w.num_q_heads * w.head_dim_qk * nq
+        res[f"gqa_share_q{nq}"] = {"shard_us": round(us, 2),
+                                   "hbm_gbs": round(byts / us / 1e3, 1),
+                                   "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4),
+                                   "tflops": round(flops / us / 1e6, 2)}
+        del inp
+    w = wl.MLA_DECODE.with_(q_len=2)
+    inp = wl.make_inputs(w, device="cuda")
+    us = shard_kernel_us(dca, torch, w, inp, dca.MLA)
+    byts, flops, tok = mla_launch_cost(w, w.seq_lens(), 0)
+    flops *= 2
+    res["mla_decode_q2"] = {"shard_us": round(us, 2),
+                            "mfma_util": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "tflops": round(flops / us / 1e6, 1),
+                            "hbm_gbs": round(byts / us / 1e3, 1)}
+    del inp
+    torch.cuda.empty_cache()
+    return res
 
 
 def secondary_ragged(dca, wl, torch, steps=5):

@@ -13,9 +13,12 @@ namespace dcp {
 // shard kernels and the split combine of the same call.
 //   header  int32[64]: [0] device error word, [1] number of work items, [2] tokens per item
 //   off     int32[batch + 1]: first work item of each request (prefix sum)
-//   items   int4[max_items]: (request, local token begin, local token end, 0)
-//   plse    float[max_items * Hq]:      per-item log-sum-exp (natural log)
-//   po      float[max_items * Hq * Dv]: per-item normalized partial output
+//   items   int4[max_items]: (request, local token begin, local token end, partial index),
+//           in dispatch order (longest first); a request's partials have consecutive
+//           indices off[b] .. off[b+1)
+//   plse    float[max_items * rows]:      per-partial log-sum-exp (natural log)
+//   po      float[max_items * rows * Dv]: per-partial normalized output
+// (rows = query rows per request: q_len * Hq)
 // ---------------------------------------------------------------------------------------
 struct WsLayout {
   size_t off_off, items_off, plse_off, po_off, total;

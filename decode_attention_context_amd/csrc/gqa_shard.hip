@@ -134,10 +134,10 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int item = blockIdx.x;
-  if (item >= a.header[1]) return;
-  const int4 it = a.items[item];
+  if ((int)blockIdx.x >= a.header[1]) return;
+  const int4 it = a.items[blockIdx.x];   // in dispatch order, longest first
   const int b = it.x, j0 = it.y, j1 = it.z;
+  const int item = it.w;                 // index of the item's partial
   const int kvh = blockIdx.y;
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   // The wave's query rows (wave-uniform): row rho = w * HPW + h of the R = q_len * G rows

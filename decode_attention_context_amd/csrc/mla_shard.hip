@@ -179,10 +179,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const int ngroups = kGroups * a.q_len;
   const int hgq = (blk / kXcds) % ngroups;
   const int qi = hgq / kGroups, hg = hgq - qi * kGroups;
-  const int item = (blk / (kXcds * ngroups)) * kXcds + blk % kXcds;
-  if (item >= a.header[1]) return;
-  const int4 it = a.items[item];
+  const int slot = (blk / (kXcds * ngroups)) * kXcds + blk % kXcds;
+  if (slot >= a.header[1]) return;
+  const int4 it = a.items[slot];   // in dispatch order, longest first
   const int b = it.x, j0 = it.y;
+  const int item = it.w;           // index of the item's partial
   // query position qi sees a prefix of the shard's tokens
   const int j1 = a.q_len == 1 ? it.z
                               : min(it.z, row_local_end(a.seq_lens, b, a.len_cap, a.q_len, qi,

@@ -7,9 +7,18 @@
 //   2. chunk = the item size: total local tokens / target item count, rounded up to the
 //      kernel's tile and clamped to [min_chunk, the longest request];
 //   3. n_b = ceil(local_b / chunk) items per request; off = exclusive prefix sum;
-//   4. items[off_b + i] = (b, i * chunk, min((i + 1) * chunk, local_b)).
+//   4. item i of request b = (b, i * chunk, min((i + 1) * chunk, local_b), off_b + i), the
+//      last field being the index of its partial output;
+//   5. the items are stored in dispatch order, by descending tile count (a counting sort
+//      over kBuckets buckets, longer items sharing the top bucket): workgroup slot k runs
+//      items[k].
 // Since chunk >= total / target, the item count never exceeds target + batch, which is the
-// bound the host sizes the workspace with.
+// bound the host sizes the workspace with.  A request's partials keep consecutive indices
+// (the split combine reads them together); only the dispatch order changes.  Greedy
+// dispatch of the longest items first keeps a ragged batch's long requests from starting
+// in the last round: for 512 lognormal lengths around 67k tokens on 8 ranks it takes the
+// simulated makespan from 1.54x to 1.04x the even share of one round.  The order within a
+// bucket depends on atomics; no result does (each partial has its fixed index).
 #include "launch.h"
 
 namespace dcp {
@@ -17,6 +26,7 @@ namespace dcp {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kBuckets = 1024;   // tile-count buckets of the dispatch order
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int batch, int rank, int cp, int interleave,
@@ -25,6 +35,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __shared__ long long s_a[kPlanThreads];
   __shared__ long long s_b[kPlanThreads];
   __shared__ int s_err[kPlanThreads];
+  __shared__ int s_hist[kBuckets];   // items per bucket, then next free position per bucket
   const int tid = threadIdx.x;
   const int per = (batch + kPlanThreads - 1) / kPlanThreads;
   const int b0 = min(tid * per, batch);
@@ -83,6 +94,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     __syncthreads();
   }
   long long base = s_a[tid] - cnt;
+  for (int k = tid; k < kBuckets; k += kPlanThreads) s_hist[k] = 0;
+  __syncthreads();
+  // bucket of an item: kBuckets - 1 - (tile count, capped): longest first
+  auto bucket = [&](long long len) -> int {
+    const long long nt = (len + tile - 1) / tile;
+    return kBuckets - 1 - (int)(nt < kBuckets - 1 ? nt : kBuckets - 1);
+  };
   for (int b = b0; b < b1; ++b) {
     int e = 0;
     const long long loc = local_of(b, e);
@@ -91,7 +109,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     for (long long i = 0; i < n; ++i) {
       const long long j0 = i * chunk;
       const long long j1 = j0 + chunk < loc ? j0 + chunk : loc;
-      items[base + i] = make_int4(b, (int)j0, (int)j1, 0);
+      atomicAdd(&s_hist[bucket(j1 - j0)], 1);
+    }
+    base += n;
+  }
+  __syncthreads();
+  // exclusive prefix sum of the bucket counts (Hillis-Steele over kBuckets entries)
+  {
+    const int mine = tid < kBuckets ? s_hist[tid] : 0;
+    for (int s = 1; s < kBuckets; s <<= 1) {
+      const int v = (tid < kBuckets && tid >= s) ? s_hist[tid - s] : 0;
+      __syncthreads();
+      if (tid < kBuckets) s_hist[tid] += v;
+      __syncthreads();
+    }
+    const int incl = tid < kBuckets ? s_hist[tid] : 0;
+    __syncthreads();
+    if (tid < kBuckets) s_hist[tid] = incl - mine;
+    __syncthreads();
+  }
+  base = s_a[tid] - cnt;
+  for (int b = b0; b < b1; ++b) {
+    int e = 0;
+    const long long loc = local_of(b, e);
+    const long long n = (loc + chunk - 1) / chunk;
+    for (long long i = 0; i < n; ++i) {
+      const long long j0 = i * chunk;
+      const long long j1 = j0 + chunk < loc ? j0 + chunk : loc;
+      items[atomicAdd(&s_hist[bucket(j1 - j0)], 1)] =
+          make_int4(b, (int)j0, (int)j1, (int)(base + i));
     }
     base += n;
   }
