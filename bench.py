@@ -469,6 +469,21 @@ def secondary_ragged(dca, wl, torch, steps=5):
     flops = sum(c[1] for c in costs)
     merge_s = sorted(a.elapsed_time(b) for a, b in merge_ev)[len(merge_ev) // 2] / 1e3
     merge_bytes = (C + 1) * w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
+    # the same merge over bf16 partials (what shards called with a bf16 output write): the
+    # float32 partials rounded once, caches flushed before each launch
+    o_parts, l_parts, o, lse = step.bufs
+    o16 = o_parts.to(torch.bfloat16)
+    flush = torch.ones(1 << 28, device="cuda")
+    ms16 = []
+    for _ in range(9):
+        flush.sum()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        dca.merge(o16, l_parts, out=o, lse_out=lse, events=ev)
+        torch.cuda.synchronize()
+        ms16.append(ev[0].elapsed_time(ev[1]))
+    merge16_s = sorted(ms16)[len(ms16) // 2] / 1e3
+    merge16_bytes = w.batch * w.num_q_heads * (C * (w.head_dim_v * 2 + 4) + (w.head_dim_v + 1) * 4)
+    del o16, flush
     graph = capture_step(torch, step)
     graph.replay()
     torch.cuda.synchronize()
@@ -489,6 +504,9 @@ def secondary_ragged(dca, wl, torch, steps=5):
             "merge8_bytes": merge_bytes,
             "merge8_gbs": round(merge_bytes / merge_s / 1e9, 1),
             "merge8_hbm_frac": round(merge_bytes / merge_s / 1e9 / HBM_PEAK_GBS, 4),
+            "merge8_bf16_partials_us": round(merge16_s * 1e6, 2),
+            "merge8_bf16_partials_bytes": merge16_bytes,
+            "merge8_bf16_partials_gbs": round(merge16_bytes / merge16_s / 1e9, 1),
             "step_ms": round(step_s * 1e3, 3),
             "kv_tokens_per_s": round(int(lens.sum()) / step_s, 1)}
 

@@ -66,6 +66,9 @@ _SIGS = {
                             _P, _P, _P, ctypes.c_size_t, _P]),
     "dcp_attn_shard_timed": (_I, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I,
                                   _F, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+    "dcp_attn_shard_ex": (_I, [ctypes.POINTER(Desc), _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I,
+                               _I, _I, _F, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+    "dcp_merge_ex": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "dcp_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "dcp_merge_timed": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "dcp_shard_slots": (_I, [_P, _P, _I, _I, _I, _I64, _I, _I, _I, _P, _P, _P, _P]),
@@ -162,7 +165,7 @@ def alloc_workspace(desc, batch, max_seq_len, cp_size, interleave, device=None, 
 
 def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave, scale, *,
           kind=None, max_seq_len=None, out=None, lse=None, workspace=None, stream=None,
-          events=None):
+          events=None, out_dtype=torch.float32):
     """Partial attention of the gathered queries over rank `rank`'s shard.
 
     GQA: q [b, Hq, D], kv_pages = K pages [nb, Hkv, B, D], v_pages = V pages (same shape).
@@ -170,8 +173,9 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     Multi-token decode: q [b, q_len, Hq, D] (q_len <= 4), query position i of request b at
     global position seq_len - q_len + i, causally masked (dcp_attn_shard_mq).
     block_table int32 [b, max_blocks]; seq_lens int32 [b] (global lengths).
-    Returns (O_r float32 [b, Hq, Dv] or [b, q_len, Hq, Dv], lse_r float32 [b, Hq] or
-    [b, q_len, Hq], workspace).
+    Returns (O_r [b, Hq, Dv] or [b, q_len, Hq, Dv], lse_r float32 [b, Hq] or [b, q_len, Hq],
+    workspace); O_r is float32, or bf16 (rounded to nearest even) with
+    out_dtype=torch.bfloat16 (dcp_attn_shard_ex).
     `events` = (begin, end) torch.cuda.Event pair that takes the attention kernel's own start
     and end time stamps."""
     lib = load()
@@ -201,10 +205,10 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     dv = desc.head_dim_v
     rows = (batch,) + ((q_len,) if q.dim() == 4 else ()) + (desc.num_q_heads,)
     if out is None:
-        out = torch.empty(rows + (dv,), dtype=torch.float32, device=q.device)
+        out = torch.empty(rows + (dv,), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty(rows, dtype=torch.float32, device=q.device)
-    _need(out, "out", dtype=torch.float32)
+    _need(out, "out", dtype=out_dtype)
     _need(lse, "lse", dtype=torch.float32)
     if tuple(out.shape) != rows + (dv,) or tuple(lse.shape) != rows:
         raise ValueError("out / lse have the wrong shape")
@@ -214,7 +218,17 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     args = (_ptr(q), _ptr(kv_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), batch,
             int(max_seq_len), rank, cp_size, interleave, float(scale), _ptr(out), _ptr(lse),
             _ptr(workspace), workspace.numel(), _stream(stream))
-    if events is None:
+    if out_dtype != torch.float32:
+        evs = (ctypes.c_void_p(0), ctypes.c_void_p(0))
+        if events is not None:
+            for ev in events:
+                if not ev.cuda_event:   # torch creates the HIP event on its first record
+                    ev.record(stream)
+            evs = tuple(ctypes.c_void_p(ev.cuda_event) for ev in events)
+        _check("dcp_attn_shard_ex",
+               lib.dcp_attn_shard_ex(ctypes.byref(desc), q_len, _dtype_code(out_dtype), *args,
+                                     *evs))
+    elif events is None:
         if q.dim() == 3:
             _check("dcp_attn_shard", lib.dcp_attn_shard(ctypes.byref(desc), *args))
         else:
@@ -236,12 +250,14 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
 
 def merge(o_partials, lse_partials, *, out_dtype=torch.float32, out=None, lse_out=None,
           want_lse=True, stream=None, events=None):
-    """LSE merge of o_partials [C, b, H, Dv] / lse_partials [C, b, H] -> (O, lse).  Partials
+    """LSE merge of o_partials [C, b, H, Dv] (float32, or bf16 through dcp_merge_ex) /
+    lse_partials [C, b, H] -> (O, lse).  Partials
     of multi-token decode, [C, b, q_len, H, Dv] / [C, b, q_len, H], merge the same way (rows
     b x q_len*H).  `events` = (begin, end) torch.cuda.Event pair that takes the merge
     kernel's own start and end time stamps."""
     lib = load()
-    _need(o_partials, "o_partials", dtype=torch.float32)
+    _need(o_partials, "o_partials")
+    in_dtype = _dtype_code(o_partials.dtype)
     _need(lse_partials, "lse_partials", dtype=torch.float32)
     if o_partials.dim() not in (4, 5) or lse_partials.dim() != o_partials.dim() - 1:
         raise ValueError("o_partials must be [C, b, H, Dv] or [C, b, q_len, H, Dv]")
@@ -259,7 +275,18 @@ def merge(o_partials, lse_partials, *, out_dtype=torch.float32, out=None, lse_ou
         raise ValueError("out has the wrong shape")
     if want_lse and lse_out is None:
         lse_out = torch.empty(rows_shape, dtype=torch.float32, device=o_partials.device)
-    if events is None:
+    if in_dtype != F32:
+        evs = (ctypes.c_void_p(0), ctypes.c_void_p(0))
+        if events is not None:
+            for ev in events:
+                if not ev.cuda_event:
+                    ev.record(stream)
+            evs = tuple(ctypes.c_void_p(ev.cuda_event) for ev in events)
+        _check("dcp_merge_ex",
+               lib.dcp_merge_ex(_ptr(o_partials), in_dtype, _ptr(lse_partials), c, b, h, dv,
+                                _ptr(out), _dtype_code(out_dtype), _ptr(lse_out),
+                                _stream(stream), *evs))
+    elif events is None:
         st = lib.dcp_merge(_ptr(o_partials), _ptr(lse_partials), c, b, h, dv, _ptr(out),
                            _dtype_code(out_dtype), _ptr(lse_out), _stream(stream))
         _check("dcp_merge", st)

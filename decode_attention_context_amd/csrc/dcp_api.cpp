@@ -84,12 +84,14 @@ bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
   return true;
 }
 
-int shard_impl(const dcp_attn_desc* d, int q_len, const void* q, const void* kv,
+int shard_impl(const dcp_attn_desc* d, int q_len, int o_dtype, const void* q, const void* kv,
                const void* v, const int32_t* bt, const int32_t* lens, int batch,
-               int64_t max_seq_len, int rank, int cp, int il, float scale, float* o, float* lse,
+               int64_t max_seq_len, int rank, int cp, int il, float scale, void* o, float* lse,
                void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   int st = check_desc(d, q_len, batch, max_seq_len, cp, il);
   if (st != DCP_OK) return st;
+  if (o_dtype != DCP_F32 && o_dtype != DCP_BF16) return DCP_EINVAL;
+  const int o_bf16 = o_dtype == DCP_BF16;
   if (rank < 0 || rank >= cp || !std::isfinite(scale)) return DCP_EINVAL;
   if (batch == 0) return DCP_OK;
   if (!q || !kv || !bt || !lens || !o || !lse) return DCP_EINVAL;
@@ -108,15 +110,16 @@ int shard_impl(const dcp_attn_desc* d, int q_len, const void* q, const void* kv,
   if (e != hipSuccess) return DCP_ELAUNCH;
   if (d->kind == DCP_GQA) {
     dcp::GqaArgs a{q, kv, v, bt, d->num_q_heads, d->num_kv_heads, d->head_dim_qk, d->block_size,
-                   d->max_blocks_per_seq, d->num_blocks, rank, cp, il, scale, d->dtype, rows};
+                   d->max_blocks_per_seq, d->num_blocks, rank, cp, il, scale, d->dtype, rows,
+                   o_bf16};
     e = dcp::launch_gqa_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   } else {
     dcp::MlaArgs a{q, kv, bt, d->block_size, d->max_blocks_per_seq, d->num_blocks,
-                   rank, cp, il, scale, rows};
+                   rank, cp, il, scale, rows, o_bf16};
     e = dcp::launch_mla_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   }
   if (e != hipSuccess) return DCP_ELAUNCH;
-  e = dcp::launch_split_combine(w, batch, q_len * d->num_q_heads, d->head_dim_v, o, lse,
+  e = dcp::launch_split_combine(w, batch, q_len * d->num_q_heads, d->head_dim_v, o, o_bf16, lse,
                                 stream);
   return e == hipSuccess ? DCP_OK : DCP_ELAUNCH;
 }
@@ -143,9 +146,20 @@ int dcp_attn_shard(const dcp_attn_desc* desc, const void* q, const void* kv_page
                    int batch, int64_t max_seq_len, int rank, int cp_size, int interleave,
                    float scale, float* o_partial, float* lse, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
-  return shard_impl(desc, 1, q, kv_pages, v_pages, block_table, seq_lens, batch, max_seq_len,
-                    rank, cp_size, interleave, scale, o_partial, lse, workspace,
+  return shard_impl(desc, 1, DCP_F32, q, kv_pages, v_pages, block_table, seq_lens, batch,
+                    max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
                     workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dcp_attn_shard_ex(const dcp_attn_desc* desc, int q_len, int o_dtype, const void* q,
+                      const void* kv_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* seq_lens, int batch, int64_t max_seq_len, int rank,
+                      int cp_size, int interleave, float scale, void* o_partial, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t ev_begin, hipEvent_t ev_end) {
+  return shard_impl(desc, q_len, o_dtype, q, kv_pages, v_pages, block_table, seq_lens, batch,
+                    max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
+                    workspace_bytes, stream, ev_begin, ev_end);
 }
 
 int dcp_attn_shard_mq(const dcp_attn_desc* desc, int q_len, const void* q, const void* kv_pages,
@@ -153,7 +167,7 @@ int dcp_attn_shard_mq(const dcp_attn_desc* desc, int q_len, const void* q, const
                       int batch, int64_t max_seq_len, int rank, int cp_size, int interleave,
                       float scale, float* o_partial, float* lse, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  return shard_impl(desc, q_len, q, kv_pages, v_pages, block_table, seq_lens, batch,
+  return shard_impl(desc, q_len, DCP_F32, q, kv_pages, v_pages, block_table, seq_lens, batch,
                     max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
                     workspace_bytes, stream, nullptr, nullptr);
 }
@@ -165,7 +179,7 @@ int dcp_attn_shard_mq_timed(const dcp_attn_desc* desc, int q_len, const void* q,
                             float scale, float* o_partial, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
                             hipEvent_t ev_end) {
-  return shard_impl(desc, q_len, q, kv_pages, v_pages, block_table, seq_lens, batch,
+  return shard_impl(desc, q_len, DCP_F32, q, kv_pages, v_pages, block_table, seq_lens, batch,
                     max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
                     workspace_bytes, stream, ev_begin, ev_end);
 }
@@ -176,24 +190,32 @@ int dcp_attn_shard_timed(const dcp_attn_desc* desc, const void* q, const void* k
                          int cp_size, int interleave, float scale, float* o_partial,
                          float* lse, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  return shard_impl(desc, 1, q, kv_pages, v_pages, block_table, seq_lens, batch, max_seq_len,
-                    rank, cp_size, interleave, scale, o_partial, lse, workspace,
+  return shard_impl(desc, 1, DCP_F32, q, kv_pages, v_pages, block_table, seq_lens, batch,
+                    max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
                     workspace_bytes, stream, ev_begin, ev_end);
+}
+
+int dcp_merge_ex(const void* o_partials, int in_dtype, const float* lse_partials, int cp_size,
+                 int batch, int num_heads, int head_dim_v, void* o_out, int out_dtype,
+                 float* lse_out, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (cp_size < 1 || batch < 0 || num_heads < 1 || head_dim_v < 1) return DCP_EINVAL;
+  if (out_dtype != DCP_F32 && out_dtype != DCP_BF16) return DCP_EINVAL;
+  if (in_dtype != DCP_F32 && in_dtype != DCP_BF16) return DCP_EINVAL;
+  if ((int64_t)batch * num_heads * head_dim_v * cp_size > ((int64_t)1 << 40)) return DCP_EUNSUPPORTED;
+  if (batch == 0) return DCP_OK;
+  if (!o_partials || !lse_partials || !o_out) return DCP_EINVAL;
+  if (!aligned(o_partials, 16) || !aligned(o_out, 16)) return DCP_EINVAL;
+  const hipError_t e = dcp::launch_merge(o_partials, in_dtype == DCP_BF16, lse_partials, cp_size,
+                                         batch, num_heads, head_dim_v, o_out,
+                                         out_dtype == DCP_BF16, lse_out, stream, ev_begin, ev_end);
+  return e == hipSuccess ? DCP_OK : DCP_ELAUNCH;
 }
 
 int dcp_merge_timed(const float* o_partials, const float* lse_partials, int cp_size, int batch,
                     int num_heads, int head_dim_v, void* o_out, int out_dtype, float* lse_out,
                     hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (cp_size < 1 || batch < 0 || num_heads < 1 || head_dim_v < 1) return DCP_EINVAL;
-  if (out_dtype != DCP_F32 && out_dtype != DCP_BF16) return DCP_EINVAL;
-  if ((int64_t)batch * num_heads * head_dim_v * cp_size > ((int64_t)1 << 40)) return DCP_EUNSUPPORTED;
-  if (batch == 0) return DCP_OK;
-  if (!o_partials || !lse_partials || !o_out) return DCP_EINVAL;
-  if (!aligned(o_partials, 16) || !aligned(o_out, 16)) return DCP_EINVAL;
-  const hipError_t e = dcp::launch_merge(o_partials, lse_partials, cp_size, batch, num_heads,
-                                         head_dim_v, o_out, out_dtype == DCP_BF16, lse_out, stream,
-                                         ev_begin, ev_end);
-  return e == hipSuccess ? DCP_OK : DCP_ELAUNCH;
+  return dcp_merge_ex(o_partials, DCP_F32, lse_partials, cp_size, batch, num_heads, head_dim_v,
+                      o_out, out_dtype, lse_out, stream, ev_begin, ev_end);
 }
 
 int dcp_merge(const float* o_partials, const float* lse_partials, int cp_size, int batch,

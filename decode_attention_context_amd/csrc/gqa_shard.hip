@@ -87,7 +87,8 @@ struct GqaKArgs {
   const int32_t* seq_lens;
   int64_t len_cap;
   int q_len;
-  float* o_out;
+  int o_bf16;    // O written in bf16 (requests with a single item; others via the combine)
+  void* o_out;
   float* lse_out;
   int32_t* header;
   const int32_t* off;
@@ -464,13 +465,20 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
     const float lse = lt > 0.f ? (m[h] + __log2f(lt)) * kLn2 : neg_inf();
     if (!live[h]) continue;   // a repeated row (uniform)
     const int row = rrow[h];
-    float* dst = single ? a.o_out + ((size_t)b * RQ + row) * D
+    float* dst = single ? static_cast<float*>(a.o_out) + ((size_t)b * RQ + row) * D
                         : a.po + ((size_t)item * RQ + row) * D;
+    uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + ((size_t)b * RQ + row) * D;
+    const bool bf16_out = single && a.o_bf16;   // uniform
     if constexpr (kBf16) {
       // lane (g, i16): dims 32 g + i16 and 32 g + 16 + i16
       const int d0 = 32 * (lane >> 4) + (lane & 15);
-      dst[d0] = acc[h][0] * inv;
-      dst[d0 + 16] = acc[h][1] * inv;
+      if (bf16_out) {
+        dstb[d0] = (uint16_t)f32_to_bf16_rne(acc[h][0] * inv);
+        dstb[d0 + 16] = (uint16_t)f32_to_bf16_rne(acc[h][1] * inv);
+      } else {
+        dst[d0] = acc[h][0] * inv;
+        dst[d0 + 16] = acc[h][1] * inv;
+      }
     } else {
       // the four token groups of each row chunk are summed across the 16-lane rows
       float o[NA];
@@ -484,8 +492,14 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
                                                            false, false);
         o[k] = (__uint_as_float(r32[0]) + __uint_as_float(r32[1])) * inv;
       }
-      if (pr == 0)
-        *reinterpret_cast<float4*>(dst + 4 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
+      if (pr == 0) {
+        if (bf16_out)
+          *reinterpret_cast<uint2*>(dstb + 4 * pcl) =
+              make_uint2(f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16),
+                         f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16));
+        else
+          *reinterpret_cast<float4*>(dst + 4 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
+      }
     }
     if (lane == 0) {
       if (single) a.lse_out[(size_t)b * RQ + row] = lse;
@@ -531,7 +545,7 @@ bool gqa_supported(int dtype, int head_dim, int group, int q_len) {
 }
 
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream, hipEvent_t ev0,
+                            void* o_out, float* lse_out, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1) {
   GqaKArgs k;
   k.q = a.q;
@@ -550,6 +564,7 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
   k.seq_lens = a.rows.seq_lens;
   k.len_cap = a.rows.len_cap;
   k.q_len = a.rows.q_len;
+  k.o_bf16 = a.o_bf16;
   k.o_out = o_out;
   k.lse_out = lse_out;
   k.header = ws.header;

@@ -17,13 +17,15 @@ hipError_t launch_plan(const int32_t* seq_lens, int batch, int rank, int cp, int
 
 // LSE merge of `n` partials per row (rows = batch * heads); ev0 / ev1 (nullable) take the
 // merge kernel's own start and end time stamps.
-hipError_t launch_merge(const float* o_partials, const float* lse_partials, int n, int batch,
-                        int heads, int dv, void* o_out, int out_bf16, float* lse_out,
+// Partials are float32, or bf16 when in_bf16.
+hipError_t launch_merge(const void* o_partials, int in_bf16, const float* lse_partials, int n,
+                        int batch, int heads, int dv, void* o_out, int out_bf16, float* lse_out,
                         hipStream_t stream, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
-// Combine of the split partials of each request into the shard output.
-hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, float* o_out,
-                                float* lse_out, hipStream_t stream);
+// Combine of the split partials of each request into the shard output (float32, or bf16
+// rounded to nearest even when out_bf16).
+hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, void* o_out,
+                                int out_bf16, float* lse_out, hipStream_t stream);
 
 // Query rows of a request: q_len positions x the query heads.  Row i of a multi-token
 // request sits at position seq_len - q_len + i and sees the positions up to its own, so it
@@ -46,10 +48,11 @@ struct GqaArgs {
   float scale;
   int dtype;  // 0 f32, 1 bf16
   RowArgs rows;
+  int o_bf16;  // partial output O in bf16 (round to nearest even) instead of float32
 };
 // ev0 / ev1 (nullable): events stamped with the attention kernel's own start and end.
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream,
+                            void* o_out, float* lse_out, hipStream_t stream,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 bool gqa_supported(int dtype, int head_dim, int group, int q_len);
 
@@ -62,9 +65,10 @@ struct MlaArgs {
   int rank, cp, interleave;
   float scale;
   RowArgs rows;
+  int o_bf16;  // partial output O in bf16 (round to nearest even) instead of float32
 };
 hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream,
+                            void* o_out, float* lse_out, hipStream_t stream,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_shard_slots(const int32_t* block_table, const int32_t* seq_lens, int batch,

@@ -42,6 +42,35 @@ __device__ __forceinline__ void st(float* p, T v) {
   *reinterpret_cast<T*>(p) = v;
 }
 
+// VEC consecutive elements of a partial row as floats: float32 partials are loaded as they
+// are, bf16 partials (2 bytes per element) are loaded at half the width and widened exactly.
+template <int VEC, bool kBf16In>
+__device__ __forceinline__ typename VecT<VEC>::T ldp(const void* base, int64_t elem) {
+  using V = typename VecT<VEC>::T;
+  if constexpr (!kBf16In) {
+    return ld<V>(static_cast<const float*>(base) + elem);
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + elem;
+    V v;
+    float* pv = reinterpret_cast<float*>(&v);
+    if constexpr (VEC == 4) {
+      typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+      const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      pv[0] = __uint_as_float(u.x << 16);
+      pv[1] = __uint_as_float(u.x & 0xffff0000u);
+      pv[2] = __uint_as_float(u.y << 16);
+      pv[3] = __uint_as_float(u.y & 0xffff0000u);
+    } else if constexpr (VEC == 2) {
+      const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+      pv[0] = __uint_as_float(u << 16);
+      pv[1] = __uint_as_float(u & 0xffff0000u);
+    } else {
+      pv[0] = __uint_as_float((uint32_t)__builtin_nontemporal_load(p) << 16);
+    }
+    return v;
+  }
+}
+
 template <int VEC>
 __device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename VecT<VEC>::T& v) {
   const float* p = reinterpret_cast<const float*>(&v);
@@ -52,8 +81,8 @@ __device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename 
 // Merge `n` partial rows o_base[r * o_stride .. + dv) with lse l_base[r * l_stride].
 // The lse values are spread over the lanes (64 per pass) and reduced with DPP, so the row
 // costs one round trip for them; the partial rows are then streamed 8 at a time.
-template <int VEC>
-__device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int64_t o_stride,
+template <int VEC, bool kBf16In = false>
+__device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64_t o_stride,
                                           const float* __restrict__ l_base, int64_t l_stride,
                                           int n, int dv, float* __restrict__ out_f32,
                                           uint16_t* __restrict__ out_bf16,
@@ -102,7 +131,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
         for (int u = 0; u < 8; ++u) {
           wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r + u));
           if (wv[u] != 0.f)
-            v[u] = ld<V>(o_base + (int64_t)(r0 + r + u) * o_stride + d);
+            v[u] = ldp<VEC, kBf16In>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -111,7 +140,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
       for (; r < nr; ++r) {
         const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r));
         if (wr != 0.f)
-          vfma<VEC>(acc, wr, ld<V>(o_base + (int64_t)(r0 + r) * o_stride + d));
+          vfma<VEC>(acc, wr, ldp<VEC, kBf16In>(o_base, (int64_t)(r0 + r) * o_stride + d));
       }
     }
     if (out_f32) {
@@ -133,8 +162,8 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ o_base, int6
 // accumulates in place in the registers of the first partial, so that the loads in flight
 // (up to 64 registers) leave room for the most waves per SIMD.  When every partial is empty
 // all weights are 0 and the row comes out as O = 0, lse = -inf.
-template <int VEC, bool kBf16Out>
-__device__ __forceinline__ void merge_row_small(const float* __restrict__ o_base,
+template <int VEC, bool kBf16Out, bool kBf16In = false>
+__device__ __forceinline__ void merge_row_small(const void* __restrict__ o_base,
                                                 int64_t o_stride,
                                                 const float* __restrict__ l_base,
                                                 int64_t l_stride, int n, int dv,
@@ -150,7 +179,7 @@ __device__ __forceinline__ void merge_row_small(const float* __restrict__ o_base
 #pragma unroll
     for (int c = 0; c < kMaxC; ++c)
       if (r < n && c < nc)
-        v[r][c] = ld<V>(o_base + (int64_t)r * o_stride + (c * 64 + lane) * VEC);
+        v[r][c] = ldp<VEC, kBf16In>(o_base, (int64_t)r * o_stride + (c * 64 + lane) * VEC);
   x = __builtin_isfinite(x) ? x : neg_inf();
   const float m2 = lanes8_max(x) * kLog2e;   // -inf when every partial is empty
   const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
@@ -208,9 +237,9 @@ __host__ __device__ __forceinline__ bool merge_small_ok(int n, int dv, int vec) 
 constexpr int kRowsPerBlock = 4;
 
 // dcp_merge with at most 8 partials: one row per wave, all loads up front
-template <int VEC, bool kBf16Out>
+template <int VEC, bool kBf16Out, bool kBf16In>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void merge_small_kernel(
-    const float* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
+    const void* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
     int batch, int heads, int dv, void* __restrict__ out, float* __restrict__ lse_out) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rows = (int64_t)batch * heads;
@@ -218,45 +247,51 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void merge_small_kernel(
   const int lane = threadIdx.x & 63;
   void* o = kBf16Out ? (void*)(static_cast<uint16_t*>(out) + row * dv)
                      : (void*)(static_cast<float*>(out) + row * dv);
-  merge_row_small<VEC, kBf16Out>(o_partials + row * dv, rows * dv, lse_partials + row, rows, n,
-                                 dv, o, lse_out ? lse_out + row : nullptr, lane);
+  const void* ob = kBf16In ? (const void*)(static_cast<const uint16_t*>(o_partials) + row * dv)
+                           : (const void*)(static_cast<const float*>(o_partials) + row * dv);
+  merge_row_small<VEC, kBf16Out, kBf16In>(ob, rows * dv, lse_partials + row, rows, n, dv, o,
+                                          lse_out ? lse_out + row : nullptr, lane);
 }
 
-template <int VEC>
+template <int VEC, bool kBf16In>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void merge_kernel(
-    const float* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
+    const void* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
     int batch, int heads, int dv, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
     float* __restrict__ lse_out) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rows = (int64_t)batch * heads;
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  merge_row<VEC>(o_partials + row * dv, rows * dv, lse_partials + row, rows, n, dv,
-                 out_f32 ? out_f32 + row * dv : nullptr, out_bf16 ? out_bf16 + row * dv : nullptr,
-                 lse_out ? lse_out + row : nullptr, lane);
+  const void* ob = kBf16In ? (const void*)(static_cast<const uint16_t*>(o_partials) + row * dv)
+                           : (const void*)(static_cast<const float*>(o_partials) + row * dv);
+  merge_row<VEC, kBf16In>(ob, rows * dv, lse_partials + row, rows, n, dv,
+                          out_f32 ? out_f32 + row * dv : nullptr,
+                          out_bf16 ? out_bf16 + row * dv : nullptr,
+                          lse_out ? lse_out + row : nullptr, lane);
 }
 
 // Split combine: request b's items [off[b], off[b+1]) hold partials of every head.  A
 // request with a single item was written directly by the shard kernel; a request with no
 // item (empty shard) gets O = 0, lse = -inf.
-template <int VEC>
+template <int VEC, bool kBf16Out>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
     const int32_t* __restrict__ off, const float* __restrict__ plse, const float* __restrict__ po,
-    int batch, int hq, int dv, float* __restrict__ o_out, float* __restrict__ lse_out) {
+    int batch, int hq, int dv, void* __restrict__ o_out, float* __restrict__ lse_out) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= (int64_t)batch * hq) return;
   const int b = (int)(row / hq), h = (int)(row - (int64_t)b * hq);
   const int i0 = off[b], n = off[b + 1] - i0;
   if (n == 1) return;
   const int lane = threadIdx.x & 63;
+  float* of = kBf16Out ? nullptr : static_cast<float*>(o_out) + row * dv;
+  uint16_t* obf = kBf16Out ? static_cast<uint16_t*>(o_out) + row * dv : nullptr;
   if (merge_small_ok(n, dv, VEC))
-    merge_row_small<VEC, false>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv,
-                                plse + (int64_t)i0 * hq + h, hq, n, dv, o_out + row * dv,
-                                lse_out + row, lane);
+    merge_row_small<VEC, kBf16Out>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv,
+                                   plse + (int64_t)i0 * hq + h, hq, n, dv,
+                                   kBf16Out ? (void*)obf : (void*)of, lse_out + row, lane);
   else
     merge_row<VEC>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv,
-                   plse + (int64_t)i0 * hq + h, hq, n, dv, o_out + row * dv, nullptr,
-                   lse_out + row, lane);
+                   plse + (int64_t)i0 * hq + h, hq, n, dv, of, obf, lse_out + row, lane);
 }
 
 int pick_vec(int dv) {
@@ -267,64 +302,65 @@ int pick_vec(int dv) {
 
 }  // namespace
 
-hipError_t launch_merge(const float* o_partials, const float* lse_partials, int n, int batch,
-                        int heads, int dv, void* o_out, int out_bf16, float* lse_out,
+hipError_t launch_merge(const void* o_partials, int in_bf16, const float* lse_partials, int n,
+                        int batch, int heads, int dv, void* o_out, int out_bf16, float* lse_out,
                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t rows = (int64_t)batch * heads;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const dim3 block(64 * kRowsPerBlock);
   float* of = out_bf16 ? nullptr : static_cast<float*>(o_out);
   uint16_t* ob = out_bf16 ? static_cast<uint16_t*>(o_out) : nullptr;
-  if (merge_small_ok(n, dv, pick_vec(dv))) {
-#define DCP_MERGE_SMALL(V, B)                                                                  \
-  hipExtLaunchKernelGGL((merge_small_kernel<V, B>), grid, block, 0, stream, ev0, ev1, 0,      \
+  const int vec = pick_vec(dv);
+  if (merge_small_ok(n, dv, vec)) {
+#define DCP_MERGE_SMALL(V, B, I)                                                               \
+  hipExtLaunchKernelGGL((merge_small_kernel<V, B, I>), grid, block, 0, stream, ev0, ev1, 0,   \
                         o_partials, lse_partials, n, batch, heads, dv, o_out, lse_out)
-    const int vec = pick_vec(dv);
+#define DCP_MERGE_SMALL_V(B, I)            \
+  if (vec == 4) DCP_MERGE_SMALL(4, B, I);  \
+  else if (vec == 2) DCP_MERGE_SMALL(2, B, I); \
+  else DCP_MERGE_SMALL(1, B, I)
     if (out_bf16) {
-      if (vec == 4) DCP_MERGE_SMALL(4, true);
-      else if (vec == 2) DCP_MERGE_SMALL(2, true);
-      else DCP_MERGE_SMALL(1, true);
+      if (in_bf16) { DCP_MERGE_SMALL_V(true, true); } else { DCP_MERGE_SMALL_V(true, false); }
     } else {
-      if (vec == 4) DCP_MERGE_SMALL(4, false);
-      else if (vec == 2) DCP_MERGE_SMALL(2, false);
-      else DCP_MERGE_SMALL(1, false);
+      if (in_bf16) { DCP_MERGE_SMALL_V(false, true); } else { DCP_MERGE_SMALL_V(false, false); }
     }
+#undef DCP_MERGE_SMALL_V
 #undef DCP_MERGE_SMALL
     return hipGetLastError();
   }
-  switch (pick_vec(dv)) {
-    case 4:
-      hipExtLaunchKernelGGL(merge_kernel<4>, grid, block, 0, stream, ev0, ev1, 0, o_partials,
-                         lse_partials, n, batch, heads, dv, of, ob, lse_out);
-      break;
-    case 2:
-      hipExtLaunchKernelGGL(merge_kernel<2>, grid, block, 0, stream, ev0, ev1, 0, o_partials,
-                         lse_partials, n, batch, heads, dv, of, ob, lse_out);
-      break;
-    default:
-      hipExtLaunchKernelGGL(merge_kernel<1>, grid, block, 0, stream, ev0, ev1, 0, o_partials,
-                            lse_partials, n, batch, heads, dv, of, ob, lse_out);
+#define DCP_MERGE(V, I)                                                                         \
+  hipExtLaunchKernelGGL((merge_kernel<V, I>), grid, block, 0, stream, ev0, ev1, 0, o_partials, \
+                        lse_partials, n, batch, heads, dv, of, ob, lse_out)
+  if (in_bf16) {
+    if (vec == 4) DCP_MERGE(4, true);
+    else if (vec == 2) DCP_MERGE(2, true);
+    else DCP_MERGE(1, true);
+  } else {
+    if (vec == 4) DCP_MERGE(4, false);
+    else if (vec == 2) DCP_MERGE(2, false);
+    else DCP_MERGE(1, false);
   }
+#undef DCP_MERGE
   return hipGetLastError();
 }
 
-hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, float* o_out,
-                                float* lse_out, hipStream_t stream) {
+hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, void* o_out,
+                                int out_bf16, float* lse_out, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * hq;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  switch (pick_vec(dv)) {
-    case 4:
-      hipLaunchKernelGGL(split_combine_kernel<4>, grid, dim3(64 * kRowsPerBlock), 0, stream,
-                         ws.off, ws.plse, ws.po, batch, hq, dv, o_out, lse_out);
-      break;
-    case 2:
-      hipLaunchKernelGGL(split_combine_kernel<2>, grid, dim3(64 * kRowsPerBlock), 0, stream,
-                         ws.off, ws.plse, ws.po, batch, hq, dv, o_out, lse_out);
-      break;
-    default:
-      hipLaunchKernelGGL(split_combine_kernel<1>, grid, dim3(64 * kRowsPerBlock), 0, stream,
-                         ws.off, ws.plse, ws.po, batch, hq, dv, o_out, lse_out);
+  const dim3 block(64 * kRowsPerBlock);
+#define DCP_COMBINE(V, B)                                                                  \
+  hipLaunchKernelGGL((split_combine_kernel<V, B>), grid, block, 0, stream, ws.off, ws.plse, \
+                     ws.po, batch, hq, dv, o_out, lse_out)
+  switch (pick_vec(dv) * 2 + (out_bf16 ? 1 : 0)) {
+    case 8: DCP_COMBINE(4, false); break;
+    case 9: DCP_COMBINE(4, true); break;
+    case 4: DCP_COMBINE(2, false); break;
+    case 5: DCP_COMBINE(2, true); break;
+    case 2: DCP_COMBINE(1, false); break;
+    default: DCP_COMBINE(1, true);
   }
+#undef DCP_COMBINE
   return hipGetLastError();
 }
 

@@ -109,7 +109,8 @@ struct MlaKArgs {
   const int32_t* seq_lens;
   int64_t len_cap;
   int q_len;
-  float* o_out;
+  int o_bf16;    // O written in bf16 (requests with a single item; others via the combine)
+  void* o_out;
   float* lse_out;
   int32_t* header;
   const int32_t* off;
@@ -646,13 +647,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int head = head_p + 16 * hh;
-      float* dst = (single ? a.o_out + (orow + head) * kDv : a.po + (prow + head) * kDv) +
+      float* dst = (single ? static_cast<float*>(a.o_out) + (orow + head) * kDv
+                           : a.po + (prow + head) * kDv) +
                    dq * 128;
+      uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + (orow + head) * kDv + dq * 128;
       const float inv = hh ? inv1 : inv0;
+      if (single && a.o_bf16) {   // uniform
 #pragma unroll
-      for (int dt = 0; dt < kQuarterTiles; ++dt) {
-        const f4 v = acc[hh][dt] * inv;
-        *reinterpret_cast<f4*>(dst + 16 * dt + 4 * g) = v;
+        for (int dt = 0; dt < kQuarterTiles; ++dt) {
+          const f4 v = acc[hh][dt] * inv;
+          *reinterpret_cast<uint2*>(dstb + 16 * dt + 4 * g) =
+              make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                         f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < kQuarterTiles; ++dt) {
+          const f4 v = acc[hh][dt] * inv;
+          *reinterpret_cast<f4*>(dst + 16 * dt + 4 * g) = v;
+        }
       }
     }
   }
@@ -661,7 +674,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 }  // namespace
 
 hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& ws,
-                            float* o_out, float* lse_out, hipStream_t stream, hipEvent_t ev0,
+                            void* o_out, float* lse_out, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1) {
   MlaKArgs k;
   k.q = static_cast<const uint16_t*>(a.q);
@@ -677,6 +690,7 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   k.seq_lens = a.rows.seq_lens;
   k.len_cap = a.rows.len_cap;
   k.q_len = a.rows.q_len;
+  k.o_bf16 = a.o_bf16;
   k.o_out = o_out;
   k.lse_out = lse_out;
   k.header = ws.header;

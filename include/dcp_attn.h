@@ -163,6 +163,25 @@ int dcp_attn_shard_mq_timed(const dcp_attn_desc* desc, int q_len, const void* q,
                             size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
                             hipEvent_t ev_end);
 
+/* The general shard call: q_len query positions per request as in dcp_attn_shard_mq, the
+ * partial output O in o_dtype, and optional timing events as in dcp_attn_shard_timed.
+ *   o_dtype    DCP_F32: o_partial is float32 (as in dcp_attn_shard);
+ *              DCP_BF16: o_partial is bf16 [batch][q_len][num_q_heads][head_dim_v], each
+ *              value the float32 result rounded to nearest even.  The partials every rank
+ *              exchanges and the merge reads then take half the bytes (the blog's "DCP
+ *              execution flow" exchanges partial outputs with their LSE; the LSE stays
+ *              float32).  Split partials inside the workspace stay float32.
+ *   ev_begin, ev_end   nullable; as in dcp_attn_shard_timed.
+ * Every other argument, the workspace (dcp_workspace_size_mq) and the errors are as for
+ * dcp_attn_shard_mq; dcp_attn_shard, _timed, _mq and _mq_timed are this call with
+ * o_dtype = DCP_F32. */
+int dcp_attn_shard_ex(const dcp_attn_desc* desc, int q_len, int o_dtype, const void* q,
+                      const void* kv_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* seq_lens, int batch, int64_t max_seq_len, int rank,
+                      int cp_size, int interleave, float scale, void* o_partial, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t ev_begin, hipEvent_t ev_end);
+
 /* LSE-weighted merge of cp_size partials into attention over the union of their tokens
  * (blog, "DCP execution flow", step 3: the LSE values reweight the partial results with
  * the online-softmax trick).  With m = max of the finite lse_r:
@@ -186,6 +205,14 @@ int dcp_merge(const float* o_partials, const float* lse_partials, int cp_size, i
 int dcp_merge_timed(const float* o_partials, const float* lse_partials, int cp_size, int batch,
                     int num_heads, int head_dim_v, void* o_out, int out_dtype, float* lse_out,
                     hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+
+/* The general merge: dcp_merge with the partials o_partials in in_dtype (DCP_F32: float32;
+ * DCP_BF16: bf16, e.g. as written by dcp_attn_shard_ex, widened exactly to float32 before
+ * the float32 arithmetic) and optional timing events as in dcp_merge_timed (nullable).
+ * dcp_merge and dcp_merge_timed are this call with in_dtype = DCP_F32. */
+int dcp_merge_ex(const void* o_partials, int in_dtype, const float* lse_partials, int cp_size,
+                 int batch, int num_heads, int head_dim_v, void* o_out, int out_dtype,
+                 float* lse_out, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
 
 /* Physical slots (page * block_size + t % block_size, int64) of the tokens a rank stores,
  * in ascending global position t: the library's block-table walk made visible.
