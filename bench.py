@@ -259,7 +259,7 @@ def main():
         traffic = load_counters("gqa_shard", "gqa_shard.hip", w.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "gqa_shard_kernel<bf16,G=8>",
+                "traffic": traffic, "kernel": "gqa_shard_kernel<bf16,NW=4,mfma>",
                 "algorithmic_bytes_per_launch": int(bytes_avg),
                 "avg_launch_us": round(dur_s * 1e6, 2)}
         kernel_name = "gqa_shard"

@@ -23,6 +23,7 @@ CASES = [
     wl.TINY_GQA.with_(name="bf16o_gqa_f32in_i3", batch=3, num_q_heads=4, num_kv_heads=2,
                       block_size=8, cp_size=2, interleave=3, lengths=(1, 10, 333), seed=72),
     wl.MLA_DECODE.with_(name="bf16o_mla_c8", batch=3, lengths=(1, 130, 30000), seed=73),
+    wl.GQA_SHARE.with_(name="bf16o_gqa_q4", batch=3, q_len=4, lengths=(2, 900, 20000), seed=75),
     wl.MLA_DECODE.with_(name="bf16o_mla_q2_i1", batch=2, q_len=2, cp_size=4, interleave=1,
                         lengths=(3, 2100), seed=74),
 ]

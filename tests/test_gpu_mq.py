@@ -4,7 +4,8 @@ the request's draft tokens) against the CPU oracle (GPU).
 Every case runs all ranks' shards through dcp_attn_shard_mq, merges them with dcp_merge
 and compares every rank's partial and the merged output of the checked requests with the
 oracle, elementwise (tolerances in parity_helpers).  The cases cover every q_len, GQA rows
-per KV head from 2 to 64 (the kernel's whole range of rows per wave), both dtypes, both
+per KV head from 2 to 64 (the vector kernel's whole range of rows per wave; bf16 with 8 to
+32 rows runs on the matrix cores), both dtypes, both
 MLA tile paths (page-contiguous and token-granular), requests shorter than q_len (query
 positions before the sequence start: empty rows), positions whose visible tokens end
 inside or before an item, and the full-size GQA share and MLA decode shapes.
@@ -51,6 +52,15 @@ MQ_GQA = [
     # G = 4, q_len 3: 12 rows (repeated rows past the end of the wave grid)
     G.with_(name="mq_gqa_g4_q3_c3", batch=3, q_len=3, num_q_heads=8, num_kv_heads=2,
             block_size=16, cp_size=3, interleave=16, lengths=(4, 65, 1000), seed=55),
+    # matrix-core rows: G = 16, q_len 2 (32 rows, position = row / 16); two KV heads of
+    # G = 4 at q_len 4 (16 rows) on page-contiguous tiles
+    G.with_(name="mq_gqa_g16_q2", batch=2, q_len=2, num_q_heads=16, lengths=(5, 2600),
+            seed=59),
+    G.with_(name="mq_gqa_g4_q4_h2", batch=3, q_len=4, num_q_heads=8, num_kv_heads=2,
+            block_size=64, interleave=64, lengths=(4, 130, 5000), seed=60),
+    # G = 2, q_len 4: 8 rows on the matrix cores, position = row / 2
+    G.with_(name="mq_gqa_g2_q4", batch=2, q_len=4, num_q_heads=4, num_kv_heads=2,
+            lengths=(3, 1700), seed=50),
     # G = 1, q_len 3: 3 rows on 4 waves
     G.with_(name="mq_gqa_g1_q3", batch=2, q_len=3, num_q_heads=2, num_kv_heads=2,
             block_size=64, cp_size=1, interleave=64, lengths=(700, 66), seed=56),
