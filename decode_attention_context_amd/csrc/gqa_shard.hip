@@ -127,9 +127,9 @@ __device__ __forceinline__ int v_swz_t(int r) {
 constexpr int waves_for(int r) { return r >= 8 ? 8 : (r > 4 ? 8 : (r > 2 ? 4 : r)); }
 constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r); }
 
-// kMfma: the matrix-core variant for 8 <= R <= 32 query rows per KV head, bf16 only, NW = 4 * (16-row tiles); HPW is unused.  Wave w = (16-row tile rt = w / 4,
-// token quarter tq = w % 4 of every tile) keeps its own online softmax over its 16 tokens
-// of each tile:
+// kMfma: the matrix-core variant for 8 <= R <= 32 query rows per KV head, bf16 only: four
+// waves, HPW = 16-row tiles per wave (rows past R are padding).  Wave w takes token quarter
+// w of every tile for all rows and keeps its own online softmax over those tokens:
 //   * S^T (16 tokens x 16 rows) = K (16 x 128) . Q^T on v_mfma_f32_16x16x32_bf16, the K
 //     operand (lane = token, 8 dims) read straight from the 4-row K blocks and the query
 //     operand resident in registers for the whole item.  Lane (group g, i16) gets row i16,
@@ -138,14 +138,15 @@ constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r
 //     v_mfma_f32_16x16x16_bf16 (tokens 4 g .. 4 g + 3 of column i16), so
 //     O^T (128 dims x 16 rows) += V^T (128 x 16 tokens) . P^T needs no LDS round trip; the
 //     V^T operand (one dim of 4 consecutive tokens) is one ds_read_b64_tr_b16 per 16 dims;
+//   * every K and V^T operand read feeds one MFMA per row tile;
 //   * a row's maximum over the tile is the max of a lane's four scores combined across the
 //     four 16-lane groups (permlane swaps); rows sit in lanes, so the lazy rescale is per
 //     lane under a wave-uniform branch;
-//   * after the last tile the four token quarters of each row tile merge through LDS by
-//     the LSE identity (weights exp2(m_k - max m), empty quarters weight 0).
+//   * after the last tile the four token quarters of each row merge through LDS by the LSE
+//     identity (weights exp2(m_k - max m), empty quarters weight 0).
 template <bool kBf16, int NW, int HPW, bool kMfma = false>
 __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
-  static_assert(!kMfma || (kBf16 && NW % 4 == 0), "matrix-core variant: bf16, 4 waves per row tile");
+  static_assert(!kMfma || (kBf16 && NW == 4), "matrix-core variant: bf16, four waves");
   constexpr int kElemBytes = kBf16 ? 2 : 4;
   constexpr int D = kRowBytes / kElemBytes;     // head dim
   constexpr int NA = kBf16 ? 2 : 4;             // dims (accumulators) per lane per head
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
   // [buffer][K blocks | V rows]
   __shared__ u32x4 kvs[kNBuf * kBufBytes / 16];
   __shared__ uint32_t pbuf[kMfma ? 1 : NW][HPW][kMfma ? 1 : kPWords];
-  __shared__ float mls[kMfma ? NW * 16 * 2 : 1];   // matrix-core variant: (m, l) per wave row
+  __shared__ float mls[kMfma ? NW * 16 * HPW * 2 : 1];   // matrix-core variant: (m, l) per row
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -318,35 +319,46 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
   };
 
   if constexpr (kMfma) {
+    constexpr int RT = HPW;   // 16-row tiles per wave
     const int g = lane >> 4, i16 = lane & 15;
-    const int rt = w >> 2, tq = w & 3;
-    // this lane's query row (rows past R repeat row R - 1 and are not written) and the local
-    // end of the tokens it sees; lim_lo, the smallest such end in the workgroup (position 0),
-    // decides when a tile needs masking
-    const int rho = min(16 * rt + i16, R - 1);
-    const int qi = rho / G;
-    const int qrow = qi * a.hq + kvh * G + (rho - qi * G);
-    const int lim_l = a.q_len == 1 ? j1
-                                   : min(j1, row_local_end(a.seq_lens, b, a.len_cap, a.q_len,
-                                                           qi, a.rank, a.cp, a.interleave));
+    const int tq = w;         // token quarter of every tile
+    // this lane's query row in each row tile (rows past R repeat row R - 1 and are not
+    // written) and the local end of the tokens it sees; lim_lo, the smallest such end in
+    // the workgroup (position 0), decides when a tile needs masking
+    int lim_l[RT];
+    bf16x8 qop[RT][4];   // query operand of the 4 k-steps: dims 32 ks + 8 g .. + 7
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int rho = min(16 * r + i16, R - 1);
+      const int qi = rho / G;
+      const int qrow = qi * a.hq + kvh * G + (rho - qi * G);
+      lim_l[r] = a.q_len == 1 ? j1
+                              : min(j1, row_local_end(a.seq_lens, b, a.len_cap, a.q_len, qi,
+                                                      a.rank, a.cp, a.interleave));
+      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                                       ((size_t)b * RQ + qrow) * D) + g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qop[r][ks] = __builtin_bit_cast(bf16x8, qp[4 * ks]);
+    }
     const int lim_lo = a.q_len == 1 ? j1
                                     : min(j1, row_local_end(a.seq_lens, b, a.len_cap, a.q_len,
                                                             0, a.rank, a.cp, a.interleave));
-    // query operand of the 4 k-steps: dims 32 ks + 8 g .. + 7 of row qrow
-    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                                     ((size_t)b * RQ + qrow) * D) + g;
-    bf16x8 qop[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qop[ks] = __builtin_bit_cast(bf16x8, qp[4 * ks]);
 
-    float m = neg_inf(), negm = 0.f, ls = 0.f;
-    f4 acc[D / 16];
+    float m[RT], negm[RT], ls[RT];
+    f4 acc[RT][D / 16];
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) acc[db] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RT; ++r) {
+      m[r] = neg_inf();
+      negm[r] = 0.f;
+      ls[r] = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) acc[r][db] = f4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // K operand: tile row 16 tq + i16, chunk 4 ks + g of the 4-row blocks; V^T operand: this
     // lane addresses tile row 16 tq + 4 g + i16 / 4, bytes 8 (i16 mod 4) of the swizzled
-    // 32-byte slot of dims 16 db .. 16 db + 15
+    // 32-byte slot of dims 16 db .. 16 db + 15.  Every operand read feeds one MFMA per row
+    // tile.
     const int rk = 16 * tq + i16;
     const int koff = (rk >> 2) * kKBlock + (rk & 3) * 16 + 64 * g;
     const int rv = 16 * tq + 4 * g + (i16 >> 2);
@@ -363,123 +375,141 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
       const uint64_t vm1 = ti == 0 ? vm_first : (ti + 1 < ntiles ? issue_tile(ti + 1) : 0ull);
       const char DCP_LDS* tb = kvb + (ti % kNBuf) * kBufBytes;
 
-      // ---- S^T of this wave's 16 tokens x 16 rows
+      // ---- S^T of this wave's 16 tokens x 16 rows, per row tile
       bf16x8 kop[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         kop[ks] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + koff + 256 * ks);
-      f4 sc = {0.f, 0.f, 0.f, 0.f};
+      f4 sc[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) sc[r] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks], qop[ks], sc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          sc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks], qop[r][ks], sc[r], 0, 0, 0);
 
       // ---- online softmax (base 2) per row = per lane column, lazy rescale as in the
       // vector kernel (slack kRescaleSlack), here with a per-lane factor
       const int jt = j0 + ti * kTile;
-      float x[4];
+      const bool partial = vm0 != ~0ull || jt + kTile > lim_lo;   // uniform
+      s4 pb[RT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = sc[e] * a.sl2;
-      if (vm0 != ~0ull || jt + kTile > lim_lo) {   // partial tile (uniform)
-        asm volatile("");
+      for (int r = 0; r < RT; ++r) {
+        float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tt = 16 * tq + 4 * g + e;
-          x[e] = (((vm0 >> tt) & 1) && jt + tt < lim_l) ? x[e] : neg_inf();
+        for (int e = 0; e < 4; ++e) x[e] = sc[r][e] * a.sl2;
+        if (partial) {
+          asm volatile("");
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tt = 16 * tq + 4 * g + e;
+            x[e] = (((vm0 >> tt) & 1) && jt + tt < lim_l[r]) ? x[e] : neg_inf();
+          }
         }
-      }
-      const float tmax = rows_max(max_f(max_f(x[0], x[1]), max_f(x[2], x[3])));
-      const bool need = tmax > m + kRescaleSlack;   // m = -inf: any valid token
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {   // uniform branch
-        const float alpha = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
-        m = need ? tmax : m;
-        negm = need ? -tmax : negm;
-        ls *= alpha;
+        const float tmax = rows_max(max_f(max_f(x[0], x[1]), max_f(x[2], x[3])));
+        const bool need = tmax > m[r] + kRescaleSlack;   // m = -inf: any valid token
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {      // uniform branch
+          const float alpha = need ? __builtin_amdgcn_exp2f(m[r] - tmax) : 1.f;  // -inf -> 0
+          m[r] = need ? tmax : m[r];
+          negm[r] = need ? -tmax : negm[r];
+          ls[r] *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
-      }
-      float p[4];
+          for (int db = 0; db < D / 16; ++db) acc[r][db] *= alpha;
+        }
+        float p[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] + negm);   // masked: 0
-      ls += (p[0] + p[1]) + (p[2] + p[3]);
-      const f2 p01 = {p[0], p[1]}, p23 = {p[2], p[3]};
-      const u32x2 pw = {__builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2)),
-                        __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2))};
-      const s4 pb = __builtin_bit_cast(s4, pw);
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] + negm[r]);  // masked: 0
+        ls[r] += (p[0] + p[1]) + (p[2] + p[3]);
+        const f2 p01 = {p[0], p[1]}, p23 = {p[2], p[3]};
+        const u32x2 pw = {__builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2)),
+                          __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2))};
+        pb[r] = __builtin_bit_cast(s4, pw);
+      }
 
       // ---- O^T += V^T P^T, 16 dims per MFMA
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const u32x2 v = lds_tr16(tb + voff + 32 * (db ^ vsw));
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, v), pb,
-                                                            acc[db], 0, 0, 0);
+        const s4 v = __builtin_bit_cast(s4, lds_tr16(tb + voff + 32 * (db ^ vsw)));
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[r][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pb[r], acc[r][db], 0, 0, 0);
       }
       vm0 = vm1;
     }
 
-    // ---- merge the four token quarters of each row tile through LDS (the tile buffers are
-    // free once every wave has passed the barrier; no copy is in flight)
+    // ---- merge the four token quarters of each row through LDS (the tile buffers are free
+    // once every wave has passed the barrier; no copy is in flight).  Scratch rows are
+    // (wave, row tile, lane column).
     constexpr int kOStride = D + 4;   // floats per row: rows 16 bytes apart in the banks
-    static_assert(NW * 16 * kOStride * 4 <= (int)sizeof(kvs), "merge scratch");
+    constexpr int kRows = 16 * RT;    // rows per wave
+    static_assert(NW * kRows * kOStride * 4 <= (int)sizeof(kvs), "merge scratch");
     float DCP_LDS* osc = (float DCP_LDS*)&kvs[0];
-    const float lt = rows_sum(ls);
     wait_vmcnt<0>();
     __syncthreads();
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      *reinterpret_cast<f4 DCP_LDS*>(osc + (w * 16 + i16) * kOStride + 16 * db + 4 * g) = acc[db];
-    if (g == 0) {
-      mls[(w * 16 + i16) * 2] = m;
-      mls[(w * 16 + i16) * 2 + 1] = lt;
+    for (int r = 0; r < RT; ++r) {
+      const float lt = rows_sum(ls[r]);
+      const int sr = w * kRows + 16 * r + i16;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<f4 DCP_LDS*>(osc + sr * kOStride + 16 * db + 4 * g) = acc[r][db];
+      if (g == 0) {
+        mls[sr * 2] = m[r];
+        mls[sr * 2 + 1] = lt;
+      }
     }
     __syncthreads();
-    // wave (rt, tq) finishes dims 32 tq .. 32 tq + 31 of the 16 rows of row tile rt
-    const int row = lane >> 2;
+    // wave tq finishes dims 32 tq .. 32 tq + 31 of every row
     const int d0 = 32 * tq + 8 * (lane & 3);
-    float mk[4], wk[4];
-    float M = neg_inf();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      mk[k] = mls[((4 * rt + k) * 16 + row) * 2];
-      M = max_f(M, mk[k]);
-    }
-    float L = 0.f;
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RT; ++r) {
+      const int row = 16 * r + (lane >> 2);
+      float mk[4];
+      float M = neg_inf();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      wk[k] = mk[k] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
-      L += wk[k] * mls[((4 * rt + k) * 16 + row) * 2 + 1];
-      const float DCP_LDS* src = osc + ((4 * rt + k) * 16 + row) * kOStride + d0;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const f4 v = *reinterpret_cast<const f4 DCP_LDS*>(src + 4 * hh);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[4 * hh + e] += wk[k] * v[e];
+      for (int k = 0; k < 4; ++k) {
+        mk[k] = mls[(k * kRows + row) * 2];
+        M = max_f(M, mk[k]);
       }
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
-    const int rho_o = 16 * rt + row;
-    if (rho_o < R) {
-      const int qi_o = rho_o / G;
-      const int orow = qi_o * a.hq + kvh * G + (rho_o - qi_o * G);
+      float L = 0.f;
+      float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] *= inv;
-      if (single && a.o_bf16) {
-        uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0;
-        *reinterpret_cast<uint4*>(dstb) =
-            make_uint4(f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16),
-                       f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16),
-                       f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16),
-                       f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16));
-      } else {
-        float* dst = single ? static_cast<float*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0
-                            : a.po + ((size_t)item * RQ + orow) * D + d0;
-        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      for (int k = 0; k < 4; ++k) {
+        const float wk = mk[k] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
+        L += wk * mls[(k * kRows + row) * 2 + 1];
+        const float DCP_LDS* src = osc + (k * kRows + row) * kOStride + d0;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f4 v = *reinterpret_cast<const f4 DCP_LDS*>(src + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[4 * hh + e] += wk * v[e];
+        }
       }
-      if (tq == 0 && (lane & 3) == 0) {
-        if (single) a.lse_out[(size_t)b * RQ + orow] = lse;
-        else a.plse[(size_t)item * RQ + orow] = lse;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
+      if (row < R) {
+        const int qi_o = row / G;
+        const int orow = qi_o * a.hq + kvh * G + (row - qi_o * G);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= inv;
+        if (single && a.o_bf16) {
+          uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0;
+          *reinterpret_cast<uint4*>(dstb) =
+              make_uint4(f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16),
+                         f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16),
+                         f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16),
+                         f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16));
+        } else {
+          float* dst = single ? static_cast<float*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0
+                              : a.po + ((size_t)item * RQ + orow) * D + d0;
+          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+        if (tq == 0 && (lane & 3) == 0) {
+          if (single) a.lse_out[(size_t)b * RQ + orow] = lse;
+          else a.plse[(size_t)item * RQ + orow] = lse;
+        }
       }
     }
     return;
@@ -707,11 +737,11 @@ void launch_r(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEve
                         0, k);
 }
 
-// Matrix-core variant: NW = 4 waves per 16-row tile.
-template <int NW>
+// Matrix-core variant: four waves, RT 16-row tiles per wave.
+template <int RT>
 void launch_m(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  hipExtLaunchKernelGGL((gqa_shard_kernel<true, NW, 1, true>), grid, dim3(64 * NW), 0, s, e0,
-                        e1, 0, k);
+  hipExtLaunchKernelGGL((gqa_shard_kernel<true, 4, RT, true>), grid, dim3(256), 0, s, e0, e1,
+                        0, k);
 }
 
 // R = q_len * G query rows per KV head; rows sharing a (waves, rows per wave) shape share
@@ -724,8 +754,8 @@ hipError_t launch_g(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEv
                     hipEvent_t e1) {
   if constexpr (kBf16) {
     if (rows >= 8 && rows <= 32) {
-      if (rows <= 16) launch_m<4>(k, grid, s, e0, e1);
-      else launch_m<8>(k, grid, s, e0, e1);
+      if (rows <= 16) launch_m<1>(k, grid, s, e0, e1);
+      else launch_m<2>(k, grid, s, e0, e1);
       return hipGetLastError();
     }
   }
