@@ -181,7 +181,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_qwen3_235b_share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="time only the main workload's step (no interleave-1 pass, no other "
+                         "workloads): a kernel trace of it then holds only the step's launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -297,7 +299,9 @@ def main():
                     "merge_us": round(merge_us, 2),
                     "merge_gbs": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1)},
     }
-    line["kernels"][f"{kernel_name}_interleave1_us"] = fine_interleave_us(dca, torch, w, inp, kind)
+    if not args.no_secondary:
+        line["kernels"][f"{kernel_name}_interleave1_us"] = fine_interleave_us(dca, torch, w, inp,
+                                                                             kind)
     if not args.no_secondary and kind == dca.GQA:
         line["secondary"] = secondary_mla(dca, wl, torch)
         line["secondary_ragged"] = secondary_ragged(dca, wl, torch)

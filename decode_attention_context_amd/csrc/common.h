@@ -66,7 +66,10 @@ __device__ __forceinline__ int row_local_end(const int32_t* seq_lens, int b, int
                                              int q_len, int qi, int rank, int cp, int il) {
   int64_t L = seq_lens[b];
   L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
-  return (int)dcp_walk_local_count(L - q_len + 1 + qi, rank, cp, il);
+  const int64_t Lq = L - q_len + 1 + qi;   // below 2^31 (len_cap is)
+  return Lq <= 0 ? 0
+                 : (int)dcp_walk_local_count32((uint32_t)Lq, (uint32_t)rank, (uint32_t)cp,
+                                               (uint32_t)il);
 }
 
 // Butterfly reductions across the 64 lanes of a wave.

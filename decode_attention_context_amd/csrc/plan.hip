@@ -9,16 +9,18 @@
 //   3. n_b = ceil(local_b / chunk) items per request; off = exclusive prefix sum;
 //   4. item i of request b = (b, i * chunk, min((i + 1) * chunk, local_b), off_b + i), the
 //      last field being the index of its partial output;
-//   5. the items are stored in dispatch order, by descending tile count (a counting sort
-//      over kBuckets buckets, longer items sharing the top bucket): workgroup slot k runs
-//      items[k].
+//   5. the items are stored in dispatch order, by descending tile count: the full-size
+//      items of every request first (by request), then the shorter last items of the
+//      requests by a counting sort over kBuckets buckets (longer ones sharing the top
+//      bucket): workgroup slot k runs items[k].
 // Since chunk >= total / target, the item count never exceeds target + batch, which is the
 // bound the host sizes the workspace with.  A request's partials keep consecutive indices
 // (the split combine reads them together); only the dispatch order changes.  Greedy
 // dispatch of the longest items first keeps a ragged batch's long requests from starting
 // in the last round: for 512 lognormal lengths around 67k tokens on 8 ranks it takes the
-// simulated makespan from 1.54x to 1.04x the even share of one round.  The order within a
-// bucket depends on atomics; no result does (each partial has its fixed index).
+// simulated makespan from 1.54x to 1.04x the even share of one round.  The order of the
+// shorter items within a bucket depends on atomics; no result does (each partial has its
+// fixed index).
 #include "launch.h"
 
 namespace dcp {
@@ -26,28 +28,70 @@ namespace dcp {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kBuckets = 1024;   // tile-count buckets of the dispatch order
+static_assert(kBuckets == kPlanThreads, "one bucket per thread in the bucket scan");
+
+// Inclusive scan inside a wave (shuffles, no LDS).
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan over the workgroup: a scan inside each wave, then every thread adds the
+// totals of the waves before its own (two barriers; s_w is free again on return).
+template <typename T>
+__device__ __forceinline__ T block_excl_scan(T v, T* s_w, T& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const T incl = wave_incl_scan(v, lane);
+  if (lane == 63) s_w[wid] = incl;
+  __syncthreads();
+  T pre = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanWaves; ++k) {
+    const T t = s_w[k];
+    pre += k < wid ? t : T(0);
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + incl - v;
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int batch, int rank, int cp, int interleave,
     int64_t len_cap, int64_t target, int tile, int min_chunk, int32_t* __restrict__ header,
     int32_t* __restrict__ off, int4* __restrict__ items) {
-  __shared__ long long s_a[kPlanThreads];
-  __shared__ long long s_b[kPlanThreads];
-  __shared__ int s_err[kPlanThreads];
+  __shared__ long long s_sum[kPlanWaves];
+  __shared__ long long s_max[kPlanWaves];
+  __shared__ int s_err[kPlanWaves];
+  __shared__ int s_w[kPlanWaves];
+  __shared__ unsigned long long s_w64[kPlanWaves];
   __shared__ int s_hist[kBuckets];   // items per bucket, then next free position per bucket
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
   const int per = (batch + kPlanThreads - 1) / kPlanThreads;
   const int b0 = min(tid * per, batch);
   const int b1 = min(b0 + per, batch);
+  s_hist[tid] = 0;
 
-  auto local_of = [&](int b, int& err) -> long long {
+  // per-request arithmetic in 32 bits: lengths are clamped to len_cap and the host bounds
+  // len_cap and interleave * cp below 2^31, so every local count, item size and item
+  // boundary fits (64-bit divisions are long software sequences on the GPU)
+  auto local_of = [&](int b, int& err) -> uint32_t {
     long long L = seq_lens[b];
     if (L < 0) { err |= kErrSeqLen; L = 0; }
     if (L > len_cap) { err |= kErrSeqLen; L = len_cap; }
-    return dcp_walk_local_count(L, rank, cp, interleave);
+    return dcp_walk_local_count32((uint32_t)L, (uint32_t)rank, (uint32_t)cp,
+                                  (uint32_t)interleave);
   };
 
+  // 1. total and longest local length, error bits
   long long sum = 0, mx = 0;
   int err = 0;
   for (int b = b0; b < b1; ++b) {
@@ -55,95 +99,86 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     sum += loc;
     mx = loc > mx ? loc : mx;
   }
-  s_a[tid] = sum;
-  s_b[tid] = mx;
-  s_err[tid] = err;
-  __syncthreads();
-  for (int s = kPlanThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) {
-      s_a[tid] += s_a[tid + s];
-      s_b[tid] = s_b[tid] > s_b[tid + s] ? s_b[tid] : s_b[tid + s];
-      s_err[tid] |= s_err[tid + s];
-    }
-    __syncthreads();
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    sum += __shfl_xor(sum, o, 64);
+    const long long m2 = __shfl_xor(mx, o, 64);
+    mx = m2 > mx ? m2 : mx;
+    err |= __shfl_xor(err, o, 64);
   }
-  const long long total = s_a[0];
-  const long long maxloc = s_b[0];
-  const int err_all = s_err[0];
+  if (lane == 0) {
+    s_sum[wid] = sum;
+    s_max[wid] = mx;
+    s_err[wid] = err;
+  }
   __syncthreads();
+  long long total = 0, maxloc = 0;
+  int err_all = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanWaves; ++k) {
+    total += s_sum[k];
+    maxloc = s_max[k] > maxloc ? s_max[k] : maxloc;
+    err_all |= s_err[k];
+  }
 
-  long long chunk = (total + target - 1) / target;
-  chunk = (chunk + tile - 1) / tile * tile;
-  if (chunk < min_chunk) chunk = min_chunk;
+  // 2. item size (one 64-bit division; the result is at most the longest request rounded
+  // up to the tile)
+  long long chunk64 = (total + target - 1) / target;
+  chunk64 = (chunk64 + tile - 1) / tile * tile;
+  if (chunk64 < min_chunk) chunk64 = min_chunk;
   const long long cap = (maxloc + tile - 1) / tile * tile;
-  if (chunk > cap) chunk = cap;
-  if (chunk < tile) chunk = tile;
+  if (chunk64 > cap) chunk64 = cap;
+  if (chunk64 < tile) chunk64 = tile;
+  const uint32_t chunk = (uint32_t)chunk64;
+  const uint32_t utile = (uint32_t)tile;
 
-  long long cnt = 0;
-  for (int b = b0; b < b1; ++b) {
-    int e = 0;
-    cnt += (local_of(b, e) + chunk - 1) / chunk;
-  }
-  // inclusive scan of the per-thread counts (Hillis-Steele over the workgroup)
-  s_a[tid] = cnt;
-  __syncthreads();
-  for (int s = 1; s < kPlanThreads; s <<= 1) {
-    const long long v = tid >= s ? s_a[tid - s] : 0;
-    __syncthreads();
-    s_a[tid] += v;
-    __syncthreads();
-  }
-  long long base = s_a[tid] - cnt;
-  for (int k = tid; k < kBuckets; k += kPlanThreads) s_hist[k] = 0;
-  __syncthreads();
-  // bucket of an item: kBuckets - 1 - (tile count, capped): longest first
-  auto bucket = [&](long long len) -> int {
-    const long long nt = (len + tile - 1) / tile;
+  // 3. request b has n = ceil(loc / chunk) items: nf = loc / chunk full items of exactly
+  // chunk tokens (all in the top bucket: no item is longer) and, when loc mod chunk != 0, a
+  // tail item.  One scan of the packed pair (n, nf) gives the partial indices (off) and the
+  // dispatch positions of the full items, which go first, by request; the tails follow,
+  // ordered by bucket (one LDS atomic per request with a tail).  Item counts are at most
+  // target + batch, so 32 bits hold them.
+  auto items_of = [&](uint32_t loc) -> int { return (int)(loc / chunk + (loc % chunk != 0)); };
+  auto bucket = [&](uint32_t len) -> int {   // kBuckets - 1 - (tile count, capped)
+    const uint32_t nt = len / utile + (len % utile != 0);
     return kBuckets - 1 - (int)(nt < kBuckets - 1 ? nt : kBuckets - 1);
   };
+  unsigned long long packed = 0;
   for (int b = b0; b < b1; ++b) {
     int e = 0;
-    const long long loc = local_of(b, e);
-    const long long n = (loc + chunk - 1) / chunk;
-    off[b] = (int32_t)base;
-    for (long long i = 0; i < n; ++i) {
-      const long long j0 = i * chunk;
-      const long long j1 = j0 + chunk < loc ? j0 + chunk : loc;
-      atomicAdd(&s_hist[bucket(j1 - j0)], 1);
-    }
-    base += n;
+    const uint32_t loc = local_of(b, e);
+    const uint32_t nf = loc / chunk;
+    packed += ((unsigned long long)(uint32_t)items_of(loc) << 32) | nf;
+    if (loc - nf * chunk != 0) atomicAdd(&s_hist[bucket(loc - nf * chunk)], 1);
   }
+  unsigned long long packed_total = 0;
+  const unsigned long long pre = block_excl_scan(packed, s_w64, packed_total);
+  const int n_items = (int)(packed_total >> 32);
+  const int n_full = (int)(packed_total & 0xffffffffu);
+  // 4. tail positions: n_full + exclusive scan of the tail counts (thread = bucket)
+  int unused = 0;
+  const int first = block_excl_scan(s_hist[tid], s_w, unused);
+  s_hist[tid] = n_full + first;
   __syncthreads();
-  // exclusive prefix sum of the bucket counts (Hillis-Steele over kBuckets entries)
-  {
-    const int mine = tid < kBuckets ? s_hist[tid] : 0;
-    for (int s = 1; s < kBuckets; s <<= 1) {
-      const int v = (tid < kBuckets && tid >= s) ? s_hist[tid - s] : 0;
-      __syncthreads();
-      if (tid < kBuckets) s_hist[tid] += v;
-      __syncthreads();
-    }
-    const int incl = tid < kBuckets ? s_hist[tid] : 0;
-    __syncthreads();
-    if (tid < kBuckets) s_hist[tid] = incl - mine;
-    __syncthreads();
-  }
-  base = s_a[tid] - cnt;
+  int base = (int)(pre >> 32);
+  int fpos = (int)(pre & 0xffffffffu);
   for (int b = b0; b < b1; ++b) {
     int e = 0;
-    const long long loc = local_of(b, e);
-    const long long n = (loc + chunk - 1) / chunk;
-    for (long long i = 0; i < n; ++i) {
-      const long long j0 = i * chunk;
-      const long long j1 = j0 + chunk < loc ? j0 + chunk : loc;
-      items[atomicAdd(&s_hist[bucket(j1 - j0)], 1)] =
-          make_int4(b, (int)j0, (int)j1, (int)(base + i));
-    }
+    const uint32_t loc = local_of(b, e);
+    const int n = items_of(loc);
+    const int nf = (int)(loc / chunk);
+    off[b] = base;
+    for (int i = 0; i < nf; ++i)
+      items[fpos + i] = make_int4(b, (int)(i * chunk), (int)((i + 1) * chunk), base + i);
+    if (nf < n)
+      items[atomicAdd(&s_hist[bucket(loc - nf * chunk)], 1)] =
+          make_int4(b, (int)(nf * chunk), (int)loc, base + nf);
     base += n;
+    fpos += nf;
   }
-  if (tid == kPlanThreads - 1) {
-    off[batch] = (int32_t)s_a[kPlanThreads - 1];
-    header[1] = (int32_t)s_a[kPlanThreads - 1];
+  if (tid == 0) {
+    off[batch] = n_items;
+    header[1] = n_items;
     header[2] = (int32_t)chunk;
     header[0] = err_all;
   }

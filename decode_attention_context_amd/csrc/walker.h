@@ -29,6 +29,17 @@ DCP_HD int64_t dcp_walk_local_count(int64_t L, int rank, int C, int I) {
   return full * I + extra;
 }
 
+// The same count in 32-bit arithmetic, for L and I * C below 2^31 (the library's bounds on
+// sequence lengths and on I * C): one 32-bit division instead of a 64-bit one.
+DCP_HD uint32_t dcp_walk_local_count32(uint32_t L, uint32_t rank, uint32_t C, uint32_t I) {
+  const uint32_t ic = I * C;
+  const uint32_t full = L / ic;
+  const uint32_t rest = L - full * ic;   // < I * C
+  const uint32_t lo = rank * I;
+  const uint32_t extra = rest <= lo ? 0u : (rest - lo > I ? I : rest - lo);
+  return full * I + extra;
+}
+
 // Global position of local token j of `rank` (32-bit: positions are below 2^31).
 DCP_HD uint32_t dcp_walk_global_pos(uint32_t j, uint32_t rank, uint32_t C, uint32_t I) {
   const uint32_t c = j / I;
