@@ -305,6 +305,7 @@ def main():
     if not args.no_secondary and kind == dca.GQA:
         line["secondary"] = secondary_mla(dca, wl, torch)
         line["secondary_ragged"] = secondary_ragged(dca, wl, torch)
+        line["secondary_long"] = secondary_long(dca, wl, torch)
         line["secondary_multi_token"] = secondary_multi_token(dca, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
@@ -511,6 +512,51 @@ def secondary_ragged(dca, wl, torch, steps=5):
             "merge8_bf16_partials_us": round(merge16_s * 1e6, 2),
             "merge8_bf16_partials_bytes": merge16_bytes,
             "merge8_bf16_partials_gbs": round(merge16_bytes / merge16_s / 1e9, 1),
+            "step_ms": round(step_s * 1e3, 3),
+            "kv_tokens_per_s": round(int(lens.sum()) / step_s, 1)}
+
+
+def secondary_long(dca, wl, torch, steps=10):
+    """Long-context MLA (8 requests x 200000 tokens, C = 4, I = 128): all 4 shard kernels of
+    a step (sum of their durations, MFMA utilisation, HBM rate), the merge of 4 partials per
+    (request, head) row (10.5 MB: latency-bound), and the whole step replayed as a HIP
+    graph."""
+    w = wl.MLA_LONG
+    inp = wl.make_inputs(w, device="cuda")
+    lens = w.seq_lens()
+    step, shard_ev, merge_ev, ws = run_step_fns(dca, w, inp, dca.MLA)
+    for _ in range(2):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    assert dca.read_device_errors(ws) == 0
+    C = w.cp_size
+    shard_ms = [a.elapsed_time(b) for a, b in shard_ev]
+    shards_s = sum(shard_ms) / steps / 1e3
+    costs = [mla_launch_cost(w, lens, r) for r in range(C)]
+    byts = sum(c[0] for c in costs)
+    flops = sum(c[1] for c in costs)
+    merge_s = sorted(a.elapsed_time(b) for a, b in merge_ev)[len(merge_ev) // 2] / 1e3
+    merge_bytes = (C + 1) * w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
+    graph = capture_step(torch, step)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    del inp, graph
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "kv_tokens": int(lens.sum()),
+            "mla_shards_us": round(shards_s * 1e6, 1),
+            "mla_shard_us_per_rank": [round(sum(shard_ms[r::C]) / steps * 1e3, 2)
+                                      for r in range(C)],
+            "mla_mfma_util": round(flops / shards_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mla_hbm_gbs": round(byts / shards_s / 1e9, 1),
+            "merge4_us": round(merge_s * 1e6, 2), "merge4_bytes": merge_bytes,
             "step_ms": round(step_s * 1e3, 3),
             "kv_tokens_per_s": round(int(lens.sum()) / step_s, 1)}
 
