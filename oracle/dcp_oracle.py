@@ -36,6 +36,11 @@ Readings taken where the pages are silent (also listed in the design notes):
       its cache; row i sits at position seq_len - q_len + i and attends every position up
       to and including its own (a causal mask among the draft tokens, aligned to the end
       of the sequence).  A row whose position is negative attends nothing.
+  R9  fp8 KV cache (the lower-byte KV variant; the pages leave the KV dtype open): K and V
+      pages hold OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+      exponent 0 is subnormal; S.1111.111 is NaN; no infinities), each tensor with one
+      float32 scale: the cached value is decode(code) * scale.  Attention is then the plain
+      definition over those values; queries keep their own dtype.
 """
 
 import math
@@ -252,6 +257,27 @@ def mla_full_mq(q_rows, latent_pages, block_table_row, seq_len, scale, block_siz
 # LSE merge  ([Blog] "DCP execution flow", step 3: partial outputs and LSE values are
 # combined with the online-softmax trick)
 # ----------------------------------------------------------------------------------------
+
+# ----------------------------------------------------------------------------------------
+# fp8 KV cache (reading R9): the values an fp8 cache represents, then the plain definitions
+# ----------------------------------------------------------------------------------------
+
+def fp8_e4m3_decode(codes):
+    """Exact float64 values of OCP FP8 E4M3 codes (uint8): (-1)^s * (1 + m/8) * 2^(e-7) for
+    exponent e in 1..15, (-1)^s * (m/8) * 2^-6 for e = 0, NaN for the code S.1111.111."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_kv_values(codes, kv_scale):
+    """The cache values an fp8 page array stands for: decode(code) * scale (reading R9)."""
+    return fp8_e4m3_decode(codes) * float(kv_scale)
+
 
 def merge(o_parts, lse_parts):
     """Combine C partials into the attention over the union of their token sets.
