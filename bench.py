@@ -58,10 +58,11 @@ def gqa_launch_bytes(w, lens, rank):
     """Algorithmic HBM bytes of one GQA shard launch: the K and V rows the rank owns, the
     queries, the block-table entries of owned pages, and the O / lse written."""
     elem = 2 if w.dtype == "bf16" else 4
+    kv_elem = 1 if w.kv_dtype == "fp8" else elem
     tok = sum(owned_tokens_count(int(L), rank, w.cp_size, w.interleave) for L in lens)
     pages = sum(owned_pages_count(int(L), rank, w.cp_size, w.interleave, w.block_size)
                 for L in lens)
-    kv = tok * 2 * w.num_kv_heads * w.head_dim_qk * elem
+    kv = tok * 2 * w.num_kv_heads * w.head_dim_qk * kv_elem
     q = w.batch * w.num_q_heads * w.head_dim_qk * elem
     out = w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
     return kv + q + out + pages * 4, tok
@@ -163,7 +164,8 @@ def run_step_fns(dca, w, inp, kind):
                 shard_events.append(ev)
             dca.shard(q, kv, v, inp["block_table"], inp["seq_lens"], r, C, w.interleave,
                       w.scale, kind=kind, max_seq_len=inp["max_seq_len"], out=o_parts[r],
-                      lse=l_parts[r], workspace=ws, events=ev)
+                      lse=l_parts[r], workspace=ws, events=ev, k_scale=inp.get("k_scale"),
+                      v_scale=inp.get("v_scale"))
         ev = None
         if record:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -258,10 +260,13 @@ def main():
         bytes_avg = sum(c[0] for c in costs) / C
         dur_s = sum(per_rank_ms) / C / 1e3
         achieved = bytes_avg / dur_s / 1e9
-        traffic = load_counters("gqa_shard", "gqa_shard.hip", w.name)
+        fp8 = w.kv_dtype == "fp8"
+        traffic = (load_counters("gqa_fp8", "gqa_fp8.hip", w.name) if fp8
+                   else load_counters("gqa_shard", "gqa_shard.hip", w.name))
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "gqa_shard_kernel<bf16,NW=4,mfma>",
+                "traffic": traffic,
+                "kernel": "gqa_fp8_kernel<RT=1>" if fp8 else "gqa_shard_kernel<bf16,NW=4,mfma>",
                 "algorithmic_bytes_per_launch": int(bytes_avg),
                 "avg_launch_us": round(dur_s * 1e6, 2)}
         kernel_name = "gqa_shard"
@@ -306,6 +311,7 @@ def main():
         line["secondary"] = secondary_mla(dca, wl, torch)
         line["secondary_ragged"] = secondary_ragged(dca, wl, torch)
         line["secondary_long"] = secondary_long(dca, wl, torch)
+        line["secondary_fp8kv"] = secondary_fp8kv(dca, wl, torch)
         line["secondary_multi_token"] = secondary_multi_token(dca, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
@@ -410,7 +416,8 @@ def shard_kernel_us(dca, torch, w, inp, kind, steps=10):
         ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         _, _, ws = dca.shard(inp["q"], kv, v, inp["block_table"], inp["seq_lens"], 0, w.cp_size,
                              w.interleave, w.scale, kind=kind, max_seq_len=inp["max_seq_len"],
-                             workspace=ws, events=ev)
+                             workspace=ws, events=ev, k_scale=inp.get("k_scale"),
+                             v_scale=inp.get("v_scale"))
         torch.cuda.synchronize()
         if i >= 3:
             ms.append(ev[0].elapsed_time(ev[1]))
@@ -514,6 +521,25 @@ def secondary_ragged(dca, wl, torch, steps=5):
             "merge8_bf16_partials_gbs": round(merge16_bytes / merge16_s / 1e9, 1),
             "step_ms": round(step_s * 1e3, 3),
             "kv_tokens_per_s": round(int(lens.sum()) / step_s, 1)}
+
+
+def secondary_fp8kv(dca, wl, torch):
+    """The GQA share with its K / V cache in fp8 (OCP E4M3 codes, one scale each): the
+    rank-0 shard kernel at q_len 1 and 4 (HBM rate on half the cache bytes, KV tokens/s)."""
+    res = {"workload": wl.GQA_SHARE_FP8.name}
+    for nq in (1, 4):
+        w = wl.GQA_SHARE_FP8.with_(q_len=nq)
+        inp = wl.make_inputs(w, device="cuda")
+        us = shard_kernel_us(dca, torch, w, inp, dca.GQA)
+        byts, tok = gqa_launch_bytes(w, w.seq_lens(), 0)
+        byts += (nq - 1) * w.batch * w.num_q_heads * (w.head_dim_qk * 2 + (w.head_dim_v + 1) * 4)
+        res[f"q{nq}"] = {"shard_us": round(us, 2), "algorithmic_bytes": int(byts),
+                         "hbm_gbs": round(byts / us / 1e3, 1),
+                         "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "kv_tokens_per_s": round(tok / us * 1e6, 1)}
+        del inp
+    torch.cuda.empty_cache()
+    return res
 
 
 def secondary_long(dca, wl, torch, steps=10):

@@ -68,6 +68,9 @@ _SIGS = {
                                   _F, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
     "dcp_attn_shard_ex": (_I, [ctypes.POINTER(Desc), _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I,
                                _I, _I, _F, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+    "dcp_attn_shard_fp8kv": (_I, [ctypes.POINTER(Desc), _I, _I, _P, _P, _P, _F, _F, _P, _P, _I,
+                                  _I64, _I, _I, _I, _F, _P, _P, _P, ctypes.c_size_t, _P, _P,
+                                  _P]),
     "dcp_merge_ex": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "dcp_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "dcp_merge_timed": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
@@ -165,7 +168,7 @@ def alloc_workspace(desc, batch, max_seq_len, cp_size, interleave, device=None, 
 
 def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave, scale, *,
           kind=None, max_seq_len=None, out=None, lse=None, workspace=None, stream=None,
-          events=None, out_dtype=torch.float32):
+          events=None, out_dtype=torch.float32, k_scale=None, v_scale=None):
     """Partial attention of the gathered queries over rank `rank`'s shard.
 
     GQA: q [b, Hq, D], kv_pages = K pages [nb, Hkv, B, D], v_pages = V pages (same shape).
@@ -177,7 +180,9 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     workspace); O_r is float32, or bf16 (rounded to nearest even) with
     out_dtype=torch.bfloat16 (dcp_attn_shard_ex).
     `events` = (begin, end) torch.cuda.Event pair that takes the attention kernel's own start
-    and end time stamps."""
+    and end time stamps.
+    fp8 KV cache (GQA, bf16 q): K and V pages of dtype uint8 or torch.float8_e4m3fn holding
+    OCP FP8 E4M3 codes, with the float scales k_scale and v_scale (dcp_attn_shard_fp8kv)."""
     lib = load()
     if kind is None:
         kind = MLA if v_pages is None else GQA
@@ -185,9 +190,18 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     if q.dim() not in (3, 4):
         raise ValueError(f"q must be [b, Hq, D] or [b, q_len, Hq, D], got {tuple(q.shape)}")
     q_len = q.shape[1] if q.dim() == 4 else 1
-    _need(kv_pages, "kv_pages", dtype=q.dtype)
+    fp8 = kind == GQA and kv_pages.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an fp8 KV cache needs k_scale and v_scale")
+        if q.dtype != torch.bfloat16:
+            raise TypeError("an fp8 KV cache takes bf16 queries")
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale / v_scale apply to an fp8 KV cache only")
+    kv_dtype = kv_pages.dtype if fp8 else q.dtype
+    _need(kv_pages, "kv_pages", dtype=kv_dtype)
     if kind == GQA:
-        _need(v_pages, "v_pages", dtype=q.dtype)
+        _need(v_pages, "v_pages", dtype=kv_dtype)
         if v_pages.shape != kv_pages.shape:
             raise ValueError("K and V pages must have the same shape")
     elif v_pages is not None:
@@ -218,7 +232,18 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     args = (_ptr(q), _ptr(kv_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), batch,
             int(max_seq_len), rank, cp_size, interleave, float(scale), _ptr(out), _ptr(lse),
             _ptr(workspace), workspace.numel(), _stream(stream))
-    if out_dtype != torch.float32:
+    if fp8:
+        evs = (ctypes.c_void_p(0), ctypes.c_void_p(0))
+        if events is not None:
+            for ev in events:
+                if not ev.cuda_event:   # torch creates the HIP event on its first record
+                    ev.record(stream)
+            evs = tuple(ctypes.c_void_p(ev.cuda_event) for ev in events)
+        _check("dcp_attn_shard_fp8kv",
+               lib.dcp_attn_shard_fp8kv(ctypes.byref(desc), q_len, _dtype_code(out_dtype),
+                                        _ptr(q), _ptr(kv_pages), _ptr(v_pages), float(k_scale),
+                                        float(v_scale), *args[3:], *evs))
+    elif out_dtype != torch.float32:
         evs = (ctypes.c_void_p(0), ctypes.c_void_p(0))
         if events is not None:
             for ev in events:

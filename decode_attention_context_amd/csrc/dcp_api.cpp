@@ -84,12 +84,24 @@ bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
   return true;
 }
 
+// fp8 KV cache of a GQA shard call: K / V pages hold fp8 codes, values code * scale.
+struct KvFp8 {
+  float k_scale, v_scale;
+};
+
 int shard_impl(const dcp_attn_desc* d, int q_len, int o_dtype, const void* q, const void* kv,
                const void* v, const int32_t* bt, const int32_t* lens, int batch,
                int64_t max_seq_len, int rank, int cp, int il, float scale, void* o, float* lse,
-               void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+               void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
+               const KvFp8* fp8 = nullptr) {
   int st = check_desc(d, q_len, batch, max_seq_len, cp, il);
   if (st != DCP_OK) return st;
+  if (fp8) {
+    if (d->kind != DCP_GQA || d->dtype != DCP_BF16) return DCP_EUNSUPPORTED;
+    if (!dcp::gqa_fp8_supported(d->head_dim_qk, d->num_q_heads / d->num_kv_heads, q_len))
+      return DCP_EUNSUPPORTED;
+    if (!std::isfinite(fp8->k_scale) || !std::isfinite(fp8->v_scale)) return DCP_EINVAL;
+  }
   if (o_dtype != DCP_F32 && o_dtype != DCP_BF16) return DCP_EINVAL;
   const int o_bf16 = o_dtype == DCP_BF16;
   if (rank < 0 || rank >= cp || !std::isfinite(scale)) return DCP_EINVAL;
@@ -112,7 +124,9 @@ int shard_impl(const dcp_attn_desc* d, int q_len, int o_dtype, const void* q, co
     dcp::GqaArgs a{q, kv, v, bt, d->num_q_heads, d->num_kv_heads, d->head_dim_qk, d->block_size,
                    d->max_blocks_per_seq, d->num_blocks, rank, cp, il, scale, d->dtype, rows,
                    o_bf16};
-    e = dcp::launch_gqa_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
+    e = fp8 ? dcp::launch_gqa_fp8_shard(a, fp8->k_scale, fp8->v_scale, p.max_items, w, o, lse,
+                                        stream, ev0, ev1)
+            : dcp::launch_gqa_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   } else {
     dcp::MlaArgs a{q, kv, bt, d->block_size, d->max_blocks_per_seq, d->num_blocks,
                    rank, cp, il, scale, rows, o_bf16};
@@ -160,6 +174,19 @@ int dcp_attn_shard_ex(const dcp_attn_desc* desc, int q_len, int o_dtype, const v
   return shard_impl(desc, q_len, o_dtype, q, kv_pages, v_pages, block_table, seq_lens, batch,
                     max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
                     workspace_bytes, stream, ev_begin, ev_end);
+}
+
+int dcp_attn_shard_fp8kv(const dcp_attn_desc* desc, int q_len, int o_dtype, const void* q,
+                         const void* k_pages, const void* v_pages, float k_scale,
+                         float v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                         int batch, int64_t max_seq_len, int rank, int cp_size, int interleave,
+                         float scale, void* o_partial, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
+                         hipEvent_t ev_end) {
+  const KvFp8 f{k_scale, v_scale};
+  return shard_impl(desc, q_len, o_dtype, q, k_pages, v_pages, block_table, seq_lens, batch,
+                    max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
+                    workspace_bytes, stream, ev_begin, ev_end, &f);
 }
 
 int dcp_attn_shard_mq(const dcp_attn_desc* desc, int q_len, const void* q, const void* kv_pages,

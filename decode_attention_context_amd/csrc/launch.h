@@ -56,6 +56,15 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 bool gqa_supported(int dtype, int head_dim, int group, int q_len);
 
+// fp8 KV cache (OCP FP8 E4M3 codes, one float32 scale per tensor; bf16 queries): the same
+// shard with K / V values decode(code) * scale.  Supported for head_dim 128 and 8 to 32
+// query rows (q_len * group) per KV head.
+hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
+                                int64_t max_items, const WsPtrs& ws, void* o_out,
+                                float* lse_out, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                                hipEvent_t ev1 = nullptr);
+bool gqa_fp8_supported(int head_dim, int group, int q_len);
+
 struct MlaArgs {
   const void* q;
   const void* latent;

@@ -13,7 +13,8 @@ input tokens.  The trace itself is not available; the lognormal lengths stand in
 Queries: [batch][Hq][Dk], or [batch][q_len][Hq][Dk] for multi-token decode (q_len > 1:
 the request's last q_len cache tokens are its draft tokens, each verified by one query row).
 Cache layouts:
-  GQA  k_pages, v_pages: [num_blocks][Hkv][block_size][D]   (fp32 or bf16)
+  GQA  k_pages, v_pages: [num_blocks][Hkv][block_size][D]   (fp32 or bf16; or uint8 fp8
+       codes with k_scale / v_scale when kv_dtype is "fp8")
   MLA  latent_pages:     [num_blocks][block_size][576]      (bf16)
   block_table: int32 [batch][max_blocks_per_seq], physical page per logical page,
                padded with -1;  seq_lens: int32 [batch], global context lengths.
@@ -56,6 +57,8 @@ class Workload:
     lengths: tuple = field(default=())
     ragged: dict = field(default=None)   # lognormal recipe, see ragged_lengths()
     q_len: int = 1            # query positions per request (multi-token decode when > 1)
+    kv_dtype: str = ""        # "" = dtype; "fp8": GQA K / V pages of OCP FP8 E4M3 codes
+    kv_scales: tuple = (0.5, 0.25)   # fp8 cache: (k_scale, v_scale), value = code * scale
 
     def seq_lens(self):
         if self.ragged is not None:
@@ -106,7 +109,10 @@ MLA_RAGGED = Workload("mla_ragged_512", "mla", "bf16", batch=512, num_q_heads=ML
                       cp_size=8, interleave=64, scale=_scale(192), seed=1005,
                       ragged=dict(median=67000, sigma=0.8, lo=1, hi=262144, seed=1005))
 
-WORKLOADS = {w.name: w for w in (TINY_GQA, GQA_SHARE, MLA_DECODE, MLA_LONG, MLA_RAGGED)}
+# the GQA share with its K / V cache in fp8 (the lower-byte cache variant)
+GQA_SHARE_FP8 = replace(GQA_SHARE, name="gqa_qwen3_235b_share_fp8kv", kv_dtype="fp8")
+WORKLOADS = {w.name: w for w in (TINY_GQA, GQA_SHARE, MLA_DECODE, MLA_LONG, MLA_RAGGED,
+                                 GQA_SHARE_FP8)}
 
 
 def torch_dtype(name):
@@ -119,6 +125,19 @@ def _fill_normal(t, gen, chunk_elems=1 << 28):
     for s in range(0, flat.numel(), chunk_elems):
         flat[s:s + chunk_elems].normal_(generator=gen)
     return t
+
+
+def _fill_fp8(shape, gen, scale, device, chunk_elems=1 << 26):
+    """fp8 cache pages: N(0,1) float32 draws divided by `scale`, rounded to OCP FP8 E4M3 by
+    torch's float8_e4m3fn conversion (nearest, saturating to the largest finite value is not
+    needed: |x| / scale stays far below 448), stored as uint8 codes."""
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), chunk_elems):
+        n = min(chunk_elems, flat.numel() - s)
+        x = torch.empty(n, dtype=torch.float32, device=device).normal_(generator=gen)
+        flat[s:s + n] = (x / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return out
 
 
 def make_inputs(w, device="cpu", seed=None):
@@ -148,8 +167,14 @@ def make_inputs(w, device="cpu", seed=None):
     if w.kind == "gqa":
         out["q"] = _fill_normal(torch.empty(qshape, dtype=dt, device=device), gen)
         shape = (num_blocks, w.num_kv_heads, bsz, w.head_dim_qk)
-        out["k_pages"] = _fill_normal(torch.empty(shape, dtype=dt, device=device), gen)
-        out["v_pages"] = _fill_normal(torch.empty(shape, dtype=dt, device=device), gen)
+        if w.kv_dtype == "fp8":
+            ks, vs = w.kv_scales
+            out["k_pages"] = _fill_fp8(shape, gen, ks, device)
+            out["v_pages"] = _fill_fp8(shape, gen, vs, device)
+            out["k_scale"], out["v_scale"] = float(ks), float(vs)
+        else:
+            out["k_pages"] = _fill_normal(torch.empty(shape, dtype=dt, device=device), gen)
+            out["v_pages"] = _fill_normal(torch.empty(shape, dtype=dt, device=device), gen)
     else:
         out["q"] = _fill_normal(torch.empty(qshape, dtype=dt, device=device), gen)
         out["latent_pages"] = _fill_normal(

@@ -182,6 +182,25 @@ int dcp_attn_shard_ex(const dcp_attn_desc* desc, int q_len, int o_dtype, const v
                       void* workspace, size_t workspace_bytes, hipStream_t stream,
                       hipEvent_t ev_begin, hipEvent_t ev_end);
 
+/* The shard call of a GQA cache stored in fp8 (the lower-byte KV variant: the pages leave
+ * the KV dtype open).  k_pages / v_pages hold OCP FP8 E4M3 codes (uint8; sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent 0 subnormal; S.1111.111 NaN, no infinities),
+ * [num_blocks][num_kv_heads][block_size][head_dim], 16-byte aligned; the cached key / value
+ * is decode(code) * k_scale / v_scale (finite floats).  desc->kind = DCP_GQA and
+ * desc->dtype = DCP_BF16 describe the bf16 queries; head_dim 128 and 8 to 32 query rows
+ * (q_len * num_q_heads / num_kv_heads) per KV head are supported, other shapes return
+ * DCP_EUNSUPPORTED without launching.  Scores are scale * q . k; everything else (q_len,
+ * o_dtype, outputs, workspace from dcp_workspace_size_mq with the same desc, events,
+ * errors) is as in dcp_attn_shard_ex.  A code of NaN in a page the call reads gives NaN
+ * outputs for the rows that see it. */
+int dcp_attn_shard_fp8kv(const dcp_attn_desc* desc, int q_len, int o_dtype, const void* q,
+                         const void* k_pages, const void* v_pages, float k_scale,
+                         float v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                         int batch, int64_t max_seq_len, int rank, int cp_size, int interleave,
+                         float scale, void* o_partial, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
+                         hipEvent_t ev_end);
+
 /* LSE-weighted merge of cp_size partials into attention over the union of their tokens
  * (blog, "DCP execution flow", step 3: the LSE values reweight the partial results with
  * the online-softmax trick).  With m = max of the finite lse_r:

@@ -51,7 +51,8 @@ def run_shards(inp, kind, cp_size, interleave, scale, ranks=None):
     for r in (range(cp_size) if ranks is None else ranks):
         o, l, ws = dca.shard(q, kv, v, inp["block_table"], inp["seq_lens"], r, cp_size,
                              interleave, scale, kind=kind, max_seq_len=inp["max_seq_len"],
-                             workspace=ws)
+                             workspace=ws, k_scale=inp.get("k_scale"),
+                             v_scale=inp.get("v_scale"))
         os_.append(o)
         ls_.append(l)
         assert dca.read_device_errors(ws) == 0
@@ -72,8 +73,12 @@ def request_host(inp, kind, b):
     q = inp["q"][b].float().cpu().numpy().astype(np.float64)
     row = np.arange(npages, dtype=np.int64)
     if kind == dca.GQA:
-        k = inp["k_pages"][pages].float().cpu().numpy().astype(np.float64)
-        v = inp["v_pages"][pages].float().cpu().numpy().astype(np.float64)
+        if inp["k_pages"].dtype == torch.uint8:   # fp8 cache: the values its codes stand for
+            k = orc.fp8_kv_values(inp["k_pages"][pages].cpu().numpy(), inp["k_scale"])
+            v = orc.fp8_kv_values(inp["v_pages"][pages].cpu().numpy(), inp["v_scale"])
+        else:
+            k = inp["k_pages"][pages].float().cpu().numpy().astype(np.float64)
+            v = inp["v_pages"][pages].float().cpu().numpy().astype(np.float64)
         return dict(q=q, k=k, v=v, row=row, L=L, B=B)
     lat = inp["latent_pages"][pages].float().cpu().numpy().astype(np.float64)
     return dict(q=q, lat=lat, row=row, L=L, B=B)
