@@ -1,7 +1,7 @@
 // plan.hip — work planning of a shard call and the exported block-table walk.
 //
 // A shard call's work is split into items: contiguous ranges of a request's local tokens
-// (the tokens its rank owns, in ascending position).  The planner runs as one workgroup:
+// (the tokens its rank owns, in ascending position).  The planner runs as one wave:
 //   1. local_b = tokens of request b on this rank (the walker's closed form); seq_len is
 //      clamped to the block table's capacity (error bit DCP_DEVERR_SEQ_LEN otherwise);
 //   2. chunk = the item size: total local tokens / target item count, rounded up to the
@@ -27,12 +27,10 @@ namespace dcp {
 
 namespace {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kBuckets = 1024;   // tile-count buckets of the dispatch order
-static_assert(kBuckets == kPlanThreads, "one bucket per thread in the bucket scan");
+constexpr int kBucketsPerLane = kBuckets / 64;
 
-// Inclusive scan inside a wave (shuffles, no LDS).
+// Inclusive scan across the 64 lanes of the wave (shuffles, no LDS).
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T x, int lane) {
 #pragma unroll
@@ -43,42 +41,19 @@ __device__ __forceinline__ T wave_incl_scan(T x, int lane) {
   return x;
 }
 
-// Exclusive scan over the workgroup: a scan inside each wave, then every thread adds the
-// totals of the waves before its own (two barriers; s_w is free again on return).
-template <typename T>
-__device__ __forceinline__ T block_excl_scan(T v, T* s_w, T& total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const T incl = wave_incl_scan(v, lane);
-  if (lane == 63) s_w[wid] = incl;
-  __syncthreads();
-  T pre = 0, tot = 0;
-#pragma unroll
-  for (int k = 0; k < kPlanWaves; ++k) {
-    const T t = s_w[k];
-    pre += k < wid ? t : T(0);
-    tot += t;
-  }
-  __syncthreads();
-  total = tot;
-  return pre + incl - v;
-}
-
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+// One wave plans the call: every reduction and scan is a shuffle, so no workgroup barrier
+// is needed (the bucket histogram lives in LDS, written and read by this wave only).
+__global__ __launch_bounds__(64) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int batch, int rank, int cp, int interleave,
     int64_t len_cap, int64_t target, int tile, int min_chunk, int32_t* __restrict__ header,
     int32_t* __restrict__ off, int4* __restrict__ items) {
-  __shared__ long long s_sum[kPlanWaves];
-  __shared__ long long s_max[kPlanWaves];
-  __shared__ int s_err[kPlanWaves];
-  __shared__ int s_w[kPlanWaves];
-  __shared__ unsigned long long s_w64[kPlanWaves];
-  __shared__ int s_hist[kBuckets];   // items per bucket, then next free position per bucket
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
-  const int per = (batch + kPlanThreads - 1) / kPlanThreads;
-  const int b0 = min(tid * per, batch);
+  __shared__ int s_hist[kBuckets];   // tail items per bucket, then next free position
+  const int lane = threadIdx.x;
+  const int per = (batch + 63) / 64;
+  const int b0 = min(lane * per, batch);
   const int b1 = min(b0 + per, batch);
-  s_hist[tid] = 0;
+#pragma unroll
+  for (int k = 0; k < kBucketsPerLane; ++k) s_hist[lane * kBucketsPerLane + k] = 0;
 
   // per-request arithmetic in 32 bits: lengths are clamped to len_cap and the host bounds
   // len_cap and interleave * cp below 2^31, so every local count, item size and item
@@ -106,27 +81,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     mx = m2 > mx ? m2 : mx;
     err |= __shfl_xor(err, o, 64);
   }
-  if (lane == 0) {
-    s_sum[wid] = sum;
-    s_max[wid] = mx;
-    s_err[wid] = err;
-  }
-  __syncthreads();
-  long long total = 0, maxloc = 0;
-  int err_all = 0;
-#pragma unroll
-  for (int k = 0; k < kPlanWaves; ++k) {
-    total += s_sum[k];
-    maxloc = s_max[k] > maxloc ? s_max[k] : maxloc;
-    err_all |= s_err[k];
-  }
 
-  // 2. item size (one 64-bit division; the result is at most the longest request rounded
-  // up to the tile)
-  long long chunk64 = (total + target - 1) / target;
+  // 2. item size (the call's one 64-bit division; the result is at most the longest
+  // request rounded up to the tile)
+  long long chunk64 = (sum + target - 1) / target;
   chunk64 = (chunk64 + tile - 1) / tile * tile;
   if (chunk64 < min_chunk) chunk64 = min_chunk;
-  const long long cap = (maxloc + tile - 1) / tile * tile;
+  const long long cap = (mx + tile - 1) / tile * tile;
   if (chunk64 > cap) chunk64 = cap;
   if (chunk64 < tile) chunk64 = tile;
   const uint32_t chunk = (uint32_t)chunk64;
@@ -144,6 +105,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     return kBuckets - 1 - (int)(nt < kBuckets - 1 ? nt : kBuckets - 1);
   };
   unsigned long long packed = 0;
+  __syncthreads();   // the histogram is cleared
   for (int b = b0; b < b1; ++b) {
     int e = 0;
     const uint32_t loc = local_of(b, e);
@@ -151,15 +113,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     packed += ((unsigned long long)(uint32_t)items_of(loc) << 32) | nf;
     if (loc - nf * chunk != 0) atomicAdd(&s_hist[bucket(loc - nf * chunk)], 1);
   }
-  unsigned long long packed_total = 0;
-  const unsigned long long pre = block_excl_scan(packed, s_w64, packed_total);
-  const int n_items = (int)(packed_total >> 32);
-  const int n_full = (int)(packed_total & 0xffffffffu);
-  // 4. tail positions: n_full + exclusive scan of the tail counts (thread = bucket)
-  int unused = 0;
-  const int first = block_excl_scan(s_hist[tid], s_w, unused);
-  s_hist[tid] = n_full + first;
-  __syncthreads();
+  const unsigned long long incl = wave_incl_scan(packed, lane);
+  const unsigned long long total =
+      __shfl(incl, 63, 64);
+  const unsigned long long pre = incl - packed;
+  const int n_items = (int)(total >> 32);
+  const int n_full = (int)(total & 0xffffffffu);
+  __syncthreads();   // the histogram is complete
+  // 4. tail positions: n_full + exclusive scan of the tail counts (lane = 16 buckets)
+  int cnt[kBucketsPerLane];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kBucketsPerLane; ++k) {
+    cnt[k] = s_hist[lane * kBucketsPerLane + k];
+    mine += cnt[k];
+  }
+  int run = n_full + wave_incl_scan(mine, lane) - mine;
+#pragma unroll
+  for (int k = 0; k < kBucketsPerLane; ++k) {
+    s_hist[lane * kBucketsPerLane + k] = run;
+    run += cnt[k];
+  }
+  __syncthreads();   // the positions are in place
   int base = (int)(pre >> 32);
   int fpos = (int)(pre & 0xffffffffu);
   for (int b = b0; b < b1; ++b) {
@@ -176,11 +151,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     base += n;
     fpos += nf;
   }
-  if (tid == 0) {
+  if (lane == 0) {
     off[batch] = n_items;
     header[1] = n_items;
     header[2] = (int32_t)chunk;
-    header[0] = err_all;
+    header[0] = err;
   }
 }
 
@@ -220,7 +195,7 @@ __global__ void clear_word_kernel(int32_t* w) { *w = 0; }
 hipError_t launch_plan(const int32_t* seq_lens, int batch, int rank, int cp, int interleave,
                        int64_t len_cap, int64_t target_items, int tile, int min_chunk,
                        const WsPtrs& ws, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch,
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, stream, seq_lens, batch,
                      rank, cp, interleave, len_cap, target_items, tile, min_chunk, ws.header,
                      ws.off, ws.items);
   return hipGetLastError();
