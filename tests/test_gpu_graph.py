@@ -1,6 +1,6 @@
 """The shard and merge entry points do no host synchronisation and allocate nothing
 themselves, so one decode step (every rank's shard call + the merge) can be captured in a
-HIP graph and replayed.  Every replay must reproduce the eager result bit for bit (the
+HIP graph and replayed (GQA, MLA at interleave 1, and multi-token GQA over an fp8 cache).  Every replay must reproduce the eager result bit for bit (the
 kernels are deterministic), with the program's own eager work and synchronisations between
 the replays.
 """
@@ -16,6 +16,8 @@ CASES = [
     wl.GQA_SHARE.with_(name="graph_gqa", batch=4, lengths=(1, 77, 1000, 5000), seed=31),
     wl.MLA_DECODE.with_(name="graph_mla_i1", batch=3, cp_size=4, interleave=1,
                         lengths=(5, 300, 2100), seed=32),
+    wl.GQA_SHARE_FP8.with_(name="graph_gqa_fp8kv_q2", batch=3, q_len=2, lengths=(3, 700, 4000),
+                           seed=33),
 ]
 
 
@@ -27,19 +29,20 @@ def test_graph_replay_matches_eager(gpu_lib, w):
     kv = inp["k_pages"] if kind == dca.GQA else inp["latent_pages"]
     v = inp["v_pages"] if kind == dca.GQA else None
     C = w.cp_size
-    b, H, Dv = w.batch, w.num_q_heads, w.head_dim_v
-    o_parts = torch.empty(C, b, H, Dv, device="cuda")
-    l_parts = torch.empty(C, b, H, device="cuda")
-    out = torch.empty(b, H, Dv, device="cuda")
-    lse = torch.empty(b, H, device="cuda")
-    ws = dca.alloc_workspace(dca.make_desc(kind, inp["q"], kv, inp["block_table"]), b,
-                             inp["max_seq_len"], C, w.interleave)
+    rows = (w.batch,) + ((w.q_len,) if w.q_len > 1 else ()) + (w.num_q_heads,)
+    o_parts = torch.empty((C,) + rows + (w.head_dim_v,), device="cuda")
+    l_parts = torch.empty((C,) + rows, device="cuda")
+    out = torch.empty(rows + (w.head_dim_v,), device="cuda")
+    lse = torch.empty(rows, device="cuda")
+    ws = dca.alloc_workspace(dca.make_desc(kind, inp["q"], kv, inp["block_table"]), w.batch,
+                             inp["max_seq_len"], C, w.interleave, q_len=w.q_len)
 
     def step():
         for r in range(C):
             dca.shard(inp["q"], kv, v, inp["block_table"], inp["seq_lens"], r, C, w.interleave,
                       w.scale, kind=kind, max_seq_len=inp["max_seq_len"], out=o_parts[r],
-                      lse=l_parts[r], workspace=ws)
+                      lse=l_parts[r], workspace=ws, k_scale=inp.get("k_scale"),
+                      v_scale=inp.get("v_scale"))
         dca.merge(o_parts, l_parts, out=out, lse_out=lse)
 
     s = torch.cuda.Stream()
