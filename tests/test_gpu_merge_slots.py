@@ -90,29 +90,46 @@ def test_slots_bit_exact_edges(gpu_lib, B, C, I, lens):
     _slots_case(bt, lens, B, nb, C, I, f"B={B} C={C} I={I}")
 
 
-def test_device_error_word(gpu_lib):
+ERR_CASES = [
+    # (workload, rank, cp_size, interleave): page-contiguous and token-granular tiles of the
+    # bf16 GQA, fp8 GQA and MLA kernels
+    (wl.GQA_SHARE.with_(batch=2, lengths=(300, 200), seed=31), 0, 1, 128),
+    (wl.GQA_SHARE.with_(batch=2, lengths=(300, 200), seed=31), 1, 2, 1),
+    (wl.GQA_SHARE_FP8.with_(batch=2, lengths=(300, 200), seed=34), 0, 1, 128),
+    (wl.GQA_SHARE_FP8.with_(batch=2, lengths=(300, 200), seed=34), 1, 2, 1),
+    (wl.MLA_DECODE.with_(batch=2, lengths=(300, 200), seed=35), 0, 1, 64),
+    (wl.MLA_DECODE.with_(batch=2, lengths=(300, 200), seed=35), 1, 2, 1),
+]
+
+
+@pytest.mark.parametrize("w,rank,cp,il", ERR_CASES,
+                         ids=["gqa", "gqa_i1", "gqa_fp8", "gqa_fp8_i1", "mla", "mla_i1"])
+def test_device_error_word(gpu_lib, w, rank, cp, il):
     """Contract violations only the device sees are flagged, never fault, and leave the
     remaining tokens' attention intact."""
-    w = wl.GQA_SHARE.with_(batch=2, lengths=(300, 200), seed=31)
+    print(f"[deverr] {w.name} rank={rank} cp={cp} il={il}", flush=True)
     inp = wl.make_inputs(w, device="cuda")
+    kind = dca.GQA if w.kind == "gqa" else dca.MLA
+    kv = inp["k_pages"] if kind == dca.GQA else inp["latent_pages"]
+    v = inp["v_pages"] if kind == dca.GQA else None
+    kw = dict(kind=kind, k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"))
     bt = inp["block_table"].clone()
     # request 1 claims more tokens than its block-table row covers
     lens = inp["seq_lens"].clone()
     lens[1] = bt.shape[1] * w.block_size + 50
-    o, l, ws = dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], bt, lens, 0, 1, 128,
-                         w.scale)
+    o, l, ws = dca.shard(inp["q"], kv, v, bt, lens, rank, cp, il, w.scale, **kw)
     assert dca.read_device_errors(ws) & dca.DEVERR_SEQ_LEN
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
-    # a block id outside the cache
+    # a block id outside the cache (logical page 1 of request 0; its other pages remain)
     bt2 = inp["block_table"].clone()
     bt2[0, 1] = 10 ** 6
-    o, l, ws = dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], bt2, inp["seq_lens"], 0, 1,
-                         128, w.scale, workspace=ws)
+    o, l, ws = dca.shard(inp["q"], kv, v, bt2, inp["seq_lens"], rank, cp, il, w.scale,
+                         workspace=ws, **kw)
     assert dca.read_device_errors(ws) & dca.DEVERR_BLOCK_ID
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
     # a clean call clears the word
-    dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"], 0,
-              1, 128, w.scale, workspace=ws)
+    dca.shard(inp["q"], kv, v, inp["block_table"], inp["seq_lens"], rank, cp, il, w.scale,
+              workspace=ws, **kw)
     assert dca.read_device_errors(ws) == 0
 
 
