@@ -9,9 +9,10 @@
 //
 // Design (the bf16 kernel's matrix-core variant, re-laid for 128-byte rows):
 //   * Four waves per (work item, KV head), two workgroups per CU; wave w takes token
-//     quarter w of every 64-token tile for all R = q_len * G query rows (one or two 16-row
-//     tiles, rows past R padding) and keeps its own online softmax; the quarters merge
-//     through LDS by the LSE identity after the last tile.
+//     quarter w of every 64-token tile for all R = q_len * G <= 32 query rows (one or two
+//     16-row tiles, rows past R padding: idle matrix lanes cost nothing in an HBM-bound
+//     kernel) and keeps its own online softmax; the quarters merge through LDS by the LSE
+//     identity after the last tile.
 //   * 64-token tiles of K and V rows (8 KiB each) are copied HBM -> LDS by
 //     global_load_lds_dwordx4 with the non-temporal policy into a double buffer, paced by
 //     each wave's vector-memory counter and a bare s_barrier (a 3-deep ring, two tiles in
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
 
 bool gqa_fp8_supported(int head_dim, int group, int q_len) {
   const int rows = group * q_len;
-  return head_dim == kD && q_len >= 1 && q_len <= kMaxQLen && rows >= 8 && rows <= 32;
+  return head_dim == kD && q_len >= 1 && q_len <= kMaxQLen && rows >= 1 && rows <= 32;
 }
 
 hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
@@ -456,7 +457,7 @@ hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
   k.po = ws.po;
   const dim3 grid((unsigned)max_items, (unsigned)a.hkv);
   const int rows = a.rows.q_len * (a.hq / a.hkv);
-  if (rows < 8 || rows > 32) return hipErrorInvalidValue;
+  if (rows < 1 || rows > 32) return hipErrorInvalidValue;
   if (rows <= 16)
     hipExtLaunchKernelGGL((gqa_fp8_kernel<1>), grid, dim3(64 * kWaves), 0, stream, ev0, ev1, 0, k);
   else
