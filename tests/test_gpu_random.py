@@ -1,0 +1,60 @@
+"""Seeded random parity sweep against the CPU oracle (GPU).
+
+Each case draws a kernel (bf16 GQA, fp32 GQA, GQA over an fp8 cache, MLA), a group size,
+KV heads, q_len, cp_size, interleave, block size and ragged lengths (with edge values:
+1, a block, a block + 1, an interleave period) from its own seed, runs every rank's shard
+and the merge, and compares them elementwise with the oracle (tolerances in
+parity_helpers).  The draws are fixed by the seeds, so a failure names its case.
+"""
+import numpy as np
+import pytest
+
+import decode_attention_context_amd as dca
+from decode_attention_context_amd import workloads as wl
+from parity_helpers import check_requests, run_shards
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    kind = ["gqa_bf16", "gqa_f32", "gqa_fp8", "mla"][seed % 4]
+    q_len = int(rng.integers(1, 5))
+    block = int(rng.choice([16, 32, 64, 128]))
+    cp = int(rng.integers(1, 9))
+    il = int(rng.choice([1, 2, 3, 16, 32, 64, 100, 128, 256]))
+    batch = int(rng.integers(1, 4))
+    edges = [1, block, block + 1, il * cp, il * cp + 1]
+    lengths = tuple(int(rng.choice(edges)) if rng.random() < 0.3 else int(rng.integers(1, 2500))
+                    for _ in range(batch))
+    if kind == "mla":
+        return wl.MLA_DECODE.with_(name=f"rand{seed}_mla", batch=batch, q_len=q_len,
+                                   block_size=block, cp_size=cp, interleave=il,
+                                   lengths=lengths, seed=seed)
+    hkv = int(rng.choice([1, 2]))
+    groups = [1, 2, 4, 8, 16]
+    if kind == "gqa_fp8":
+        groups = [g for g in groups if g * q_len <= 32]
+    g = int(rng.choice(groups))
+    base = wl.TINY_GQA if kind == "gqa_f32" else (wl.GQA_SHARE_FP8 if kind == "gqa_fp8"
+                                                   else wl.GQA_SHARE)
+    return base.with_(name=f"rand{seed}_{kind}", batch=batch, q_len=q_len,
+                      num_q_heads=g * hkv, num_kv_heads=hkv, block_size=block, cp_size=cp,
+                      interleave=il, lengths=lengths, seed=seed)
+
+
+SEEDS = list(range(2000, 2048))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_case(gpu_lib, seed):
+    w = _draw(seed)
+    print(f"[rand] {w.name}: q_len={w.q_len} batch={w.batch} Hq={w.num_q_heads} "
+          f"Hkv={w.num_kv_heads} C={w.cp_size} I={w.interleave} B={w.block_size} "
+          f"lengths={w.lengths}", flush=True)
+    inp = wl.make_inputs(w, device="cuda")
+    kind = dca.GQA if w.kind == "gqa" else dca.MLA
+    o_parts, l_parts = run_shards(inp, kind, w.cp_size, w.interleave, w.scale)
+    o_m, l_m = dca.merge(o_parts, l_parts)
+    check_requests(inp, kind, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
+                   list(range(w.batch)), w.name)
