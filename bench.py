@@ -36,6 +36,17 @@ def _src_hash(name):
     return h.hexdigest()[:16]
 
 
+def gqa_kernel_name(w):
+    """The GQA shard kernel variant the library launches for workload w."""
+    rows = w.q_len * (w.num_q_heads // w.num_kv_heads)
+    rt = 1 if rows <= 16 else 2
+    if w.kv_dtype == "fp8":
+        return f"gqa_fp8_kernel<RT={rt}>"
+    if w.dtype == "bf16" and 8 <= rows <= 32:
+        return f"gqa_shard_kernel<bf16, matrix cores, RT={rt}>"
+    return f"gqa_shard_kernel<{w.dtype}, vector ALUs, {rows} rows>"
+
+
 def owned_tokens_count(L, rank, cp, il):
     """Tokens of an L-token sequence stored by `rank` (the library's host walker)."""
     import decode_attention_context_amd as dca
@@ -266,7 +277,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "gqa_fp8_kernel<RT=1>" if fp8 else "gqa_shard_kernel<bf16,NW=4,mfma>",
+                "kernel": gqa_kernel_name(w),
                 "algorithmic_bytes_per_launch": int(bytes_avg),
                 "avg_launch_us": round(dur_s * 1e6, 2)}
         kernel_name = "gqa_shard"
