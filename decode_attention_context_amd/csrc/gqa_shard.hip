@@ -127,7 +127,7 @@ __device__ __forceinline__ int v_swz_t(int r) {
 constexpr int waves_for(int r) { return r >= 8 ? 8 : (r > 4 ? 8 : (r > 2 ? 4 : r)); }
 constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r); }
 
-// kMfma: the matrix-core variant for 8 <= R <= 32 query rows per KV head, bf16 only: four
+// kMfma: the matrix-core variant for R <= 32 query rows per KV head, bf16 only: four
 // waves, HPW = 16-row tiles per wave (rows past R are padding).  Wave w takes token quarter
 // w of every tile for all rows and keeps its own online softmax over those tokens:
 //   * S^T (16 tokens x 16 rows) = K (16 x 128) . Q^T on v_mfma_f32_16x16x32_bf16, the K
@@ -745,15 +745,17 @@ void launch_m(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEve
 }
 
 // R = q_len * G query rows per KV head; rows sharing a (waves, rows per wave) shape share
-// the kernel.  bf16 with 8 to 32 rows runs the group's products on the matrix cores (one
-// 16-row tile holds 8 rows at G = 8 with half of it idle): the per-token work, 4 R D flops
-// against 4 D bytes of K and V, then stays off the vector ALUs, which at R = 8 no longer
-// hid entirely under the HBM -> LDS stream and at R >= 16 became the bound.
+// the kernel.  bf16 with up to 32 rows runs the group's products on the matrix cores (rows
+// past R pad the 16-row tile): the per-token work, 4 R D flops against 4 D bytes of K and
+// V, then stays off the vector ALUs, which did not hide entirely under the HBM -> LDS
+// stream at R = 1..8 (measured at the share's shape: 73-76% of HBM peak on the vector ALUs
+// against 79-82% on the matrix cores) and became the bound at R >= 16.  fp32, and bf16
+// with 48 or 64 rows, stay on the vector ALUs.
 template <bool kBf16>
 hipError_t launch_g(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
                     hipEvent_t e1) {
   if constexpr (kBf16) {
-    if (rows >= 8 && rows <= 32) {
+    if (rows >= 1 && rows <= 32) {
       if (rows <= 16) launch_m<1>(k, grid, s, e0, e1);
       else launch_m<2>(k, grid, s, e0, e1);
       return hipGetLastError();
