@@ -323,6 +323,7 @@ def main():
         line["secondary_ragged"] = secondary_ragged(dca, wl, torch)
         line["secondary_long"] = secondary_long(dca, wl, torch)
         line["secondary_fp8kv"] = secondary_fp8kv(dca, wl, torch)
+        line["secondary_tiny"] = secondary_tiny(dca, wl, torch)
         line["secondary_multi_token"] = secondary_multi_token(dca, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
@@ -532,6 +533,35 @@ def secondary_ragged(dca, wl, torch, steps=5):
             "merge8_bf16_partials_gbs": round(merge16_bytes / merge16_s / 1e9, 1),
             "step_ms": round(step_s * 1e3, 3),
             "kv_tokens_per_s": round(int(lens.sum()) / step_s, 1)}
+
+
+def secondary_tiny(dca, wl, torch, steps=200):
+    """The tiny fp32 case (1 request x 1024 tokens, 8 query heads on 2 KV heads, D 64,
+    C = 2, I = 16): latency-bound, so reported as latency: the graph-replayed step (both
+    shard calls + the merge) and each shard kernel's own duration."""
+    w = wl.TINY_GQA
+    inp = wl.make_inputs(w, device="cuda")
+    step, shard_ev, merge_ev, ws = run_step_fns(dca, w, inp, dca.GQA)
+    for _ in range(5):
+        step(False)
+    for _ in range(20):
+        step(True)
+    torch.cuda.synchronize()
+    assert dca.read_device_errors(ws) == 0
+    shard_us = sorted(a.elapsed_time(b) for a, b in shard_ev)[len(shard_ev) // 2] * 1e3
+    merge_us = sorted(a.elapsed_time(b) for a, b in merge_ev)[len(merge_ev) // 2] * 1e3
+    graph = capture_step(torch, step)
+    for _ in range(10):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    step_us = (time.perf_counter() - t0) / steps * 1e6
+    del inp, graph
+    return {"workload": w.name, "step_us": round(step_us, 2),
+            "shard_kernel_us_median": round(shard_us, 2), "merge_us_median": round(merge_us, 2)}
 
 
 def secondary_fp8kv(dca, wl, torch):

@@ -72,7 +72,7 @@ bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
     p->tile = dcp::kGqaTile;
     // two resident workgroups (64 KiB double buffer each) per CU and KV head, one round
     p->target = std::max<int64_t>(1, (int64_t)cus * 2 / d->num_kv_heads);
-    p->min_chunk = 4 * dcp::kGqaTile;
+    p->min_chunk = dcp::kGqaTile;
   } else {
     // two head-group workgroups per item, one resident workgroup per CU (144 KiB of LDS)
     p->tile = dcp::kMlaTile;
