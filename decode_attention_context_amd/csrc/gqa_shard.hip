@@ -8,8 +8,10 @@
 // into exact attention.
 //
 // The work is HBM-bound (per token and KV head: 2 * D * sizeof(T) bytes against
-// 4 * G * D flops), so the design is about keeping K / V bytes streaming at full rate and
-// the vector-ALU work per byte small:
+// 4 * R * D flops for R query rows), so the design is about keeping K / V bytes streaming
+// at full rate.  Two variants share the copy machinery below: bf16 with R <= 32 computes
+// both products on the matrix cores (the kMfma variant, described at the kernel); fp32,
+// and bf16 with more rows, stay on the vector ALUs as follows:
 //   * One workgroup of NW <= 8 waves per work item (request, KV head, local token range),
 //     two workgroups per CU; wave w owns HPW of the R = q_len * G query rows that share the
 //     KV head (q_len query positions per request, see below).
