@@ -31,7 +31,7 @@ def _draw(seed):
         return wl.MLA_DECODE.with_(name=f"rand{seed}_mla", batch=batch, q_len=q_len,
                                    block_size=block, cp_size=cp, interleave=il,
                                    lengths=lengths, seed=seed)
-    hkv = int(rng.choice([1, 2]))
+    hkv = int(rng.choice([1, 2, 4]))
     groups = [1, 2, 4, 8, 16]
     if kind == "gqa_fp8":
         groups = [g for g in groups if g * q_len <= 32]
