@@ -42,7 +42,7 @@ def gqa_kernel_name(w):
     rt = 1 if rows <= 16 else 2
     if w.kv_dtype == "fp8":
         return f"gqa_fp8_kernel<RT={rt}>"
-    if w.dtype == "bf16" and rows <= 32:
+    if w.dtype == "bf16":
         return f"gqa_shard_kernel<bf16, matrix cores, RT={rt}>"
     return f"gqa_shard_kernel<{w.dtype}, vector ALUs, {rows} rows>"
 

@@ -70,8 +70,12 @@ bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
   if (cus <= 0) return false;
   if (d->kind == DCP_GQA) {
     p->tile = dcp::kGqaTile;
-    // two resident workgroups (64 KiB double buffer each) per CU and KV head, one round
-    p->target = std::max<int64_t>(1, (int64_t)cus * 2 / d->num_kv_heads);
+    // two resident workgroups (64 KiB double buffer each) per CU and KV head, one round;
+    // bf16 queries with more than 32 rows per KV head take two workgroups (32-row slices)
+    // per item and KV head, so half the items
+    const int rows = q_len * (d->num_q_heads / d->num_kv_heads);
+    const int slices = (d->dtype == DCP_BF16 && rows > 32) ? 2 : 1;
+    p->target = std::max<int64_t>(1, (int64_t)cus * 2 / (d->num_kv_heads * slices));
     p->min_chunk = dcp::kGqaTile;
   } else {
     // two head-group workgroups per item, one resident workgroup per CU (144 KiB of LDS)

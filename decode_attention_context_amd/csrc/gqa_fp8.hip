@@ -8,11 +8,11 @@
 // variant, half the bytes per token of bf16.
 //
 // Design (the bf16 kernel's matrix-core variant, re-laid for 128-byte rows):
-//   * Four waves per (work item, KV head), two workgroups per CU; wave w takes token
-//     quarter w of every 64-token tile for all R = q_len * G <= 32 query rows (one or two
-//     16-row tiles, rows past R padding: idle matrix lanes cost nothing in an HBM-bound
-//     kernel) and keeps its own online softmax; the quarters merge through LDS by the LSE
-//     identity after the last tile.
+//   * Four waves per (work item, KV head, slice of 32 of the R = q_len * G <= 64 query
+//     rows), two workgroups per CU; wave w takes token quarter w of every 64-token tile for
+//     all rows of the slice (one or two 16-row tiles, rows past R padding: idle matrix
+//     lanes cost nothing in an HBM-bound kernel) and keeps its own online softmax; the
+//     quarters merge through LDS by the LSE identity after the last tile.
 //   * 64-token tiles of K and V rows (8 KiB each) are copied HBM -> LDS by
 //     global_load_lds_dwordx4 with the non-temporal policy into a double buffer, paced by
 //     each wave's vector-memory counter and a bare s_barrier (a 3-deep ring, two tiles in
@@ -106,7 +106,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
   const int4 it = a.items[blockIdx.x];   // in dispatch order, longest first
   const int b = it.x, j0 = it.y, j1 = it.z;
   const int item = it.w;
-  const int kvh = blockIdx.y;
+  // blockIdx.y = KV head + hkv * (32-row slice); the slices of one item share its K / V
+  // tiles (a later slice's reads mostly hit L2)
+  const int kvh = (int)blockIdx.y % a.hkv;
+  const int rbase = 32 * ((int)blockIdx.y / a.hkv);   // first query row of the slice
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   const int G = a.hq / a.hkv;
   const int R = a.q_len * G;
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
   bf16x8 qop[RT][4];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int rho = min(16 * r + i16, R - 1);
+    const int rho = min(rbase + 16 * r + i16, R - 1);
     const int qi = rho / G;
     const int qrow = qi * a.hq + kvh * G + (rho - qi * G);
     lim_l[r] = a.q_len == 1 ? j1
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
   const int d0 = 32 * tq + 8 * (lane & 3);
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int row = 16 * r + (lane >> 2);
+    const int row = 16 * r + (lane >> 2);   // in the slice; rbase + row in the request
     float mk[4];
     float M = neg_inf();
 #pragma unroll
@@ -392,9 +395,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
     }
     const float inv = L > 0.f ? a.v_scale / L : 0.f;
     const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
-    if (row < R) {
-      const int qi_o = row / G;
-      const int orow = qi_o * a.hq + kvh * G + (row - qi_o * G);
+    if (rbase + row < R) {
+      const int qi_o = (rbase + row) / G;
+      const int orow = qi_o * a.hq + kvh * G + (rbase + row - qi_o * G);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] *= inv;
       if (single && a.o_bf16) {
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
 
 bool gqa_fp8_supported(int head_dim, int group, int q_len) {
   const int rows = group * q_len;
-  return head_dim == kD && q_len >= 1 && q_len <= kMaxQLen && rows >= 1 && rows <= 32;
+  return head_dim == kD && q_len >= 1 && q_len <= kMaxQLen && rows >= 1 && rows <= 64;
 }
 
 hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
@@ -455,9 +458,9 @@ hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
   k.items = ws.items;
   k.plse = ws.plse;
   k.po = ws.po;
-  const dim3 grid((unsigned)max_items, (unsigned)a.hkv);
   const int rows = a.rows.q_len * (a.hq / a.hkv);
-  if (rows < 1 || rows > 32) return hipErrorInvalidValue;
+  if (rows < 1 || rows > 64) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)max_items, (unsigned)(a.hkv * ((rows + 31) / 32)));
   if (rows <= 16)
     hipExtLaunchKernelGGL((gqa_fp8_kernel<1>), grid, dim3(64 * kWaves), 0, stream, ev0, ev1, 0, k);
   else

@@ -129,8 +129,9 @@ __device__ __forceinline__ int v_swz_t(int r) {
 constexpr int waves_for(int r) { return r >= 8 ? 8 : (r > 4 ? 8 : (r > 2 ? 4 : r)); }
 constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r); }
 
-// kMfma: the matrix-core variant for R <= 32 query rows per KV head, bf16 only: four
-// waves, HPW = 16-row tiles per wave (rows past R are padding).  Wave w takes token quarter
+// kMfma: the matrix-core variant, bf16 only: four waves, HPW = 16-row tiles per wave (rows
+// past R are padding); a workgroup takes a slice of 32 of the R query rows (R > 32: two
+// workgroups per item and KV head).  Wave w takes token quarter
 // w of every tile for all rows and keeps its own online softmax over those tokens:
 //   * S^T (16 tokens x 16 rows) = K (16 x 128) . Q^T on v_mfma_f32_16x16x32_bf16, the K
 //     operand (lane = token, 8 dims) read straight from the 4-row K blocks and the query
@@ -166,7 +167,10 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
   const int4 it = a.items[blockIdx.x];   // in dispatch order, longest first
   const int b = it.x, j0 = it.y, j1 = it.z;
   const int item = it.w;                 // index of the item's partial
-  const int kvh = blockIdx.y;
+  // matrix-core variant: blockIdx.y = KV head + hkv * (32-row slice); the slices of one
+  // item share its K / V tiles (a later slice's reads mostly hit L2)
+  const int kvh = kMfma ? (int)blockIdx.y % a.hkv : (int)blockIdx.y;
+  const int rbase = kMfma ? 32 * ((int)blockIdx.y / a.hkv) : 0;   // first row of the slice
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   // The wave's query rows (wave-uniform): row rho = w * HPW + h of the R = q_len * G rows
   // of this KV head is query position qi = rho / G, head kvh * G + rho % G, request row
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
     bf16x8 qop[RT][4];   // query operand of the 4 k-steps: dims 32 ks + 8 g .. + 7
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int rho = min(16 * r + i16, R - 1);
+      const int rho = min(rbase + 16 * r + i16, R - 1);
       const int qi = rho / G;
       const int qrow = qi * a.hq + kvh * G + (rho - qi * G);
       lim_l[r] = a.q_len == 1 ? j1
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
     const int d0 = 32 * tq + 8 * (lane & 3);
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int row = 16 * r + (lane >> 2);
+      const int row = 16 * r + (lane >> 2);   // in the slice; rbase + row in the request
       float mk[4];
       float M = neg_inf();
 #pragma unroll
@@ -490,9 +494,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
       }
       const float inv = L > 0.f ? 1.f / L : 0.f;
       const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
-      if (row < R) {
-        const int qi_o = row / G;
-        const int orow = qi_o * a.hq + kvh * G + (row - qi_o * G);
+      if (rbase + row < R) {
+        const int qi_o = (rbase + row) / G;
+        const int orow = qi_o * a.hq + kvh * G + (rbase + row - qi_o * G);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] *= inv;
         if (single && a.o_bf16) {
@@ -739,27 +743,31 @@ void launch_r(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEve
                         0, k);
 }
 
-// Matrix-core variant: four waves, RT 16-row tiles per wave.
+// Matrix-core variant: four waves, RT 16-row tiles per wave, one workgroup per (item, KV
+// head, slice of 32 rows).
 template <int RT>
-void launch_m(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  hipExtLaunchKernelGGL((gqa_shard_kernel<true, 4, RT, true>), grid, dim3(256), 0, s, e0, e1,
-                        0, k);
+void launch_m(const GqaKArgs& k, dim3 grid, int slices, hipStream_t s, hipEvent_t e0,
+              hipEvent_t e1) {
+  const dim3 g(grid.x, grid.y * (unsigned)slices);
+  hipExtLaunchKernelGGL((gqa_shard_kernel<true, 4, RT, true>), g, dim3(256), 0, s, e0, e1, 0,
+                        k);
 }
 
 // R = q_len * G query rows per KV head; rows sharing a (waves, rows per wave) shape share
-// the kernel.  bf16 with up to 32 rows runs the group's products on the matrix cores (rows
-// past R pad the 16-row tile): the per-token work, 4 R D flops against 4 D bytes of K and
+// the kernel.  bf16 runs the group's products on the matrix cores (rows past R pad the
+// 16-row tile; more than 32 rows take two workgroups of 32 rows each): the per-token work, 4 R D flops against 4 D bytes of K and
 // V, then stays off the vector ALUs, which did not hide entirely under the HBM -> LDS
 // stream at R = 1..8 (measured at the share's shape: 73-76% of HBM peak on the vector ALUs
-// against 79-82% on the matrix cores) and became the bound at R >= 16.  fp32, and bf16
-// with 48 or 64 rows, stay on the vector ALUs.
+// against 79-82% on the matrix cores) and became the bound at R >= 16 (48 / 64 rows at
+// the share's shape: 13% / 10% of HBM peak on the vector ALUs).  fp32 stays on the vector
+// ALUs.
 template <bool kBf16>
 hipError_t launch_g(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
                     hipEvent_t e1) {
   if constexpr (kBf16) {
-    if (rows >= 1 && rows <= 32) {
-      if (rows <= 16) launch_m<1>(k, grid, s, e0, e1);
-      else launch_m<2>(k, grid, s, e0, e1);
+    if (rows >= 1 && rows <= 64) {
+      if (rows <= 16) launch_m<1>(k, grid, 1, s, e0, e1);
+      else launch_m<2>(k, grid, (rows + 31) / 32, s, e0, e1);
       return hipGetLastError();
     }
   }

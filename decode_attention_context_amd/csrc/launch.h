@@ -57,7 +57,7 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
 bool gqa_supported(int dtype, int head_dim, int group, int q_len);
 
 // fp8 KV cache (OCP FP8 E4M3 codes, one float32 scale per tensor; bf16 queries): the same
-// shard with K / V values decode(code) * scale.  Supported for head_dim 128 and up to 32
+// shard with K / V values decode(code) * scale.  Supported for head_dim 128 and up to 64
 // query rows (q_len * group) per KV head.
 hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
                                 int64_t max_items, const WsPtrs& ws, void* o_out,

@@ -187,7 +187,7 @@ int dcp_attn_shard_ex(const dcp_attn_desc* desc, int q_len, int o_dtype, const v
  * bits with bias 7, 3 mantissa bits; exponent 0 subnormal; S.1111.111 NaN, no infinities),
  * [num_blocks][num_kv_heads][block_size][head_dim], 16-byte aligned; the cached key / value
  * is decode(code) * k_scale / v_scale (finite floats).  desc->kind = DCP_GQA and
- * desc->dtype = DCP_BF16 describe the bf16 queries; head_dim 128 and up to 32 query rows
+ * desc->dtype = DCP_BF16 describe the bf16 queries; head_dim 128 and up to 64 query rows
  * (q_len * num_q_heads / num_kv_heads) per KV head are supported, other shapes return
  * DCP_EUNSUPPORTED without launching.  Scores are scale * q . k; everything else (q_len,
  * o_dtype, outputs, workspace from dcp_workspace_size_mq with the same desc, events,

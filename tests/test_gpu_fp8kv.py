@@ -4,8 +4,8 @@ K and V pages hold OCP FP8 E4M3 codes with one scale each; the oracle attends ov
 values decode(code) * scale in float64 (its fp8 reading, pinned on the CPU).  Every rank's
 partial and the merged output are compared elementwise with the bf16-input tolerance (the
 queries are bf16 and every fp8 value is exact in bf16).  Cases: page-contiguous and
-token-granular tiles, one and two 16-row tiles per wave (1, 2, 4, 8, 16, 24 and 32 query
-rows per KV head, multi-token decode), two KV heads, ragged and empty shards, the full-size GQA share
+token-granular tiles, one and two 16-row tiles per wave (1, 2, 4, 8, 16, 24, 32, 48 and
+64 query rows per KV head, multi-token decode), two KV heads, ragged and empty shards, the full-size GQA share
 on sampled requests, bf16 partial outputs, and the shapes the call rejects.
 """
 import pytest
@@ -34,6 +34,10 @@ CASES = [
             interleave=3, lengths=(7, 1100), seed=109),
     F.with_(name="fp8_g4_c4", batch=3, num_q_heads=8, num_kv_heads=2, cp_size=4, interleave=64,
             block_size=64, lengths=(1, 300, 2600), seed=110),
+    # 48 and 64 rows per KV head: two 32-row slices
+    F.with_(name="fp8_g16_q4", batch=2, q_len=4, num_q_heads=16, lengths=(3, 2000), seed=111),
+    F.with_(name="fp8_g16_q3_h2_i3", batch=2, q_len=3, num_q_heads=32, num_kv_heads=2,
+            block_size=16, interleave=3, lengths=(40, 900), seed=112),
 ]
 
 
@@ -78,9 +82,9 @@ def test_fp8kv_bf16_partials(gpu_lib):
 
 
 def test_fp8kv_rejects_unsupported(gpu_lib):
-    """More than 32 query rows per KV head (G = 16 at q_len 4), float32 queries, missing
-    scales: refused before any launch."""
-    w = F.with_(name="fp8_g16_q4", batch=1, q_len=4, num_q_heads=16, lengths=(100,), seed=107)
+    """A group of 32 query heads per KV head, float32 queries, missing scales: refused
+    before any launch."""
+    w = F.with_(name="fp8_g32", batch=1, num_q_heads=32, lengths=(100,), seed=107)
     inp = wl.make_inputs(w, device="cuda")
     with pytest.raises(dca.DCPError):
         dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"],

@@ -34,7 +34,7 @@ def _draw(seed):
     hkv = int(rng.choice([1, 2, 4]))
     groups = [1, 2, 4, 8, 16]
     if kind == "gqa_fp8":
-        groups = [g for g in groups if g * q_len <= 32]
+        groups = [g for g in groups if g * q_len <= 64]
     g = int(rng.choice(groups))
     base = wl.TINY_GQA if kind == "gqa_f32" else (wl.GQA_SHARE_FP8 if kind == "gqa_fp8"
                                                    else wl.GQA_SHARE)
