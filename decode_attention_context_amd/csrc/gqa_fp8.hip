@@ -110,6 +110,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
   // tiles (a later slice's reads mostly hit L2)
   const int kvh = (int)blockIdx.y % a.hkv;
   const int rbase = 32 * ((int)blockIdx.y / a.hkv);   // first query row of the slice
+  // K / V copies stream with the non-temporal policy, except when two slices read the same
+  // tiles: the second then finds them in L2
+  const bool nt = a.q_len * (a.hq / a.hkv) <= 32;
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   const int G = a.hq / a.hkv;
   const int R = a.q_len * G;
@@ -174,7 +177,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
       for (int k = 0; k < kDmaPerWave; ++k) {
         const uint32_t voff = (uint32_t)slot_row[k] < lim ? (uint32_t)slot_row[k] * kRow + slot_src[k]
                                                           : slot_src[k];
-        copy16_sbase<true>(dst + slot_dst[k], voff, slot_base(k) + rb);
+        if (nt) copy16_sbase<true>(dst + slot_dst[k], voff, slot_base(k) + rb);
+        else copy16_sbase<false>(dst + slot_dst[k], voff, slot_base(k) + rb);
       }
       return ok ? (nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1)) : 0ull;
     }
@@ -198,7 +202,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
       const uint32_t rr = __shfl(row, slot_row[k], 64);
-      copy16_vaddr<true>(dst + slot_dst[k], slot_base(k) + (size_t)rr * kRow + slot_src[k]);
+      const char* src = slot_base(k) + (size_t)rr * kRow + slot_src[k];
+      if (nt) copy16_vaddr<true>(dst + slot_dst[k], src);
+      else copy16_vaddr<false>(dst + slot_dst[k], src);
     }
     return __ballot(ok);
   };

@@ -171,6 +171,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
   // item share its K / V tiles (a later slice's reads mostly hit L2)
   const int kvh = kMfma ? (int)blockIdx.y % a.hkv : (int)blockIdx.y;
   const int rbase = kMfma ? 32 * ((int)blockIdx.y / a.hkv) : 0;   // first row of the slice
+  // K / V copies stream with the non-temporal policy, except when two slices read the same
+  // tiles: the second then finds them in L2
+  const bool nt = !(kMfma && a.q_len * (a.hq / a.hkv) > 32);
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   // The wave's query rows (wave-uniform): row rho = w * HPW + h of the R = q_len * G rows
   // of this KV head is query position qi = rho / G, head kvh * G + rho % G, request row
@@ -285,7 +288,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
     const uint32_t voff = (uint32_t)slot_row[k] < ts.lim
                               ? (uint32_t)slot_row[k] * kRowBytes + slot_src[k]
                               : slot_src[k];
-    copy16_sbase<true>(ts.dst + slot_dst[k], voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
+    if (nt) copy16_sbase<true>(ts.dst + slot_dst[k], voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
+    else copy16_sbase<false>(ts.dst + slot_dst[k], voff, (sl < 16 ? a.kp : a.vp) + ts.rb);
   };
   // ---- all of this wave's HBM -> LDS copies of tile ti; returns the mask of valid tokens
   auto issue_tile = [&](int ti) -> uint64_t {
@@ -318,8 +322,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
     for (int k = 0; k < kDmaPerWave; ++k) {
       const int sl = w * kDmaPerWave + k;
       const uint32_t rr = __shfl(row, slot_row[k], 64);
-      copy16_vaddr<true>(dst + slot_dst[k],
-                   (sl < 16 ? a.kp : a.vp) + (size_t)rr * kRowBytes + slot_src[k]);
+      const char* src = (sl < 16 ? a.kp : a.vp) + (size_t)rr * kRowBytes + slot_src[k];
+      if (nt) copy16_vaddr<true>(dst + slot_dst[k], src);
+      else copy16_vaddr<false>(dst + slot_dst[k], src);
     }
     return __ballot(ok);
   };
