@@ -44,7 +44,7 @@ def gqa_kernel_name(w):
         return f"gqa_fp8_kernel<RT={rt}>"
     if w.dtype == "bf16":
         return f"gqa_shard_kernel<bf16, matrix cores, RT={rt}>"
-    return f"gqa_shard_kernel<{w.dtype}, vector ALUs, {rows} rows>"
+    return f"gqa_shard_kernel<f32, vector ALUs, {rows} rows>"
 
 
 def owned_tokens_count(L, rank, cp, il):

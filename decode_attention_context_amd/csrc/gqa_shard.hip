@@ -9,9 +9,9 @@
 //
 // The work is HBM-bound (per token and KV head: 2 * D * sizeof(T) bytes against
 // 4 * R * D flops for R query rows), so the design is about keeping K / V bytes streaming
-// at full rate.  Two variants share the copy machinery below: bf16 with R <= 32 computes
-// both products on the matrix cores (the kMfma variant, described at the kernel); fp32,
-// and bf16 with more rows, stay on the vector ALUs as follows:
+// at full rate.  Two variants share the copy machinery below: bf16 (R <= 64 query rows per
+// KV head) computes both products on the matrix cores (the kMfma variant, described at the
+// kernel); f32 stays on the vector ALUs as follows:
 //   * One workgroup of NW <= 8 waves per work item (request, KV head, local token range),
 //     two workgroups per CU; wave w owns HPW of the R = q_len * G query rows that share the
 //     KV head (q_len query positions per request, see below).
@@ -27,19 +27,15 @@
 //   * K rows sit in 4-row blocks, chunk-major inside a block, the blocks 1088 bytes apart:
 //     a lane's row is a base address plus immediate offsets, and the rows that one LDS read
 //     serves fall in distinct bank groups.
-//   * Scores: lane = token.  The lane pulls its K row from LDS in two halves; each query
-//     head, being wave-uniform, sits in scalar registers (loaded once when a wave owns one
-//     head, streamed in 16-dword chunks otherwise) and is the scalar operand of
-//     v_dot2_f32_bf16 (bf16) or v_fma_f32 (f32): no cross-lane reduction.
+//   * Scores: lane = token.  The lane pulls its whole K row from LDS into registers; each
+//     query head, being wave-uniform, sits in scalar registers (loaded once when a wave owns
+//     one head, streamed in 16-dword chunks otherwise) and is the scalar operand of
+//     v_fma_f32: no cross-lane reduction.
 //   * Online softmax in base 2 (scale * log2 e folded into the scores).  The tile max per
 //     head is v_max_f32 with DPP operands (row butterfly, then row broadcasts into the last
 //     lane) read into a scalar; running sums stay per lane and are reduced once per item.
-//   * P.V (bf16): lane = (16-lane group, lane in group) owns two head dims; one transposed
-//     LDS read (ds_read_b64_tr_b16) gives it one dim of four consecutive tokens, i.e. two
-//     token pairs that v_dot2_f32_bf16 combines with the bf16-rounded weight pairs, which
-//     arrive wave-uniform, four pairs per LDS read.  V chunks are XOR-swizzled by bits of
-//     the row so that the transposed reads are conflict free.  f32: lane = (token group,
-//     16-byte chunk of the V row), the four token groups summed across rows once per item.
+//   * P.V: lane = (token group, 16-byte chunk of the V row), the weights going through LDS;
+//     the four token groups are summed across rows once per item.
 //   * An item that covers a request's whole shard writes (O, lse) directly; otherwise it
 //     writes a normalized partial that the split combine merges.
 //   * Multi-token decode (q_len > 1: speculative decoding or multi-token prediction, the
@@ -102,27 +98,19 @@ struct GqaKArgs {
   float* po;
 };
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-
 __device__ __forceinline__ u32x2 lds_tr16(const char DCP_LDS* p) {
   const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 DCP_LDS*)p);
   return __builtin_bit_cast(u32x2, v);
 }
 
-// V rows are stored with their 16-byte chunks XOR-swizzled by bits of the row, so that the
-// four rows of a transposed read (bf16) fall in distinct LDS banks.  f32 V rows are read
-// row-wise and stored as they are.  The matrix-core kernel's transposed reads take 8
-// consecutive rows at one pair of chunks across two 16-lane groups: its swizzle moves the
-// chunk pair by the row's low three bits, so the 8 rows land in 8 distinct 32-byte slots.
-template <bool kBf16, bool kMfma = false>
+// V rows of the matrix-core kernel are stored with their 16-byte chunks XOR-swizzled by
+// the row: its transposed reads take 8 consecutive rows at one pair of chunks across two
+// 16-lane groups, and moving the chunk pair by the row's low three bits puts the 8 rows in 8
+// distinct 32-byte slots.  f32 V rows are read row-wise and stored as they are.
+template <bool kMfma>
 __device__ __forceinline__ int v_swz_t(int r) {
-  if constexpr (kMfma) return (r & 7) << 1;
-  return kBf16 ? (((r & 1) << 1) | ((r & 2) << 2)) : 0;
+  return kMfma ? (r & 7) << 1 : 0;
 }
-
 
 // Waves and rows per wave for R query rows per KV head: up to 8 waves, rows dealt evenly;
 // rows past R (when the waves do not divide R) repeat the last row and are not written.
@@ -147,18 +135,17 @@ constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r
 //     lane under a wave-uniform branch;
 //   * after the last tile the four token quarters of each row merge through LDS by the LSE
 //     identity (weights exp2(m_k - max m), empty quarters weight 0).
-template <bool kBf16, int NW, int HPW, bool kMfma = false>
+template <bool kBf16, int NW, int HPW>
 __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
-  static_assert(!kMfma || (kBf16 && NW == 4), "matrix-core variant: bf16, four waves");
+  constexpr bool kMfma = kBf16;   // bf16 runs on the matrix cores, f32 on the vector ALUs
+  static_assert(!kMfma || NW == 4, "matrix-core variant: four waves");
   constexpr int kElemBytes = kBf16 ? 2 : 4;
   constexpr int D = kRowBytes / kElemBytes;     // head dim
-  constexpr int NA = kBf16 ? 2 : 4;             // dims (accumulators) per lane per head
   constexpr int kDmaPerWave = kSlots / NW;
-  constexpr int kPWords = kBf16 ? kTile / 2 : kTile;  // weight words per head per tile
 
   // [buffer][K blocks | V rows]
   __shared__ u32x4 kvs[kNBuf * kBufBytes / 16];
-  __shared__ uint32_t pbuf[kMfma ? 1 : NW][HPW][kMfma ? 1 : kPWords];
+  __shared__ uint32_t pbuf[kMfma ? 1 : NW][HPW][kMfma ? 1 : kTile];   // f32 weights
   __shared__ float mls[kMfma ? NW * 16 * HPW * 2 : 1];   // matrix-core variant: (m, l) per row
 
   const int lane = threadIdx.x & 63;
@@ -208,17 +195,6 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
   const char DCP_LDS* kvb = (const char DCP_LDS*)&kvs[0];
   const uint32_t lds_addr = (uint32_t)(uintptr_t)kvb;
 
-  // running max (log2 units), -m (0 while m is -inf), per-lane share of the running sum
-  float m[HPW], negm[HPW], ls[HPW], acc[HPW][NA];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    m[h] = neg_inf();
-    negm[h] = 0.f;
-    ls[h] = 0.f;
-#pragma unroll
-    for (int k = 0; k < NA; ++k) acc[h][k] = 0.f;
-  }
-
   // ---- copy slots of this wave: slot s = w * kDmaPerWave + k, one 1-KiB copy each.
   // s < 16: the K block of rows 4 s .. 4 s + 3, lane l bringing chunk l / 4 of row
   // 4 s + l % 4.  s >= 16: V 16-byte positions q = (s - 16) * 64 + lane, row q / 16, holding
@@ -237,7 +213,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
       const int q = (sl - 16) * 64 + lane;
       const int r = q / kChunks, pc = q % kChunks;
       slot_row[k] = r;
-      slot_src[k] = (uint32_t)((pc ^ v_swz_t<kBf16, kMfma>(r)) * 16);
+      slot_src[k] = (uint32_t)((pc ^ v_swz_t<kMfma>(r)) * 16);
       slot_dst[k] = (uint32_t)(kKBytes + (sl - 16) * 1024);
     }
     slot_dst[k] = __builtin_amdgcn_readfirstlane(slot_dst[k]);   // M0 operand: keep it scalar
@@ -523,159 +499,128 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
         }
       }
     }
-    return;
-  }
-
-  // query of a single head per wave: loaded once into scalar registers
-  constexpr bool kQResident = HPW == 1;
-  u32x16 qres[kChunks / 4];
-  if constexpr (kQResident) {
-#pragma unroll
-    for (int c = 0; c < kChunks / 4; ++c)
-      qres[c] = *reinterpret_cast<const u32x16 DCP_CONST*>(qh + 16 * c);
-  }
-
-  // prologue: tiles 0 and 1 in flight (both buffers are free)
-  uint64_t vm0 = issue_tile(0);
-  const uint64_t vm_first = ntiles > 1 ? issue_tile(1) : 0ull;
-
-  const int pr = lane >> 4, pcl = lane & 15;   // f32 P.V lane: token group, row chunk
-  auto v_swz = [](int r) { return v_swz_t<kBf16>(r); };
-  for (int ti = 0; ti < ntiles; ++ti) {
-    // this wave's copies of tile ti have landed (loads complete in issue order, so on the
-    // first tile only tile 1's copies may still be outstanding); after the barrier every
-    // wave's have, and from tile 1 on the buffer of tile ti-1 is free for tile ti+1.  A bare
-    // barrier: the fence of __syncthreads would also wait for LDS traffic that needs no
-    // ordering here.
-    if (ti == 0 && ntiles > 1) wait_vmcnt<kDmaPerWave>();
-    else wait_vmcnt<0>();
-    asm volatile("s_barrier" ::: "memory");
-    const uint64_t vm1 = ti == 0 ? vm_first : (ti + 1 < ntiles ? issue_tile(ti + 1) : 0ull);
-    const char DCP_LDS* kb = kvb + (ti % kNBuf) * kBufBytes +
-                             (lane >> 2) * kKBlock + (lane & 3) * 16;   // this lane's K row
-    const u32x4 DCP_LDS* vt = (const u32x4 DCP_LDS*)(kvb + (ti % kNBuf) * kBufBytes + kKBytes);
-    auto kchunk = [&](int c) { return *(const u32x4 DCP_LDS*)(kb + 64 * c); };
-
-    // ---- scores: lane = token
-    float s[HPW];
-    if constexpr (kQResident) {
-      // the whole K row moves to registers at once (64 VGPRs): all 16 reads in flight
-      float s2[2] = {0.f, 0.f};
-      u32x4 kr[kChunks];
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) kr[c] = kchunk(c);
-#pragma unroll
-      for (int c = 0; c < kChunks / 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t kd = kr[4 * c + e / 4][e % 4];
-          const uint32_t qd = qres[c][e];
-          if constexpr (kBf16) s2[e & 1] = dot2_bf16(qd, kd, s2[e & 1]);
-          else s2[e & 1] = fmaf(__uint_as_float(qd), __uint_as_float(kd), s2[e & 1]);
-        }
-      s[0] = s2[0] + s2[1];
-    } else {
-      u32x4 krow[kChunks];
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) krow[c] = kchunk(c);
-      // 16 query dwords per scalar load, one load ahead of its use; each step is its own
-      // scheduling region so that no more than two chunks (32 scalar registers) are live
-      constexpr int kQSteps = HPW * (kChunks / 4);
-      auto qload = [&](int st) -> u32x16 {
-        uint64_t qa = reinterpret_cast<uint64_t>(
-            qbase + (size_t)rrow[st / (kChunks / 4)] * (kRowBytes / 4) + 16 * (st % (kChunks / 4)));
-        asm volatile("" : "+s"(qa));
-        return *reinterpret_cast<const u32x16 DCP_CONST*>(qa);
-      };
-      float sacc[HPW][2];
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) sacc[h][0] = sacc[h][1] = 0.f;
-      u32x16 qv[2];
-      qv[0] = qload(0);
-#pragma unroll
-      for (int st = 0; st < kQSteps; ++st) {
-        if (st + 1 < kQSteps) qv[(st + 1) & 1] = qload(st + 1);
-        const int h = st / (kChunks / 4), qc = st % (kChunks / 4);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t kd = krow[4 * qc + e / 4][e % 4];
-          float& dst = sacc[h][e & 1];
-          if constexpr (kBf16) dst = dot2_bf16(qv[st & 1][e], kd, dst);
-          else dst = fmaf(__uint_as_float(qv[st & 1][e]), __uint_as_float(kd), dst);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) s[h] = sacc[h][0] + sacc[h][1];
-    }
-
-    // ---- online softmax (base 2); weights to LDS for the P.V lanes.  The running max m
-    // only moves when a tile's max exceeds it by more than kRescaleSlack (always on the
-    // first tile with a valid token); in between the weights stay below 2^kRescaleSlack and
-    // the accumulators are not touched.  The final normalisation by the running sum makes
-    // the result exact for any reference m.
-    const int jt = j0 + ti * kTile;   // local index of the tile's first token
+  } else {
+    // running max (log2 units), -m (0 while m is -inf), per-lane share of the running sum,
+    // and the lane's NA = 4 dims of each row (16-byte chunk pcl of the V row)
+    constexpr int NA = 4;
+    float m[HPW], negm[HPW], ls[HPW], acc[HPW][NA];
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-      float x = s[h] * a.sl2;
-      if (vm0 != ~0ull || jt + kTile > lim_min) {   // partial tile (uniform); the empty asm
-        asm volatile("");                            // keeps this a branch
-        x = (((vm0 >> lane) & 1) && jt + lane < lim[h]) ? x : neg_inf();
-      }
-      const float tmax = wave_max_bcast(x);
-      if (tmax > m[h] + kRescaleSlack) {   // uniform branch; m = -inf: any valid tile
-        const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);   // m = -inf -> 0
-        m[h] = tmax;
-        negm[h] = -tmax;
-        ls[h] *= alpha;
+      m[h] = neg_inf();
+      negm[h] = 0.f;
+      ls[h] = 0.f;
 #pragma unroll
-        for (int k = 0; k < NA; ++k) acc[h][k] *= alpha;
-      }
-      const float p = __builtin_amdgcn_exp2f(x + negm[h]);   // masked: 0
-      ls[h] += p;
-      if constexpr (kBf16) {
-        // tokens 2k and 2k + 1 as one bf16x2 word (round to nearest even), written by the
-        // even lane
-        const float pn = dpp<kDppQuadXor1>(p);
-        const f2 pp = {p, pn};
-        if (!(lane & 1))
-          pbuf[w][h][lane >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
-      } else {
-        pbuf[w][h][lane] = __float_as_uint(p);
-      }
+      for (int k = 0; k < NA; ++k) acc[h][k] = 0.f;
     }
 
-    // ---- P.V
-    if constexpr (kBf16) {
-      // lane (16-lane group pg, i16) owns dims 32 pg + i16 and 32 pg + 16 + i16.  One
-      // ds_read_b64_tr_b16 gives it one of those dims of 4 consecutive tokens t0 .. t0 + 3,
-      // i.e. the token pairs (t0, t0 + 1), (t0 + 2, t0 + 3) that v_dot2 takes against the
-      // weight pairs, which arrive wave-uniform, four pairs per LDS read.
-      const char DCP_LDS* vb = (const char DCP_LDS*)vt;
-      const int i16 = lane & 15, pg = lane >> 4;
+    // query of a single head per wave: loaded once into scalar registers
+    constexpr bool kQResident = HPW == 1;
+    u32x16 qres[kChunks / 4];
+    if constexpr (kQResident) {
 #pragma unroll
-      for (int q = 0; q < kTile / 8; ++q) {
-        u32x4 pq[HPW];   // weight pairs of tokens 8 q .. 8 q + 7
+      for (int c = 0; c < kChunks / 4; ++c)
+        qres[c] = *reinterpret_cast<const u32x16 DCP_CONST*>(qh + 16 * c);
+    }
+
+    // prologue: tiles 0 and 1 in flight (both buffers are free)
+    uint64_t vm0 = issue_tile(0);
+    const uint64_t vm_first = ntiles > 1 ? issue_tile(1) : 0ull;
+
+    const int pr = lane >> 4, pcl = lane & 15;   // f32 P.V lane: token group, row chunk
+    for (int ti = 0; ti < ntiles; ++ti) {
+      // this wave's copies of tile ti have landed (loads complete in issue order, so on the
+      // first tile only tile 1's copies may still be outstanding); after the barrier every
+      // wave's have, and from tile 1 on the buffer of tile ti-1 is free for tile ti+1.  A bare
+      // barrier: the fence of __syncthreads would also wait for LDS traffic that needs no
+      // ordering here.
+      if (ti == 0 && ntiles > 1) wait_vmcnt<kDmaPerWave>();
+      else wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");
+      const uint64_t vm1 = ti == 0 ? vm_first : (ti + 1 < ntiles ? issue_tile(ti + 1) : 0ull);
+      const char DCP_LDS* kb = kvb + (ti % kNBuf) * kBufBytes +
+                               (lane >> 2) * kKBlock + (lane & 3) * 16;   // this lane's K row
+      const u32x4 DCP_LDS* vt = (const u32x4 DCP_LDS*)(kvb + (ti % kNBuf) * kBufBytes + kKBytes);
+      auto kchunk = [&](int c) { return *(const u32x4 DCP_LDS*)(kb + 64 * c); };
+
+      // ---- scores: lane = token
+      float s[HPW];
+      if constexpr (kQResident) {
+        // the whole K row moves to registers at once (64 VGPRs): all 16 reads in flight
+        float s2[2] = {0.f, 0.f};
+        u32x4 kr[kChunks];
 #pragma unroll
-        for (int h = 0; h < HPW; ++h)
-          pq[h] = *reinterpret_cast<const u32x4 DCP_LDS*>(
-              (const char DCP_LDS*)&pbuf[w][h][0] + 16 * q);
+        for (int c = 0; c < kChunks; ++c) kr[c] = kchunk(c);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int r = 8 * q + 4 * half + (i16 >> 2);   // tile row this lane addresses
+        for (int c = 0; c < kChunks / 4; ++c)
 #pragma unroll
-          for (int dh = 0; dh < 2; ++dh) {
-            const int c = 2 * (2 * pg + dh) + ((i16 >> 1) & 1);   // logical 16-byte chunk
-            const u32x2 v = lds_tr16(vb + r * kRowBytes + 16 * (c ^ v_swz(r)) + (i16 & 1) * 8);
-#pragma unroll
-            for (int h = 0; h < HPW; ++h) {
-              acc[h][dh] = dot2_bf16(pq[h][2 * half], v.x, acc[h][dh]);
-              acc[h][dh] = dot2_bf16(pq[h][2 * half + 1], v.y, acc[h][dh]);
-            }
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t kd = kr[4 * c + e / 4][e % 4];
+            const uint32_t qd = qres[c][e];
+            s2[e & 1] = fmaf(__uint_as_float(qd), __uint_as_float(kd), s2[e & 1]);
           }
+        s[0] = s2[0] + s2[1];
+      } else {
+        u32x4 krow[kChunks];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) krow[c] = kchunk(c);
+        // 16 query dwords per scalar load, one load ahead of its use; each step is its own
+        // scheduling region so that no more than two chunks (32 scalar registers) are live
+        constexpr int kQSteps = HPW * (kChunks / 4);
+        auto qload = [&](int st) -> u32x16 {
+          uint64_t qa = reinterpret_cast<uint64_t>(
+              qbase + (size_t)rrow[st / (kChunks / 4)] * (kRowBytes / 4) + 16 * (st % (kChunks / 4)));
+          asm volatile("" : "+s"(qa));
+          return *reinterpret_cast<const u32x16 DCP_CONST*>(qa);
+        };
+        float sacc[HPW][2];
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) sacc[h][0] = sacc[h][1] = 0.f;
+        u32x16 qv[2];
+        qv[0] = qload(0);
+#pragma unroll
+        for (int st = 0; st < kQSteps; ++st) {
+          if (st + 1 < kQSteps) qv[(st + 1) & 1] = qload(st + 1);
+          const int h = st / (kChunks / 4), qc = st % (kChunks / 4);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t kd = krow[4 * qc + e / 4][e % 4];
+            float& dst = sacc[h][e & 1];
+            dst = fmaf(__uint_as_float(qv[st & 1][e]), __uint_as_float(kd), dst);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) s[h] = sacc[h][0] + sacc[h][1];
       }
-    } else {
+
+      // ---- online softmax (base 2); weights to LDS for the P.V lanes.  The running max m
+      // only moves when a tile's max exceeds it by more than kRescaleSlack (always on the
+      // first tile with a valid token); in between the weights stay below 2^kRescaleSlack and
+      // the accumulators are not touched.  The final normalisation by the running sum makes
+      // the result exact for any reference m.
+      const int jt = j0 + ti * kTile;   // local index of the tile's first token
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        float x = s[h] * a.sl2;
+        if (vm0 != ~0ull || jt + kTile > lim_min) {   // partial tile (uniform); the empty asm
+          asm volatile("");                            // keeps this a branch
+          x = (((vm0 >> lane) & 1) && jt + lane < lim[h]) ? x : neg_inf();
+        }
+        const float tmax = wave_max_bcast(x);
+        if (tmax > m[h] + kRescaleSlack) {   // uniform branch; m = -inf: any valid tile
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);   // m = -inf -> 0
+          m[h] = tmax;
+          negm[h] = -tmax;
+          ls[h] *= alpha;
+#pragma unroll
+          for (int k = 0; k < NA; ++k) acc[h][k] *= alpha;
+        }
+        const float p = __builtin_amdgcn_exp2f(x + negm[h]);   // masked: 0
+        ls[h] += p;
+        pbuf[w][h][lane] = __float_as_uint(p);
+      }
+
+      // ---- P.V: lane = (token group pr, 16-byte chunk pcl of the V row)
 #pragma unroll
       for (int k = 0; k < kTile / 4; ++k) {
         const u32x4 v = vt[(4 * k + pr) * kChunks + pcl];
@@ -686,33 +631,21 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
           for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(pp, __uint_as_float(v[i]), acc[h][i]);
         }
       }
+      vm0 = vm1;
     }
-    vm0 = vm1;
-  }
 
-  // ---- finalize: O = acc / l, lse = (m + log2 l) ln 2
+    // ---- finalize: O = acc / l, lse = (m + log2 l) ln 2
 #pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    const float lt = wave_sum_dpp(ls[h]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse = lt > 0.f ? (m[h] + __log2f(lt)) * kLn2 : neg_inf();
-    if (!live[h]) continue;   // a repeated row (uniform)
-    const int row = rrow[h];
-    float* dst = single ? static_cast<float*>(a.o_out) + ((size_t)b * RQ + row) * D
-                        : a.po + ((size_t)item * RQ + row) * D;
-    uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + ((size_t)b * RQ + row) * D;
-    const bool bf16_out = single && a.o_bf16;   // uniform
-    if constexpr (kBf16) {
-      // lane (g, i16): dims 32 g + i16 and 32 g + 16 + i16
-      const int d0 = 32 * (lane >> 4) + (lane & 15);
-      if (bf16_out) {
-        dstb[d0] = (uint16_t)f32_to_bf16_rne(acc[h][0] * inv);
-        dstb[d0 + 16] = (uint16_t)f32_to_bf16_rne(acc[h][1] * inv);
-      } else {
-        dst[d0] = acc[h][0] * inv;
-        dst[d0 + 16] = acc[h][1] * inv;
-      }
-    } else {
+    for (int h = 0; h < HPW; ++h) {
+      const float lt = wave_sum_dpp(ls[h]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? (m[h] + __log2f(lt)) * kLn2 : neg_inf();
+      if (!live[h]) continue;   // a repeated row (uniform)
+      const int row = rrow[h];
+      float* dst = single ? static_cast<float*>(a.o_out) + ((size_t)b * RQ + row) * D
+                          : a.po + ((size_t)item * RQ + row) * D;
+      uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + ((size_t)b * RQ + row) * D;
+      const bool bf16_out = single && a.o_bf16;   // uniform
       // the four token groups of each row chunk are summed across the 16-lane rows
       float o[NA];
 #pragma unroll
@@ -733,61 +666,59 @@ __global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
         else
           *reinterpret_cast<float4*>(dst + 4 * pcl) = make_float4(o[0], o[1], o[2], o[3]);
       }
-    }
-    if (lane == 0) {
-      if (single) a.lse_out[(size_t)b * RQ + row] = lse;
-      else a.plse[(size_t)item * RQ + row] = lse;
+      if (lane == 0) {
+        if (single) a.lse_out[(size_t)b * RQ + row] = lse;
+        else a.plse[(size_t)item * RQ + row] = lse;
+      }
     }
   }
 }
 
-template <bool kBf16, int R>
+// f32: the vector-ALU variant; R = q_len * G query rows per KV head, rows sharing a
+// (waves, rows per wave) shape sharing the kernel.
+template <int R>
 void launch_r(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int NW = waves_for(R), HPW = rows_per_wave(R);
-  hipExtLaunchKernelGGL((gqa_shard_kernel<kBf16, NW, HPW>), grid, dim3(64 * NW), 0, s, e0, e1,
+  hipExtLaunchKernelGGL((gqa_shard_kernel<false, NW, HPW>), grid, dim3(64 * NW), 0, s, e0, e1,
                         0, k);
 }
 
-// Matrix-core variant: four waves, RT 16-row tiles per wave, one workgroup per (item, KV
-// head, slice of 32 rows).
+hipError_t launch_f32(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1) {
+  switch (rows) {
+    case 1: launch_r<1>(k, grid, s, e0, e1); break;
+    case 2: launch_r<2>(k, grid, s, e0, e1); break;
+    case 3: case 4: launch_r<4>(k, grid, s, e0, e1); break;
+    case 6: case 8: launch_r<8>(k, grid, s, e0, e1); break;
+    case 12: case 16: launch_r<16>(k, grid, s, e0, e1); break;
+    case 24: launch_r<24>(k, grid, s, e0, e1); break;
+    case 32: launch_r<32>(k, grid, s, e0, e1); break;
+    case 48: launch_r<48>(k, grid, s, e0, e1); break;
+    case 64: launch_r<64>(k, grid, s, e0, e1); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// bf16: the matrix-core variant, four waves, RT 16-row tiles per wave, one workgroup per
+// (item, KV head, slice of 32 rows); rows past R pad the 16-row tile.  The per-token work,
+// 4 R D flops against 4 D bytes of K and V, then stays off the vector ALUs, which did not
+// hide entirely under the HBM -> LDS stream at R = 1..8 (measured at the share's shape with
+// the vector ALUs doing the bf16 products in v_dot2: 73-76% of HBM peak against 79-82% on
+// the matrix cores) and became the bound at R >= 16 (48 / 64 rows: 13% / 10% of HBM peak).
 template <int RT>
 void launch_m(const GqaKArgs& k, dim3 grid, int slices, hipStream_t s, hipEvent_t e0,
               hipEvent_t e1) {
   const dim3 g(grid.x, grid.y * (unsigned)slices);
-  hipExtLaunchKernelGGL((gqa_shard_kernel<true, 4, RT, true>), g, dim3(256), 0, s, e0, e1, 0,
+  hipExtLaunchKernelGGL((gqa_shard_kernel<true, 4, RT>), g, dim3(256), 0, s, e0, e1, 0,
                         k);
 }
 
-// R = q_len * G query rows per KV head; rows sharing a (waves, rows per wave) shape share
-// the kernel.  bf16 runs the group's products on the matrix cores (rows past R pad the
-// 16-row tile; more than 32 rows take two workgroups of 32 rows each): the per-token work, 4 R D flops against 4 D bytes of K and
-// V, then stays off the vector ALUs, which did not hide entirely under the HBM -> LDS
-// stream at R = 1..8 (measured at the share's shape: 73-76% of HBM peak on the vector ALUs
-// against 79-82% on the matrix cores) and became the bound at R >= 16 (48 / 64 rows at
-// the share's shape: 13% / 10% of HBM peak on the vector ALUs).  fp32 stays on the vector
-// ALUs.
-template <bool kBf16>
-hipError_t launch_g(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
-                    hipEvent_t e1) {
-  if constexpr (kBf16) {
-    if (rows >= 1 && rows <= 64) {
-      if (rows <= 16) launch_m<1>(k, grid, 1, s, e0, e1);
-      else launch_m<2>(k, grid, (rows + 31) / 32, s, e0, e1);
-      return hipGetLastError();
-    }
-  }
-  switch (rows) {
-    case 1: launch_r<kBf16, 1>(k, grid, s, e0, e1); break;
-    case 2: launch_r<kBf16, 2>(k, grid, s, e0, e1); break;
-    case 3: case 4: launch_r<kBf16, 4>(k, grid, s, e0, e1); break;
-    case 6: case 8: launch_r<kBf16, 8>(k, grid, s, e0, e1); break;
-    case 12: case 16: launch_r<kBf16, 16>(k, grid, s, e0, e1); break;
-    case 24: launch_r<kBf16, 24>(k, grid, s, e0, e1); break;
-    case 32: launch_r<kBf16, 32>(k, grid, s, e0, e1); break;
-    case 48: launch_r<kBf16, 48>(k, grid, s, e0, e1); break;
-    case 64: launch_r<kBf16, 64>(k, grid, s, e0, e1); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_bf16(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
+                       hipEvent_t e1) {
+  if (rows < 1 || rows > 64) return hipErrorInvalidValue;
+  if (rows <= 16) launch_m<1>(k, grid, 1, s, e0, e1);
+  else launch_m<2>(k, grid, (rows + 31) / 32, s, e0, e1);
   return hipGetLastError();
 }
 
@@ -830,8 +761,8 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
   k.po = ws.po;
   const dim3 grid((unsigned)max_items, (unsigned)a.hkv);
   const int rows = a.rows.q_len * (a.hq / a.hkv);
-  return a.dtype == 1 ? launch_g<true>(k, rows, grid, stream, ev0, ev1)
-                      : launch_g<false>(k, rows, grid, stream, ev0, ev1);
+  return a.dtype == 1 ? launch_bf16(k, rows, grid, stream, ev0, ev1)
+                      : launch_f32(k, rows, grid, stream, ev0, ev1);
 }
 
 }  // namespace dcp

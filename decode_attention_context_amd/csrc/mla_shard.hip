@@ -200,10 +200,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const int i16 = lane & 15;
   const uint32_t B = (uint32_t)a.block_size;
   const int32_t* btb = a.bt + (size_t)b * a.max_blocks;
-  // the block table through the constant address space: scalar loads, which do not count
-  // against the vector-memory counter the copy ring is paced with
-  const int32_t DCP_CONST* btc = reinterpret_cast<const int32_t DCP_CONST*>(
-      reinterpret_cast<uintptr_t>(btb));
   const char DCP_LDS* lds = (const char DCP_LDS*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
   const bool is_qk = w < kQkWaves;
