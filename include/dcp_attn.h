@@ -110,7 +110,10 @@ size_t dcp_workspace_size(const dcp_attn_desc* desc, int batch, int64_t max_seq_
  *   lse          out float32 [batch][num_q_heads]: natural-log log-sum-exp of the shard's
  *                scaled scores.  A request whose shard is empty gets lse = -inf, O = 0.
  *   workspace    device scratch of at least dcp_workspace_size() bytes.  Its first
- *                int32 is the device error word (DCP_DEVERR_*) of the latest call.
+ *                int32 is the device error word (DCP_DEVERR_*) of the latest call.  It
+ *                holds the call's plan and split partials until the call's kernels end:
+ *                calls in flight at the same time need workspaces of their own (calls in
+ *                order on one stream may share one).
  * Returns DCP_OK or a negative dcp_status (nothing launched). */
 int dcp_attn_shard(const dcp_attn_desc* desc, const void* q, const void* kv_pages,
                    const void* v_pages, const int32_t* block_table, const int32_t* seq_lens,

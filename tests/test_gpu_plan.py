@@ -26,6 +26,12 @@ CASES = [
     (wl.GQA_SHARE.with_(batch=64, lengths=(32768,) * 64), dca.GQA, 0),
     (wl.GQA_SHARE.with_(name="plan_gqa_ragged", batch=6, lengths=(1, 77, 128, 1000, 5000, 20001),
                         seed=81), dca.GQA, 1),
+    # 64 query rows per KV head on two KV heads: two 32-row slices per item and KV head
+    (wl.GQA_SHARE.with_(name="plan_gqa_g16_q4_h2", batch=5, q_len=4, num_q_heads=32,
+                        num_kv_heads=2, lengths=(1, 65, 5000, 20001, 300), seed=84), dca.GQA, 1),
+    # fp32 queries and cache (vector-ALU kernel)
+    (wl.GQA_SHARE.with_(name="plan_gqa_f32", dtype="f32", head_dim_qk=64, head_dim_v=64,
+                        batch=3, lengths=(1, 4000, 20001), seed=85), dca.GQA, 1),
     (wl.MLA_RAGGED, dca.MLA, 5),
     (wl.MLA_DECODE.with_(name="plan_mla_i1", batch=3, cp_size=4, interleave=1,
                          lengths=(3, 700, 9000), seed=82), dca.MLA, 3),
@@ -57,7 +63,10 @@ def test_plan(gpu_lib, w, kind, rank):
     n, chunk = int(hdr[1]), int(hdr[2])
     tile = 64 if kind == dca.GQA else 32
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    target = max(1, cus * 2 // w.num_kv_heads) if kind == dca.GQA else max(1, cus // 2)
+    rows = w.q_len * (w.num_q_heads // w.num_kv_heads)
+    slices = 2 if (kind == dca.GQA and w.dtype == "bf16" and rows > 32) else 1
+    target = (max(1, cus * 2 // (w.num_kv_heads * slices)) if kind == dca.GQA
+              else max(1, cus // 2))
     assert chunk % tile == 0 and chunk > 0
     assert n <= target + w.batch
     lens = [int(x) for x in inp["seq_lens"].cpu()]
