@@ -183,37 +183,39 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One 16-byte-per-lane HBM -> LDS copy: LDS bytes [lds + 16 lane, + 16) <- global
-// sbase + voff (scalar base, 32-bit lane offset).  M0 carries the LDS address; one wait
-// state separates its write from the copy that reads it.  kNt selects the non-temporal
-// cache policy (nt): a plain stream of HBM -> LDS copies runs at about 7.1 TB/s with it
-// against 5.9 TB/s without on MI355X, which the HBM-bound GQA kernel takes; the MLA kernel,
-// bound by its matrix work, runs about 5% slower with it and copies without.
+// sbase + voff (scalar base, 32-bit lane offset).  M0 carries the LDS address: it is an
+// input operand of the statement, so the compiler writes it (and knows it is read); one
+// wait state separates that write from the copy that reads it.  kNt selects the
+// non-temporal cache policy (nt): a plain stream of HBM -> LDS copies runs at about
+// 7.1 TB/s with it against 5.9 TB/s without on MI355X.  The copy is invisible to the
+// compiler's wait-count tracking, so it never drains it before LDS reads: the kernels
+// pace the copies with explicit vector-memory counter waits.
 template <bool kNt>
 __device__ __forceinline__ void copy16_sbase(uint32_t lds, uint32_t voff, const char* sbase) {
   if constexpr (kNt)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
-                 : "s"(lds), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(sbase), "{m0}"(lds)
+                 : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "s"(lds), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(sbase), "{m0}"(lds)
+                 : "memory");
 }
 // The same from a per-lane 64-bit address.
 template <bool kNt>
 __device__ __forceinline__ void copy16_vaddr(uint32_t lds, const char* src) {
   if constexpr (kNt)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                  :
-                 : "s"(lds), "v"(src)
-                 : "memory", "m0");
+                 : "v"(src), "{m0}"(lds)
+                 : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "s"(lds), "v"(src)
-                 : "memory", "m0");
+                 : "v"(src), "{m0}"(lds)
+                 : "memory");
 }
 
 // float -> bf16 bits, round to nearest even (NaN -> quiet NaN).

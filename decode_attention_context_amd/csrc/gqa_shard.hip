@@ -135,8 +135,13 @@ constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r
 //     lane under a wave-uniform branch;
 //   * after the last tile the four token quarters of each row merge through LDS by the LSE
 //     identity (weights exp2(m_k - max m), empty quarters weight 0).
+// Waves per SIMD the register allocation must allow (HIP's second launch bound): two
+// workgroups per CU (their LDS double buffers) give NW / 2 waves per SIMD, at least one;
+// the 8-wave f32 variants keep the 4-wave figure (their rows per wave need the registers).
+constexpr int min_waves_per_simd(int nw) { return nw >= 4 ? 2 : 1; }
+
 template <bool kBf16, int NW, int HPW>
-__global__ __launch_bounds__(64 * NW, 2) void gqa_shard_kernel(GqaKArgs a) {
+__global__ __launch_bounds__(64 * NW, min_waves_per_simd(NW)) void gqa_shard_kernel(GqaKArgs a) {
   constexpr bool kMfma = kBf16;   // bf16 runs on the matrix cores, f32 on the vector ALUs
   static_assert(!kMfma || NW == 4, "matrix-core variant: four waves");
   constexpr int kElemBytes = kBf16 ? 2 : 4;
