@@ -8,6 +8,7 @@ is missing or fails to load, every call raises.
 
 Entry points (same names as the C ABI, without the dcp_ prefix):
   shard(...)          partial decode attention over one DCP rank's shard -> (O_r, lse_r)
+  shard_noalloc(...)  the same with the library's static scratch instead of a workspace
   merge(...)          LSE-weighted merge of cp_size partials -> (O, lse)
   shard_slots(...)    the block-table walk: physical slots of a rank's tokens
   local_len(...)      tokens of a sequence a rank stores (host)
@@ -21,7 +22,7 @@ import os
 import torch
 
 __all__ = ["load", "lib_path", "GQA", "MLA", "F32", "BF16", "DCPError", "workspace_size",
-           "shard", "merge", "shard_slots", "local_len", "check_parallel",
+           "shard", "shard_noalloc", "merge", "shard_slots", "local_len", "check_parallel",
            "read_device_errors", "status_string", "DEVERR_SEQ_LEN", "DEVERR_BLOCK_ID"]
 
 GQA, MLA = 0, 1
@@ -71,6 +72,8 @@ _SIGS = {
     "dcp_attn_shard_fp8kv": (_I, [ctypes.POINTER(Desc), _I, _I, _P, _P, _P, _F, _F, _P, _P, _I,
                                   _I64, _I, _I, _I, _F, _P, _P, _P, ctypes.c_size_t, _P, _P,
                                   _P]),
+    "dcp_attn_shard_noalloc": (_I, [ctypes.POINTER(Desc), _I, _I, _P, _P, _P, _P, _P, _I,
+                                    _I64, _I, _I, _I, _F, _P, _P, _P]),
     "dcp_merge_ex": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "dcp_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "dcp_merge_timed": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
@@ -271,6 +274,51 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
             _check("dcp_attn_shard_mq_timed",
                    lib.dcp_attn_shard_mq_timed(ctypes.byref(desc), q_len, *args, *evs))
     return out, lse, workspace
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DCP_NOALLOC_SCRATCH_BYTES of include/dcp_attn.h
+
+
+def shard_noalloc(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave,
+                  scale, out, lse, *, kind=None, max_seq_len=None, stream=None):
+    """dcp_attn_shard_noalloc: the shard call with the plan and split partials in the
+    library's static device scratch (no workspace, nothing allocated by the call).  The
+    caller passes the outputs: out [b, Hq, Dv] or [b, q_len, Hq, Dv] (float32 or bf16) and
+    lse float32 [b, Hq] or [b, q_len, Hq].  Calls on one device must not overlap."""
+    lib = load()
+    if kind is None:
+        kind = MLA if v_pages is None else GQA
+    _need(q, "q")
+    if q.dim() not in (3, 4):
+        raise ValueError(f"q must be [b, Hq, D] or [b, q_len, Hq, D], got {tuple(q.shape)}")
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    _need(kv_pages, "kv_pages", dtype=q.dtype)
+    if kind == GQA:
+        _need(v_pages, "v_pages", dtype=q.dtype)
+        if v_pages.shape != kv_pages.shape:
+            raise ValueError("K and V pages must have the same shape")
+    elif v_pages is not None:
+        raise ValueError("MLA takes no v_pages")
+    _need(block_table, "block_table", dtype=torch.int32, dim=2)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1)
+    batch = q.shape[0]
+    if block_table.shape[0] != batch or seq_lens.shape[0] != batch:
+        raise ValueError("q, block_table and seq_lens disagree on the batch size")
+    desc = make_desc(kind, q, kv_pages, block_table)
+    if max_seq_len is None:
+        max_seq_len = desc.max_blocks_per_seq * desc.block_size
+    rows = (batch,) + ((q_len,) if q.dim() == 4 else ()) + (desc.num_q_heads,)
+    _need(out, "out")
+    _need(lse, "lse", dtype=torch.float32)
+    if tuple(out.shape) != rows + (desc.head_dim_v,) or tuple(lse.shape) != rows:
+        raise ValueError("out / lse have the wrong shape")
+    _check("dcp_attn_shard_noalloc",
+           lib.dcp_attn_shard_noalloc(ctypes.byref(desc), q_len, _dtype_code(out.dtype),
+                                      _ptr(q), _ptr(kv_pages), _ptr(v_pages), _ptr(block_table),
+                                      _ptr(seq_lens), batch, int(max_seq_len), rank, cp_size,
+                                      interleave, float(scale), _ptr(out), _ptr(lse),
+                                      _stream(stream)))
+    return out, lse
 
 
 def merge(o_partials, lse_partials, *, out_dtype=torch.float32, out=None, lse_out=None,

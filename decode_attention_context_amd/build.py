@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdcpattn.so")
-SOURCES = ["dcp_api.cpp", "plan.hip", "merge.hip", "gqa_shard.hip",
+SOURCES = ["dcp_api.cpp", "noalloc.hip", "plan.hip", "merge.hip", "gqa_shard.hip",
            "gqa_fp8.hip", "mla_shard.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

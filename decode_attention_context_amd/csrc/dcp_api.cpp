@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "api_internal.h"
 #include "dcp_attn.h"
 #include "launch.h"
 
@@ -143,6 +144,17 @@ int shard_impl(const dcp_attn_desc* d, int q_len, int o_dtype, const void* q, co
 }
 
 }  // namespace
+
+int dcp::shard_call(const dcp_attn_desc* desc, int q_len, int o_dtype, const void* q,
+                    const void* kv_pages, const void* v_pages, const int32_t* block_table,
+                    const int32_t* seq_lens, int batch, int64_t max_seq_len, int rank,
+                    int cp_size, int interleave, float scale, void* o_partial, float* lse,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    hipEvent_t ev_begin, hipEvent_t ev_end) {
+  return shard_impl(desc, q_len, o_dtype, q, kv_pages, v_pages, block_table, seq_lens, batch,
+                    max_seq_len, rank, cp_size, interleave, scale, o_partial, lse, workspace,
+                    workspace_bytes, stream, ev_begin, ev_end);
+}
 
 extern "C" {
 
@@ -298,6 +310,8 @@ const char* dcp_status_string(int status) {
     case DCP_EUNSUPPORTED: return "DCP_EUNSUPPORTED: shape or dtype not implemented";
     case DCP_ELAUNCH: return "DCP_ELAUNCH: HIP runtime error";
     case DCP_EWORKSPACE: return "DCP_EWORKSPACE: workspace null, misaligned or too small";
+    case DCP_ESCRATCH:
+      return "DCP_ESCRATCH: the call needs more scratch than the library's static array holds";
     default: return "unknown dcp_status";
   }
 }

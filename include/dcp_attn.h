@@ -21,7 +21,8 @@
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers unless marked host; all tensors are dense
  *     and row-major in the layouts documented below.  The caller owns every buffer; the
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no state between calls, except for the static
+ *     scratch array of dcp_attn_shard_noalloc (described there).
  *   - Work is enqueued on `stream` and never synchronizes with the host, except in
  *     dcp_read_device_errors, which says so.  The calls can be recorded in a HIP graph.
  *   - Argument errors are detected on the host before anything is launched and returned
@@ -47,7 +48,9 @@ typedef enum {
   DCP_EINVAL = -1,        /* a bad argument (null pointer, size out of range, rank >= cp_size, ...) */
   DCP_EUNSUPPORTED = -2,  /* a valid but unimplemented shape or dtype */
   DCP_ELAUNCH = -3,       /* the HIP runtime rejected a launch or a query */
-  DCP_EWORKSPACE = -4     /* the workspace is null, too small or misaligned */
+  DCP_EWORKSPACE = -4,    /* the workspace is null, too small or misaligned */
+  DCP_ESCRATCH = -5       /* dcp_attn_shard_noalloc: the call needs more than the library's
+                             static scratch (DCP_NOALLOC_SCRATCH_BYTES) */
 } dcp_status;
 
 /* Element types. */
@@ -203,6 +206,29 @@ int dcp_attn_shard_fp8kv(const dcp_attn_desc* desc, int q_len, int o_dtype, cons
                          float scale, void* o_partial, float* lse, void* workspace,
                          size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
                          hipEvent_t ev_end);
+
+/* The shard call for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): dcp_attn_shard_ex without
+ * a workspace argument and without timing events.  The plan and the split partials live in
+ * a static device array of DCP_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * device it runs on until the process ends; the call itself allocates nothing.
+ *   Runs on the current HIP device; `stream` must belong to it.
+ *   A call that needs more than DCP_NOALLOC_SCRATCH_BYTES of workspace
+ *   (dcp_workspace_size_mq with the same arguments) returns DCP_ESCRATCH without launching.
+ *   Every call on one device shares that device's array: calls whose kernels overlap on one
+ *   device (on different streams, or from several host threads without ordering) race and
+ *   give wrong results.  Calls in order on one stream are safe; each call's planner
+ *   rewrites the plan and the error word before its kernels read them.
+ *   The device error word (DCP_DEVERR_*) is kept in the array and is not readable by the
+ *   caller; device-side contract violations are handled as in dcp_attn_shard (tokens
+ *   skipped, no fault).
+ * Every other argument, the results and the errors are as in dcp_attn_shard_ex. */
+#define DCP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dcp_attn_shard_noalloc(const dcp_attn_desc* desc, int q_len, int o_dtype, const void* q,
+                           const void* kv_pages, const void* v_pages,
+                           const int32_t* block_table, const int32_t* seq_lens, int batch,
+                           int64_t max_seq_len, int rank, int cp_size, int interleave,
+                           float scale, void* o_partial, float* lse, hipStream_t stream);
 
 /* LSE-weighted merge of cp_size partials into attention over the union of their tokens
  * (blog, "DCP execution flow", step 3: the LSE values reweight the partial results with
