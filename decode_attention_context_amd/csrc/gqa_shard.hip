@@ -688,20 +688,20 @@ void launch_r(const GqaKArgs& k, dim3 grid, hipStream_t s, hipEvent_t e0, hipEve
                         0, k);
 }
 
+// Any R <= 64 rows runs on the variant of the next listed size (rows past R repeat the
+// last row and are not written).
 hipError_t launch_f32(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
                       hipEvent_t e1) {
-  switch (rows) {
-    case 1: launch_r<1>(k, grid, s, e0, e1); break;
-    case 2: launch_r<2>(k, grid, s, e0, e1); break;
-    case 3: case 4: launch_r<4>(k, grid, s, e0, e1); break;
-    case 6: case 8: launch_r<8>(k, grid, s, e0, e1); break;
-    case 12: case 16: launch_r<16>(k, grid, s, e0, e1); break;
-    case 24: launch_r<24>(k, grid, s, e0, e1); break;
-    case 32: launch_r<32>(k, grid, s, e0, e1); break;
-    case 48: launch_r<48>(k, grid, s, e0, e1); break;
-    case 64: launch_r<64>(k, grid, s, e0, e1); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (rows < 1 || rows > 64) return hipErrorInvalidValue;
+  if (rows <= 1) launch_r<1>(k, grid, s, e0, e1);
+  else if (rows <= 2) launch_r<2>(k, grid, s, e0, e1);
+  else if (rows <= 4) launch_r<4>(k, grid, s, e0, e1);
+  else if (rows <= 8) launch_r<8>(k, grid, s, e0, e1);
+  else if (rows <= 16) launch_r<16>(k, grid, s, e0, e1);
+  else if (rows <= 24) launch_r<24>(k, grid, s, e0, e1);
+  else if (rows <= 32) launch_r<32>(k, grid, s, e0, e1);
+  else if (rows <= 48) launch_r<48>(k, grid, s, e0, e1);
+  else launch_r<64>(k, grid, s, e0, e1);
   return hipGetLastError();
 }
 
@@ -729,11 +729,13 @@ hipError_t launch_bf16(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hi
 
 }  // namespace
 
+// 256-byte rows (bf16 head_dim 128, f32 head_dim 64) and any group of up to 64 query rows
+// (q_len * G) per KV head.
 bool gqa_supported(int dtype, int head_dim, int group, int q_len) {
   const int elem = dtype == 1 ? 2 : 4;
   if (head_dim * elem != kRowBytes) return false;
-  if (q_len < 1 || q_len > kMaxQLen) return false;
-  return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
+  if (q_len < 1 || q_len > kMaxQLen || group < 1) return false;
+  return group * q_len <= 64;
 }
 
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,

@@ -70,8 +70,10 @@ typedef enum { DCP_GQA = 0, DCP_MLA = 1 } dcp_kind;
 /* Shape of the paged cache and the heads.
  *   GQA: k_pages, v_pages  [num_blocks][num_kv_heads][block_size][head_dim]  (dtype),
  *        q [batch][num_q_heads][head_dim] (dtype); head_dim_qk == head_dim_v.
- *        Supported: dtype F32 or BF16 with head_dim * sizeof(dtype) in {256, 512}
- *        (f32 64/128, bf16 128/256), 1 <= G <= 16.
+ *        Supported: BF16 with head_dim 128, or F32 with head_dim 64 (256-byte rows), and
+ *        any group G = num_q_heads / num_kv_heads with q_len * G <= 64 query rows per KV
+ *        head (q_len = 1 except in dcp_attn_shard_mq / _ex / _fp8kv / _noalloc).  Every
+ *        other GQA shape returns DCP_EUNSUPPORTED without launching.
  *   MLA: latent_pages [num_blocks][block_size][head_dim_qk] (BF16),
  *        q [batch][num_q_heads][head_dim_qk] (BF16).
  *        Supported: num_q_heads 128, head_dim_qk 576, head_dim_v 512, num_kv_heads 1.
