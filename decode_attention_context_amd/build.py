@@ -19,6 +19,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source flags.  mla_shard.hip: MFMA builtins keep their accumulators in VGPRs (its
+# AGPRs are all taken by inline-asm accumulators).
+EXTRA_FLAGS = {"mla_shard.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 # The host pass of hipcc does not know the target feature named in FLAGS and says so once
 # per source; that line is the only compiler output a clean build may print.
 _BENIGN = ("packed-fp32-ops",)
@@ -26,7 +30,8 @@ _BENIGN = ("packed-fp32-ops",)
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src),
+                                                        "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if not any(b in l for b in _BENIGN))

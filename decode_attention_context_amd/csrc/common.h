@@ -17,22 +17,26 @@ namespace dcp {
 //           in dispatch order (longest first); a request's partials have consecutive
 //           indices off[b] .. off[b+1)
 //   plse    float[max_items * rows]:      per-partial log-sum-exp (natural log)
-//   po      float[max_items * rows * Dv]: per-partial normalized output
+//   po      [max_items * rows * Dv]:      per-partial normalized output, float32 (GQA) or
+//                                         bf16 rounded to nearest even (MLA: 128 KiB per
+//                                         item and position instead of 256 KiB)
 // (rows = query rows per request: q_len * Hq)
 // ---------------------------------------------------------------------------------------
 struct WsLayout {
   size_t off_off, items_off, plse_off, po_off, total;
+  int po_bf16;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline WsLayout ws_layout(int batch, int64_t max_items, int hq, int dv) {
+inline WsLayout ws_layout(int batch, int64_t max_items, int hq, int dv, bool po_bf16) {
   WsLayout w;
+  w.po_bf16 = po_bf16 ? 1 : 0;
   w.off_off = 256;
   w.items_off = w.off_off + align256(sizeof(int32_t) * (size_t)(batch + 1));
   w.plse_off = w.items_off + align256(sizeof(int32_t) * 4 * (size_t)max_items);
   w.po_off = w.plse_off + align256(sizeof(float) * (size_t)max_items * hq);
-  w.total = w.po_off + align256(sizeof(float) * (size_t)max_items * hq * dv);
+  w.total = w.po_off + align256((po_bf16 ? 2 : 4) * (size_t)max_items * hq * dv);
   return w;
 }
 
@@ -41,14 +45,15 @@ struct WsPtrs {
   int32_t* off;
   int4* items;
   float* plse;
-  float* po;
+  void* po;
+  int po_bf16;   // po holds bf16 values (else float32)
 };
 
 inline WsPtrs ws_ptrs(void* base, const WsLayout& w) {
   char* p = static_cast<char*>(base);
   return WsPtrs{reinterpret_cast<int32_t*>(p), reinterpret_cast<int32_t*>(p + w.off_off),
                 reinterpret_cast<int4*>(p + w.items_off), reinterpret_cast<float*>(p + w.plse_off),
-                reinterpret_cast<float*>(p + w.po_off)};
+                p + w.po_off, w.po_bf16};
 }
 
 constexpr int kErrSeqLen = 1;

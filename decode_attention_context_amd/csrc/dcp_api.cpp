@@ -64,8 +64,7 @@ struct Plan {
 
 // Work items: the planner splits the shard's tokens into about `target` items (never more
 // than target + batch), about one round of workgroups over the CUs (GQA: one workgroup per
-// item and KV head; MLA: two workgroups, one per half of the heads, per item and query
-// position).  Partials are kept per query row: q_len * num_q_heads rows per item.
+// item and KV head; MLA: one workgroup per item and query position).  Partials are kept per query row: q_len * num_q_heads rows per item.
 bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
   const int cus = device_cus();
   if (cus <= 0) return false;
@@ -79,13 +78,16 @@ bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
     p->target = std::max<int64_t>(1, (int64_t)cus * 2 / (d->num_kv_heads * slices));
     p->min_chunk = dcp::kGqaTile;
   } else {
-    // two head-group workgroups per item, one resident workgroup per CU (144 KiB of LDS)
+    // one workgroup (all heads) per item and query position, one resident workgroup per CU
+    // (144 KiB of LDS)
     p->tile = dcp::kMlaTile;
-    p->target = std::max<int64_t>(1, (int64_t)cus / (2 * q_len));
+    p->target = std::max<int64_t>(1, (int64_t)cus / q_len);
     p->min_chunk = 4 * dcp::kMlaTile;
   }
   p->max_items = (int64_t)batch + p->target;
-  p->lay = dcp::ws_layout(batch, p->max_items, q_len * d->num_q_heads, d->head_dim_v);
+  // MLA split partials in bf16 (the GQA ones are a few KiB per item and stay float32)
+  p->lay = dcp::ws_layout(batch, p->max_items, q_len * d->num_q_heads, d->head_dim_v,
+                          d->kind == DCP_MLA);
   return true;
 }
 

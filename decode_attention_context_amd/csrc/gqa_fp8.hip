@@ -463,7 +463,7 @@ hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
   k.off = ws.off;
   k.items = ws.items;
   k.plse = ws.plse;
-  k.po = ws.po;
+  k.po = static_cast<float*>(ws.po);
   const int rows = a.rows.q_len * (a.hq / a.hkv);
   if (rows < 1 || rows > 64) return hipErrorInvalidValue;
   const dim3 grid((unsigned)max_items, (unsigned)(a.hkv * ((rows + 31) / 32)));

@@ -765,7 +765,7 @@ hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& w
   k.off = ws.off;
   k.items = ws.items;
   k.plse = ws.plse;
-  k.po = ws.po;
+  k.po = static_cast<float*>(ws.po);
   const dim3 grid((unsigned)max_items, (unsigned)a.hkv);
   const int rows = a.rows.q_len * (a.hq / a.hkv);
   return a.dtype == 1 ? launch_bf16(k, rows, grid, stream, ev0, ev1)

@@ -281,9 +281,10 @@ __global__ __launch_bounds__(64 * merge_rows_per_block<kBf16In>()) void merge_ke
 // Split combine: request b's items [off[b], off[b+1]) hold partials of every head.  A
 // request with a single item was written directly by the shard kernel; a request with no
 // item (empty shard) gets O = 0, lse = -inf.
-template <int VEC, bool kBf16Out>
+// Split partials are float32, or bf16 when kBf16In (widened exactly).
+template <int VEC, bool kBf16Out, bool kBf16In>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
-    const int32_t* __restrict__ off, const float* __restrict__ plse, const float* __restrict__ po,
+    const int32_t* __restrict__ off, const float* __restrict__ plse, const void* __restrict__ po,
     int batch, int hq, int dv, void* __restrict__ o_out, float* __restrict__ lse_out) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= (int64_t)batch * hq) return;
@@ -293,13 +294,16 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
   const int lane = threadIdx.x & 63;
   float* of = kBf16Out ? nullptr : static_cast<float*>(o_out) + row * dv;
   uint16_t* obf = kBf16Out ? static_cast<uint16_t*>(o_out) + row * dv : nullptr;
+  const int64_t e0 = ((int64_t)i0 * hq + h) * dv;   // first element of the request's partials
+  const void* pb = kBf16In ? (const void*)(static_cast<const uint16_t*>(po) + e0)
+                           : (const void*)(static_cast<const float*>(po) + e0);
   if (merge_small_ok(n, dv, VEC))
-    merge_row_small<VEC, kBf16Out>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv,
-                                   plse + (int64_t)i0 * hq + h, hq, n, dv,
-                                   kBf16Out ? (void*)obf : (void*)of, lse_out + row, lane);
+    merge_row_small<VEC, kBf16Out, kBf16In>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h,
+                                            hq, n, dv, kBf16Out ? (void*)obf : (void*)of,
+                                            lse_out + row, lane);
   else
-    merge_row<VEC>(po + ((int64_t)i0 * hq + h) * dv, (int64_t)hq * dv,
-                   plse + (int64_t)i0 * hq + h, hq, n, dv, of, obf, lse_out + row, lane);
+    merge_row<VEC, kBf16In>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h, hq, n, dv, of,
+                            obf, lse_out + row, lane);
 }
 
 int pick_vec(int dv) {
@@ -359,17 +363,21 @@ hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, voi
   const int64_t rows = (int64_t)batch * hq;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const dim3 block(64 * kRowsPerBlock);
-#define DCP_COMBINE(V, B)                                                                  \
-  hipLaunchKernelGGL((split_combine_kernel<V, B>), grid, block, 0, stream, ws.off, ws.plse, \
+#define DCP_COMBINE(V, B, I)                                                                  \
+  hipLaunchKernelGGL((split_combine_kernel<V, B, I>), grid, block, 0, stream, ws.off, ws.plse, \
                      ws.po, batch, hq, dv, o_out, lse_out)
+#define DCP_COMBINE_I(V, B)                \
+  if (ws.po_bf16) DCP_COMBINE(V, B, true); \
+  else DCP_COMBINE(V, B, false)
   switch (pick_vec(dv) * 2 + (out_bf16 ? 1 : 0)) {
-    case 8: DCP_COMBINE(4, false); break;
-    case 9: DCP_COMBINE(4, true); break;
-    case 4: DCP_COMBINE(2, false); break;
-    case 5: DCP_COMBINE(2, true); break;
-    case 2: DCP_COMBINE(1, false); break;
-    default: DCP_COMBINE(1, true);
+    case 8: DCP_COMBINE_I(4, false); break;
+    case 9: DCP_COMBINE_I(4, true); break;
+    case 4: DCP_COMBINE_I(2, false); break;
+    case 5: DCP_COMBINE_I(2, true); break;
+    case 2: DCP_COMBINE_I(1, false); break;
+    default: DCP_COMBINE_I(1, true);
   }
+#undef DCP_COMBINE_I
 #undef DCP_COMBINE
   return hipGetLastError();
 }

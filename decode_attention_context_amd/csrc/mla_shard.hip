@@ -8,43 +8,49 @@
 // natural-log LSE of the scaled scores.
 //
 // Per token this is 128 x (576 + 512) multiply-adds against 1152 bytes of cache: a dense
-// contraction (about 242 flop/byte), so both products run on v_mfma_f32_16x16x32_bf16.
+// contraction (about 242 flop/byte, just below the bf16 ridge of MI355X), so both products
+// run on v_mfma_f32_16x16x32_bf16 and the kernel has to keep the HBM stream and the matrix
+// cores busy at the same time.
 //
 // Design:
-//   * Two workgroups of 12 waves per work item (request, local token range), each owning 64
-//     of the 128 heads (two pairs of 16-head tiles).  The two groups of an item get
-//     workgroup ids congruent mod 8, so they run on the same XCD and read each latent tile
-//     from HBM once between them (the second read hits that XCD's L2).
-//   * Warp specialisation.  Four score waves = (head pair, half of the 576 dims) compute the
-//     partial S^T = K . Q^T of both 16-head tiles of their pair (M = 16 tokens, N = 16
-//     heads, K = 32 latent dims per MFMA; every K operand read feeds two MFMAs), swap the
-//     partial scores of one head tile through LDS and finish the online softmax of the
-//     other.  Eight output waves = (head pair, quarter of the 512 value dims) keep O^T in
-//     AGPRs and, one tile behind, accumulate O^T += V^T . P^T (M = 16 value dims, N = 16
-//     heads, K = 32 tokens), the V^T operand read with ds_read_b64_tr_b16 in the token
-//     order of the score registers.  In both products every lane's results belong to one
-//     head, so the softmax max needs two cross-lane steps and the weights never move
-//     between lanes.
-//   * 32-token tiles of latent rows are copied HBM -> LDS by global_load_lds_dwordx4 (no
-//     register staging) into a 4-deep ring: two tiles in flight while the score waves work
-//     on one and the output waves on the previous one.  The copies are issued from inline
-//     assembly and paced by explicit vector-memory counter waits plus a bare s_barrier;
-//     the compiler, which does not see them, then has no reason to drain them before LDS
-//     reads.  The 16-byte chunks of a row are XOR-swizzled by (row mod 8), which spreads
-//     the operand reads over the LDS banks.
-//   * When the interleave and the block size are multiples of 32, every tile is one run of
-//     consecutive slots in one page, located by one readlane from a per-wave table of tile
-//     sources.  Otherwise (the general kernel, down to interleave 1) the cache row of every
-//     token of a window of 12 tiles sits in an LDS table that the score waves, which have
-//     no copies in flight, build a few tiles ahead; the output waves' copies then read their
-//     rows from LDS and stay paced exactly as for page-contiguous tiles.
-//   * The running max only moves when a tile's max exceeds it by more than 8 (log2 units);
-//     the output waves rescale their accumulators only on such tiles.
+//   * One workgroup of four waves (one per SIMD) per work item (request, local token range)
+//     and query position, holding all 128 heads, so each latent tile is copied from HBM
+//     into LDS exactly once.  Wave w owns heads 32 w .. 32 w + 31 (two 16-head tiles) from
+//     end to end: its query lives in 144 VGPRs and its O^T accumulators (32 heads x 512
+//     dims, float32) in all 256 AGPRs, so no score, weight or rescale factor ever moves
+//     between waves.
+//   * S^T = K Q^T per 16 tokens x 16 heads on v_mfma_f32_16x16x32_bf16 (K operand: one
+//     16-byte LDS read per lane feeding the MFMAs of both head tiles); the lane holding
+//     head i16 and tokens 4 g .. 4 g + 3 of each 16-token half then holds, packed to bf16,
+//     exactly the P^T operand of O^T += V^T P^T on the same instruction (32 tokens per
+//     MFMA), whose V^T operand is two ds_read_b64_tr_b16 per 16 value dims, again feeding
+//     both head tiles.  Per 32-token tile a wave issues 72 + 64 MFMAs against 36 + 64 LDS
+//     operand reads.
+//   * Software pipeline: iteration t runs the MFMAs of S^T for tile t + 1 while the online
+//     softmax of tile t (already in registers) runs on the vector ALUs between them, then
+//     O^T += V^T P^T of tile t.  The running max moves only when a tile's max exceeds it by
+//     more than 8 (log2 units); the accumulators are rescaled (a rare branch) only then.
+//   * 32-token tiles of latent rows (36 KiB) are copied HBM -> LDS by
+//     global_load_lds_dwordx4 (no register staging) into a 4-deep ring: tiles t and t + 1
+//     are read while t + 2 and t + 3 are in flight.  Waves 0..2 issue the copies from
+//     inline assembly (12 KiB each per tile), paced by their vector-memory counters and a
+//     bare s_barrier per tile, so the compiler never drains them before LDS reads.  The
+//     16-byte chunks of a row are XOR-swizzled by (row mod 8), which spreads the operand
+//     reads over the LDS banks.
+//   * Where each tile comes from is read from a table in LDS, built a window ahead by wave
+//     3, which issues no copies (its block-table loads can be waited for without draining
+//     a copy stream).  When the interleave and the block size are multiples of 32, a tile
+//     is one run of consecutive slots of one page and the table holds its first cache row
+//     (64 tiles per window); otherwise (down to interleave 1) it holds the cache row of
+//     every token (12 tiles per window).
 //   * Multi-token decode (q_len query positions per request, the last q_len cache tokens
-//     being the request's own draft tokens): each work item gets two workgroups per query
-//     position, all on one XCD.  Position i sees the positions up to seq_len - q_len + i,
-//     a prefix of the shard's local tokens, so its workgroups simply end the item there
-//     (possibly before its first tile: an empty partial, lse = -inf).
+//     being the request's own draft tokens): each work item gets one workgroup per query
+//     position, all on one XCD (the later ones read the tiles from L2).  Position i sees
+//     the positions up to seq_len - q_len + i, a prefix of the shard's local tokens, so its
+//     workgroup ends the item there (possibly before its first tile: an empty partial).
+//   * A request whose shard is one work item gets (O, lse) written directly; otherwise
+//     each item writes its normalized partial output in bf16 (rounded to nearest even)
+//     with its float32 LSE, and the split combine merges them.
 #include "launch.h"
 
 namespace dcp {
@@ -59,44 +65,40 @@ typedef __attribute__((ext_vector_type(2))) float f2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 #define DCP_LDS __attribute__((address_space(3)))
-#define DCP_CONST __attribute__((address_space(4)))
 
 constexpr int kHeads = 128;
 constexpr int kDk = 576;
 constexpr int kDv = 512;
-constexpr int kTile = kMlaTile;              // 32 tokens per tile
-constexpr int kNBuf = 4;                     // LDS tile ring: one computed, three in flight
-constexpr int kRowBytes = kDk * 2;           // 1152
-constexpr int kRowChunks = kRowBytes / 16;   // 72
+constexpr int kTile = kMlaTile;                // 32 tokens per tile
+constexpr int kNBuf = 4;                       // LDS tile ring
+constexpr int kRowBytes = kDk * 2;             // 1152
+constexpr int kRowChunks = kRowBytes / 16;     // 72
 constexpr int kTileBytes = kTile * kRowBytes;  // 36 KiB
-constexpr int kKSteps = kDk / 32;            // 18
-constexpr int kDvTiles = kDv / 16;           // 32
-constexpr int kHeadTiles = 4;                // 16-head tiles per workgroup (64 heads)
-constexpr int kGroups = kHeads / (16 * kHeadTiles);      // head groups (workgroups) per item
-constexpr int kQkWaves = 4;                  // score waves: (head pair, half of the 576 dims)
-constexpr int kPvWaves = 8;                  // output waves: (head pair, quarter of the 512 dims)
-constexpr int kWaves = kQkWaves + kPvWaves;  // 12 waves, three per SIMD
-constexpr int kHalfSteps = kKSteps / 2;      // 9 k-steps of 32 dims per score wave
-constexpr int kQuarterTiles = kDvTiles / 4;  // 8 dv tiles of 16 dims per output wave
-constexpr int kSlotsHi = 5;                  // 1-KiB tile copies per tile: output waves 0..3
-constexpr int kSlotsLo = 4;                  // output waves 4..7 (4 x 5 + 4 x 4 = 36 slots)
-constexpr int kPhase1Tiles = 2;              // dv tiles of an output wave before the mid barrier
-constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr float kRescaleSlack = 8.f;          // see the online softmax below
-constexpr int kAheadK = 4;                   // K operand prefetch distance (k-steps)
-constexpr int kAheadV = 3;                   // V^T operand prefetch distance (dv tiles)
-// LDS: the tile ring; the partial-score exchange [pair][head tile][lane][8 floats]; the
-// weights P [head tile][lane][16 B]; the rescale factors and the final normalisation
-// [head tile][16] floats
-constexpr int kRingBytes = kNBuf * kTileBytes;                  // 147456
-constexpr int kXOff = kRingBytes;
-constexpr int kPOff = kXOff + kHeadTiles * 64 * 32;             // + 8192
-constexpr int kAOff = kPOff + kHeadTiles * 1024;                // + 4096
-constexpr int kFOff = kAOff + kHeadTiles * 16 * 4;              // + 256
-constexpr int kTOff = kFOff + kHeadTiles * 16 * 4;              // + 256
-// general tiles: the cache rows of the tokens of kTWin tiles, built ahead by the score waves
-constexpr int kTWin = 12;
-constexpr int kLdsBytes = kTOff + kTWin * kTile * 4;            // + 1536 = 161792
+constexpr int kKSteps = kDk / 32;              // 18 k-steps of S^T = K Q^T
+constexpr int kDvTiles = kDv / 16;             // 32 value-dim tiles of O^T
+constexpr int kWaves = 4;                      // 32 heads each
+constexpr int kCopyWaves = 3;                  // waves 0..2 copy; wave 3 builds the tables
+constexpr int kBuilder = 3;
+constexpr int kSlots = kTileBytes / 1024;      // 36 one-KiB copies per tile
+constexpr int kSlotsPerWave = kSlots / kCopyWaves;   // 12
+constexpr int kXcds = 8;                       // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr float kRescaleSlack = 8.f;
+// K operand prefetch distance (k-steps): 3 where the registers allow it (the page-contiguous
+// path); the general path keeps more table state live and stays at 2 to avoid spills
+template <bool kFast> constexpr int ahead_k() { return kFast ? 3 : 2; }
+constexpr int kAheadV = 3;                     // V^T operand prefetch distance (dv tiles)
+// tile tables: two windows; page-contiguous tiles keep one entry (first row) per tile and
+// 64 tiles per window, general tiles one entry (row) per token and 12 tiles per window
+constexpr int kFastWin = 64;
+constexpr int kGenWin = 12;
+constexpr int kWinEntries = kGenWin * kTile;   // 384 >= kFastWin
+constexpr int kRingBytes = kNBuf * kTileBytes;  // 147456
+constexpr int kTabOff = kRingBytes;
+constexpr int kStageOff = kTabOff + 2 * kWinEntries * 4;   // + 3072: block-table entries
+constexpr int kSlotOff = kStageOff + kWinEntries * 4;      // + 1536: copy offsets per thread
+constexpr int kLdsBytes = kSlotOff + kWaves * 64 * 32;     // + 8192 = 160256
+static_assert(kSlots % kCopyWaves == 0, "copy slots");
+static_assert(kGenWin > 4 && kFastWin > 4, "a window is built before its first copy");
 
 struct MlaKArgs {
   const uint16_t* q;
@@ -116,7 +118,7 @@ struct MlaKArgs {
   const int32_t* off;
   const int4* items;
   float* plse;
-  float* po;
+  uint16_t* po;  // bf16 split partials
 };
 
 // Two floats to a packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32).
@@ -130,11 +132,10 @@ __device__ __forceinline__ u32x2 lds_tr16(const char DCP_LDS* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-
 // O^T tile += V^T P^T with the accumulator pinned to AGPRs.  kNop inserts wait states
-// first, for an operand written by a VALU op just before (the weights, or a rescaled
-// accumulator).  The compiler does not see this as an MFMA, so code that reads an
-// accumulator after the last one issues its own wait states (settle_acc).
+// first, for an accumulator a VALU op may have just rewritten (the rescale).  The compiler
+// does not see this as an MFMA, so code that reads an accumulator after the last one
+// issues its own wait states (settle below).
 template <bool kNop>
 __device__ __forceinline__ void mfma_acc(f4& acc, const bf16x8& va, const bf16x8& pb) {
   if constexpr (kNop)
@@ -151,36 +152,27 @@ __device__ __forceinline__ void wait_lgkm0() {
 }
 
 // kFast: the interleave and the block size are multiples of the tile, so the 32 tokens of a
-// tile are consecutive slots of one cache page.
+// tile are consecutive slots of one cache page.  kNt: the tile copies take the non-temporal
+// cache policy (one workgroup per item reads each tile: q_len = 1).
 //
-// Warp-specialised workgroup of 12 waves for 64 heads (two pairs of 16-head tiles).  Every
-// K / V operand read from LDS feeds two MFMAs (both head tiles of a pair):
-//   * score waves 0..3 = (head pair hp = w / 2, half kh = w % 2 of the 576 dims): for tile
-//     t, the partial S^T = K Q^T of both head tiles of the pair over their 288 dims
-//     (18 K reads, 36 MFMAs).  The two halves swap the partial scores of one head tile
-//     through LDS, so each finishes the online softmax of one head tile: running max,
-//     bf16 weights P and the factor that rescales the output accumulated so far, handed
-//     to the output waves through LDS;
-//   * output waves 4..11 = (head pair hp = (w - 4) / 4, quarter dq of the 512 value dims):
-//     O^T in AGPRs (both head tiles, 128 dims), one tile behind the score waves,
-//     O^T += V^T P^T (16 transposed V reads, 16 MFMAs per tile).
-// Waves are dealt round-robin over the SIMDs: each SIMD runs one score wave and two output
-// waves (68 MFMAs per tile).  Two barriers per tile: at barrier A of iteration t, tile t
-// has landed (copies paced by each wave's own vector-memory counter), P of tile t-1 is in
-// LDS and every read of tile t-2 is done, so its buffer takes the copy of tile t+2; at
-// barrier B the partial scores of tile t have been swapped.  The output waves split their
-// MFMAs over both phases, so the matrix cores stay busy while the softmax runs.
-template <bool kFast>
+// One wave issues its MFMAs in order, and a 16x16x32 MFMA leaves room for about two simple
+// vector instructions (or one exp2) beside it without slowing the matrix core (measured on
+// MI355X).  So the softmax of a tile is cut into 18 pieces of that size, one per k-step of
+// the next tile's S^T, and the tile copies are issued between the O^T MFMAs.
+template <bool kFast, bool kNt>
 __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
-  // Workgroup ids: the q_len * kGroups (query position, head group) workgroups of one work
-  // item are congruent mod 8 (same XCD) and adjacent in dispatch order.
+  // Workgroup ids (dealt round-robin over the 8 XCDs): the q_len workgroups (query
+  // positions) of one work item are congruent mod 8, and so are four consecutive work items
+  // (in dispatch order the full items of one request are consecutive): they share one XCD's
+  // L2 for the tiles and the query.  blk = 32 q_len a + 8 (4 qi + c) + x runs item
+  // 32 a + 4 x + c, position qi.
   const int blk = blockIdx.x;
-  const int ngroups = kGroups * a.q_len;
-  const int hgq = (blk / kXcds) % ngroups;
-  const int qi = hgq / kGroups, hg = hgq - qi * kGroups;
-  const int slot = (blk / (kXcds * ngroups)) * kXcds + blk % kXcds;
+  const int x8 = blk % kXcds;
+  const int grp = (blk / kXcds) % (4 * a.q_len);
+  const int qi = grp / 4;
+  const int slot = (blk / (kXcds * 4 * a.q_len)) * (kXcds * 4) + 4 * x8 + grp % 4;
   if (slot >= a.header[1]) return;
   const int4 it = a.items[slot];   // in dispatch order, longest first
   const int b = it.x, j0 = it.y;
@@ -202,466 +194,401 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const int32_t* btb = a.bt + (size_t)b * a.max_blocks;
   const char DCP_LDS* lds = (const char DCP_LDS*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-  const bool is_qk = w < kQkWaves;
   const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+  const bool copier = w < kCopyWaves;
 
-  // Page-contiguous tiles: a per-wave table of tile sources, lane k holding the first cache
-  // row of tile 64 * window + k (or ~0 for a bad page).  It is built by a lane-parallel walk
-  // and one gather of block-table entries, once per 64 tiles (the gather's vector-memory
-  // wait then drains the copies in flight, once per window), so locating a tile is one
-  // readlane: no scalar memory load inside the tile loop, whose counter the LDS operand
-  // waits share.
-  struct TileSrc {
-    const char* base;   // global address of the tile's first row
-    uint32_t lim;       // bytes of valid rows (slots past them re-read row 0, masked)
-    bool full;          // all 32 rows valid
+  // ---- tile tables (built by wave kBuilder): window W in half W & 1 of the table.
+  // stage(W) copies the block-table entries of window W's tokens (page-contiguous: of each
+  // tile's first token) into LDS by global_load_lds_dword; commit(W), one iteration later,
+  // turns them into cache rows (~0 for no token or a bad page).  The builder has no other
+  // vector-memory traffic in the tile loop, so its counter waits for exactly these copies.
+  constexpr int kWin = kFast ? kFastWin : kGenWin;
+  constexpr int kPasses = kFast ? 1 : kWinEntries / 64;   // 64 entries per pass
+  uint32_t DCP_LDS* const tab = (uint32_t DCP_LDS*)(smem + kTabOff);
+  const int32_t DCP_LDS* const stage = (const int32_t DCP_LDS*)(smem + kStageOff);
+  auto tab_entry = [&](int k, int i) -> uint32_t DCP_LDS* {
+    return tab + ((k / kWin) & 1) * kWinEntries + (k % kWin) * (kFast ? 1 : kTile) + i;
   };
-  uint32_t row_tab = 0;
-  auto build_table = [&](int win) {
-    const int tt = win * 64 + lane;
-    bool bad = false;
-    uint32_t row = ~0u;
-    if (tt < ntiles) {
-      const uint32_t t = dcp_walk_global_pos((uint32_t)(j0 + tt * kTile), a.rank, a.cp,
-                                             a.interleave);
-      const uint32_t lp = t / B;
-      const int32_t pg = btb[lp];
-      if (pg < 0 || (uint32_t)pg >= a.num_blocks) bad = true;
-      else row = (uint32_t)pg * B + (t - lp * B);
-    }
-    if (__ballot(bad) != 0 && threadIdx.x == 0) atomicOr(&a.header[0], kErrBlockId);
-    row_tab = row;
+  // entry e of window W: its tile and token, whether it exists, its global position t
+  auto entry_pos = [&](int W, int e, uint32_t& t) -> bool {
+    const int tile = W * kWin + (kFast ? e : e / kTile);
+    const int j = j0 + tile * kTile + (kFast ? 0 : e % kTile);
+    const bool valid = (!kFast || e < kWin) && tile < ntiles && j < j1;
+    t = valid ? dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave) : 0u;
+    return valid;
   };
-  if constexpr (kFast) build_table(0);
-  uint64_t vm_new = 0;
-  // source of tile ti
-  auto tile_src = [&](int ti) -> TileSrc {
-    if ((ti & 63) == 0 && ti > 0) build_table(ti >> 6);
-    const int nvalid = min(kTile, j1 - (j0 + ti * kTile));
-    const uint32_t row0 = __builtin_amdgcn_readlane(row_tab, ti & 63);
-    const bool ok = row0 != ~0u;
-    TileSrc ts;
-    ts.base = a.lat + (size_t)(ok ? row0 : 0u) * kRowBytes;
-    ts.full = ok && nvalid == kTile;
-    ts.lim = ok ? (uint32_t)nvalid * kRowBytes : 0u;
-    vm_new = ts.full ? 0xffffffffull : (ok ? ((1ull << nvalid) - 1) : 0ull);
-    return ts;
-  };
-  // mask of valid rows of tile ti (page-contiguous tiles: from the source table)
-  // General tiles: the cache row of every token of a window of kTWin tiles sits in LDS
-  // (~0 for no token or a bad page).  The score waves, which have no copies in flight,
-  // walk the tokens and load the block-table entries (gen_load) and store the rows
-  // (gen_store) a few tiles before the window is first used, so no block-table load ever
-  // waits inside the output waves, whose copies stay paced by the counter alone.
-  uint32_t DCP_LDS* const rowtab = (uint32_t DCP_LDS*)(smem + kTOff);
-  uint32_t gen_t[2];
-  int32_t gen_pg[2];
-  bool gen_ok[2];
-  auto gen_load = [&](int win) {
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int e = pass * (kQkWaves * 64) + w * 64 + lane;   // entry of the window
-      const int j = j0 + win * kTWin * kTile + e;
-      gen_ok[pass] = e < kTWin * kTile && j < j1;
-      gen_t[pass] = 0;
-      gen_pg[pass] = 0;
-      if (gen_ok[pass]) {
-        gen_t[pass] = dcp_walk_global_pos((uint32_t)j, a.rank, a.cp, a.interleave);
-        gen_pg[pass] = btb[gen_t[pass] / B];
-      }
+  // (the passes stay a loop: unrolled, their walks would be scheduled together and need
+  // registers the tile loop does not have)
+  auto stage_window = [&](int W) {
+    const uint32_t dst = lds_addr + kStageOff;
+#pragma unroll 1
+    for (int p = 0; p < kPasses; ++p) {
+      uint32_t t;
+      const bool valid = entry_pos(W, p * 64 + lane, t);
+      const int32_t* src = btb + (valid ? t / B : 0u);
+      asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+                   :
+                   : "v"(src), "{m0}"(dst + p * 256)
+                   : "memory");
     }
   };
-  auto gen_store = [&]() {
+  auto commit_window = [&](int W) {
+    wait_vmcnt<0>();   // the staged entries have landed
     bool bad = false;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int e = pass * (kQkWaves * 64) + w * 64 + lane;
-      if (e < kTWin * kTile) {
-        uint32_t row = ~0u;
-        if (gen_ok[pass]) {
-          const uint32_t lp = gen_t[pass] / B;
-          if (gen_pg[pass] < 0 || (uint32_t)gen_pg[pass] >= a.num_blocks) bad = true;
-          else row = (uint32_t)gen_pg[pass] * B + (gen_t[pass] - lp * B);
-        }
-        rowtab[e] = row;
+#pragma unroll 1
+    for (int p = 0; p < kPasses; ++p) {
+      const int e = p * 64 + lane;
+      uint32_t t;
+      uint32_t row = ~0u;
+      if (entry_pos(W, e, t)) {
+        const int32_t pg = stage[e];
+        if (pg < 0 || (uint32_t)pg >= a.num_blocks) bad = true;
+        else row = (uint32_t)pg * B + (t - (t / B) * B);
       }
+      if (!kFast || e < kWin)
+        *tab_entry(W * kWin + (kFast ? e : e / kTile), kFast ? 0 : e % kTile) = row;
     }
     if (__ballot(bad) != 0 && lane == 0) atomicOr(&a.header[0], kErrBlockId);
   };
-  // mask of valid rows of tile ti
-  auto tile_mask = [&](int ti) -> uint64_t {
+
+  // ---- copies (waves 0..2): slot s = 12 w + k of a tile, lane l holds LDS bytes
+  // 16 (64 s + l) of the tile = row r = (64 s + l) / 72, position c = (64 s + l) mod 72,
+  // which receives the row's chunk c ^ (r & 7).  The byte offset of slot k's source chunk
+  // within the tile (< 2^16) is a 16-bit entry of a per-thread LDS record (the tile loop
+  // has no registers to spare for twelve of them).
+  uint16_t DCP_LDS* const slot_rec = (uint16_t DCP_LDS*)(smem + kSlotOff) + threadIdx.x * 16;
+  if (copier) {
+#pragma unroll
+    for (int k = 0; k < kSlotsPerWave; ++k) {
+      const int q = (kSlotsPerWave * w + k) * 64 + lane;
+      const int r = q / kRowChunks;
+      slot_rec[k] = (uint16_t)(r * kRowBytes + ((q - r * kRowChunks) ^ (r & 7)) * 16);
+    }
+  }
+  // The copies of one tile: plan() reads where the tile comes from (and this thread's slot
+  // offsets), copy(k) issues slot k.
+  struct TileCopy {
+    uint32_t so[kSlotsPerWave / 2];   // slot offsets, two per register
+    const char* base;                 // page-contiguous tiles: the tile's first row
+    uint32_t dst;                     // LDS address of this wave's first slot
+    int nvalid;                       // page-contiguous tiles: rows holding tokens
+    int ti;                           // the tile (general tiles: its rows are in the table)
+    __device__ uint32_t off(int k) const { return (k & 1) ? so[k / 2] >> 16 : so[k / 2] & 0xffffu; }
+  };
+  auto plan_copy = [&](int ti) -> TileCopy {
+    TileCopy c;
+    const u32x4 lo = *(const u32x4 DCP_LDS*)slot_rec;
+    const u32x2 hi = *(const u32x2 DCP_LDS*)(slot_rec + 8);
+    c.so[0] = lo.x; c.so[1] = lo.y; c.so[2] = lo.z; c.so[3] = lo.w; c.so[4] = hi.x; c.so[5] = hi.y;
+    c.dst = lds_addr + (uint32_t)((ti % kNBuf) * kTileBytes + kSlotsPerWave * w * 1024);
+    c.ti = ti;
     if constexpr (kFast) {
-      (void)tile_src(ti);
-      return vm_new;
+      const uint32_t row0 = __builtin_amdgcn_readfirstlane(*tab_entry(ti, 0));
+      const bool ok = row0 != ~0u;
+      c.nvalid = ok ? min(kTile, j1 - (j0 + ti * kTile)) : 0;
+      c.base = a.lat + (size_t)(ok ? row0 : 0u) * kRowBytes;
+    }
+    return c;
+  };
+  auto copy_slot = [&](const TileCopy& c, int k) {
+    if constexpr (kFast) {
+      // rows past the valid ones re-read row 0 (their tokens are masked)
+      uint32_t voff = c.off(k);
+      if (c.nvalid != kTile) {   // uniform
+        const uint32_t r = voff / kRowBytes;
+        voff = (int)r < c.nvalid ? voff : voff - r * kRowBytes;
+      }
+      copy16_sbase<kNt>(c.dst + k * 1024, voff, c.base);
     } else {
-      const bool ok = lane < kTile && rowtab[(ti % kTWin) * kTile + (lane & (kTile - 1))] != ~0u;
-      return __ballot(ok);
+      // each copy takes the row of its token from the table (tokens without a valid row
+      // re-read row 0)
+      const uint32_t r = c.off(k) / kRowBytes;
+      const uint32_t row = *tab_entry(c.ti, (int)r);
+      const char* src = a.lat + (size_t)(row == ~0u ? 0u : row) * kRowBytes + (c.off(k) - r * kRowBytes);
+      copy16_vaddr<kNt>(c.dst + k * 1024, src);
     }
   };
-  if constexpr (!kFast) {
-    // window 0 before any copy
-    if (is_qk) {
-      gen_load(0);
-      gen_store();
+  auto issue_tile = [&](int ti) {
+    const TileCopy c = plan_copy(ti);
+#pragma unroll
+    for (int k = 0; k < kSlotsPerWave; ++k) copy_slot(c, k);
+  };
+  // mask of the valid tokens of tile ti (bit i = token i), wave-uniform
+  auto tile_mask = [&](int ti) -> uint32_t {
+    if constexpr (kFast) {
+      const uint32_t row0 = __builtin_amdgcn_readfirstlane(*tab_entry(ti, 0));
+      const int nvalid = row0 != ~0u ? min(kTile, j1 - (j0 + ti * kTile)) : 0;
+      return nvalid >= kTile ? 0xffffffffu : ((1u << nvalid) - 1u);
+    } else {
+      const bool ok = lane < kTile && *tab_entry(ti, lane & (kTile - 1)) != ~0u;
+      return (uint32_t)__ballot(ok);
     }
-    wait_lgkm0();
-    asm volatile("s_barrier" ::: "memory");
+  };
+
+  // ---- the query of this wave's heads (B operand of S^T = K Q^T):
+  // qreg[hh][ks] = dims 32 ks + 8 g .. + 8 of head 32 w + 16 hh + i16.  Its loads overlap
+  // the table build and the first tile copies; the tile-0 wait below covers them (they
+  // were issued first).
+  const int head0 = 32 * w + i16;
+  bf16x8 qreg[2][kKSteps];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint16_t* qrow = a.q + (orow + head0 + 16 * hh) * kDk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qreg[hh][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  }
+  // window 0 of the tile table before the first copy
+  if (w == kBuilder && ntiles > 0) {
+    stage_window(0);
+    commit_window(0);
+  }
+  wait_lgkm0();
+  asm volatile("s_barrier" ::: "memory");
+  // prologue: tiles 0..2 in flight
+  if (copier) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      if (k < ntiles) issue_tile(k);
   }
 
-  if (is_qk) {
-    // ================= score wave: head pair hp, dims 288 kh .. + 288 =================
-    const int hp = w >> 1, kh = w & 1;
-    const int own = 2 * hp + kh;   // local head tile whose softmax this wave finishes
-    // Barrier A of iteration t (both roles run ntiles + 1 iterations; the output waves'
-    // copies of tile t have landed).  Bare barriers: the fence of __syncthreads would also
-    // wait for the copies still in flight.
-    uint64_t vm0 = tile_mask(0);
-    uint64_t vm1 = ntiles > 1 ? tile_mask(1) : 0ull;
-    uint64_t vm2 = 0ull;
-    auto barrier_a = [&](int t) {
-      asm volatile("s_barrier" ::: "memory");
-      vm2 = t + 2 < ntiles ? tile_mask(t + 2) : 0ull;
-    };
-
-    const int head_p = 16 * (kHeadTiles * hg + 2 * hp) + i16;   // lane's head, tile 2 hp
-    // query (B operand of S^T = K Q^T): qreg[hh][j] = dims 32 (9 kh + j) + 8 g .. + 8 of
-    // head tile 2 hp + hh
-    bf16x8 qreg[2][kHalfSteps];
+  // O^T accumulators in AGPRs: every definition comes out of an AGPR-constrained asm
+  // statement, so the register allocator keeps the loop-carried accumulators there
+  f4 acc[2][kDvTiles];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const uint16_t* qrow =
-          a.q + (orow + head_p + 16 * hh) * kDk + 8 * g + 32 * kHalfSteps * kh;
+  for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int j = 0; j < kHalfSteps; ++j)
-        qreg[hh][j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j);
+    for (int i = 0; i < kDvTiles; ++i) {
+      acc[hh][i] = f4{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[hh][i]));
     }
-    // the query must have landed before the copy ring is paced by the counter alone
-    wait_vmcnt<0>();
-    // The query lives in AGPRs (the MFMAs read their B operand from there), leaving the
-    // VGPRs to the operand ring: both roles then fit three waves per SIMD.
+  // Wait states between the last accumulator MFMAs and VALU reads of the accumulators;
+  // every accumulator passes through an AGPR-constrained statement after them, so the
+  // reads cannot be hoisted above.
+  auto settle = [&]() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int j = 0; j < kHalfSteps; ++j) asm volatile("" : "+a"(qreg[hh][j]));
-    float m = neg_inf();   // running max (log2 units) of this lane's head of tile `own`
-    float negm = 0.f;      // -m, or 0 while m is -inf
-    float ls = 0.f;        // this lane's share of the running sum of weights
-    const int xk = i16 & 7;
-    const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
-    const int offk1 = i16 * kRowBytes + 16 * ((4 + g) ^ xk);
-    // partial scores: written for the partner's head tile, read for the own one
-    f4 DCP_LDS* xdst = (f4 DCP_LDS*)(smem + kXOff) + ((2 * hp + 1 - kh) * 64 + lane) * 2;
-    const f4 DCP_LDS* xsrc = (const f4 DCP_LDS*)(smem + kXOff) + (own * 64 + lane) * 2;
-    u32x4 DCP_LDS* pdst = (u32x4 DCP_LDS*)(smem + kPOff) + own * 64 + lane;
-    float DCP_LDS* adst = (float DCP_LDS*)(smem + kAOff) + own * 16 + i16;
+      for (int i = 0; i < kDvTiles; i += 4)
+        asm volatile("" : "+a"(acc[hh][i]), "+a"(acc[hh][i + 1]), "+a"(acc[hh][i + 2]),
+                     "+a"(acc[hh][i + 3]));
+  };
 
-    // Iteration t: phase 1 = tile t's partial scores (MFMAs) and the swap; phase 2 (after
-    // barrier B) = the online softmax of the own head tile and the hand-over of P.
-    for (int t = 0; t <= ntiles; ++t) {
-      wait_lgkm0();   // the previous tile's weights are in LDS before the barrier
-      barrier_a(t);
-      // general tiles: the window of tiles t+3 .. is built in this iteration (its first
-      // tile is first read at barrier A of the next one)
-      const bool gen_now = !kFast && (t + 3) % kTWin == 0 && t + 3 < ntiles;
-      if (gen_now) gen_load((t + 3) / kTWin);
-      f4 sm0 = {0.f, 0.f, 0.f, 0.f}, sm1 = {0.f, 0.f, 0.f, 0.f};   // own head tile
-      if (t < ntiles) {
-        const char DCP_LDS* tb = lds + (t % kNBuf) * kTileBytes;
-        // s[tt][hh]: token half tt, head tile 2 hp + hh (four independent MFMA chains)
-        f4 s[2][2];
+  // K operand (A of S^T): tile row 16 tt + i16, chunk 4 ks + g (position ^ (row & 7))
+  // (k-steps 2 m + 1 read chunk position ((4 + g) ^ xk) = (g ^ xk) ^ 4: offk0 ^ 64, the row
+  // offset being a multiple of 128)
+  const int xk = i16 & 7;
+  const int offk0 = i16 * kRowBytes + 16 * (g ^ xk);
+  // V^T operand (A of O^T): this lane addresses tile row 4 g + i16 / 4 (+ 16), bytes
+  // 8 (i16 mod 4) of the 32 value bytes of dims 16 dt .. 16 dt + 15
+  const int rv = 4 * g + (i16 >> 2);
+  const int xv = rv & 7;
+  const int qv = (i16 >> 1) & 1;
+  // dims 16 dt.. sit at chunk position (2 (dt mod 4) + qv) ^ xv = ((qv ^ xv) ^ 2 (dt mod 4))
+  // of 8-chunk group dt / 4: offv0 ^ 32 (dt mod 4), plus 128 (dt / 4)
+  const int offv0 = rv * kRowBytes + 16 * (qv ^ xv) + (i16 & 1) * 8;
+
+  auto kread = [&](const char DCP_LDS* tb, int ks, bf16x8 (&k2)[2]) {
+    const int o = ((ks & 1) ? (offk0 ^ 64) : offk0) + 128 * (ks >> 1);
+    k2[0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + o);
+    k2[1] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + 16 * kRowBytes + o);
+  };
+  // S^T MFMAs: compiler builtins, so that the hazard recognizer keeps every later write of
+  // their operand registers clear of the matrix core's reads.  Their accumulators stay in
+  // VGPRs (the file is built with -amdgpu-mfma-vgpr-form; the AGPRs all hold O^T).
+  auto qk_step = [&](const bf16x8 (&k2)[2], int ks, f4 (&s)[2][2]) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) s[tt][hh] = f4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 kop[kAheadK + 1][2];
-        auto kread = [&](int j) {
-          const int ks = kHalfSteps * kh + j;
-          const int o = ((ks & 1) ? offk1 : offk0) + 128 * (ks >> 1);
-          kop[j % (kAheadK + 1)][0] = *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + o);
-          kop[j % (kAheadK + 1)][1] =
-              *reinterpret_cast<const bf16x8 DCP_LDS*>(tb + 16 * kRowBytes + o);
-        };
-#pragma unroll
-        for (int j = 0; j < kAheadK; ++j) kread(j);
-#pragma unroll
-        for (int j = 0; j < kHalfSteps; ++j) {
-          if (j + kAheadK < kHalfSteps) kread(j + kAheadK);
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-              s[tt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (kAheadK + 1)][tt],
-                                                                  qreg[hh][j], s[tt][hh], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // hand the partner's head tile over; keep the own one
-        xdst[0] = kh ? s[0][0] : s[0][1];
-        xdst[1] = kh ? s[1][0] : s[1][1];
-        sm0 = kh ? s[0][1] : s[0][0];
-        sm1 = kh ? s[1][1] : s[1][0];
+      for (int hh = 0; hh < 2; ++hh) {
+        s[tt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            k2[tt], qreg[hh][ks], ks == 0 ? f4{0.f, 0.f, 0.f, 0.f} : s[tt][hh], 0, 0, 0);
       }
-      wait_lgkm0();   // the partial scores are in LDS before the mid barrier
-      asm volatile("s_barrier" ::: "memory");   // barrier B
-      // every wave has read the table entries of tile t+2 (at barrier A): the old window is
-      // done with
-      if (gen_now) gen_store();
-      if (t < ntiles) {
-        const f4 s0 = sm0 + xsrc[0];
-        const f4 s1 = sm1 + xsrc[1];
-        // scores: x[i] is token 4 g + i, x[4 + i] token 16 + 4 g + i; masked rows -> -inf
-        float x[8];
+  };
+
+  float m[2] = {neg_inf(), neg_inf()};   // running max (log2 units) of this lane's heads
+  float negm[2] = {0.f, 0.f};            // -m, or 0 while m is -inf
+  float ls[2] = {0.f, 0.f};              // this lane's share of the running sums
+
+  f4 sc[2][2];   // S^T of the tile whose softmax runs next: [token half][head tile]
+  // tile 0 (and the query, loaded before it) has landed in every wave's copies
+  if (ntiles > 2) wait_vmcnt<2 * kSlotsPerWave>();
+  else if (ntiles > 1) wait_vmcnt<kSlotsPerWave>();
+  else wait_vmcnt<0>();
+  asm volatile("s_barrier" ::: "memory");
+  uint32_t vmask_next = 0;
+  if (ntiles > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = s0[i];
-          x[4 + i] = s1[i];
-        }
-        if ((uint32_t)vm0 != 0xffffffffu) {   // partial tile (uniform); the empty asm keeps
-          asm volatile("");                   // the masking a branch
-          const uint32_t lo = (uint32_t)(vm0 >> (4 * g)) & 0xFu;
-          const uint32_t hi = (uint32_t)(vm0 >> (16 + 4 * g)) & 0xFu;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[i] = ((lo >> i) & 1u) ? x[i] : neg_inf();
-            x[4 + i] = ((hi >> i) & 1u) ? x[4 + i] : neg_inf();
-          }
-        }
-        // tile max of this lane's head: within the lane, then across the four 16-lane
-        // rows (which hold the same head) with two swaps
-        float tm = max_f(max_f(max_f(x[0], x[1]), max_f(x[2], x[3])),
-                         max_f(max_f(x[4], x[5]), max_f(x[6], x[7])));
-        {
-          const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tm),
-                                                             __float_as_uint(tm), false, false);
-          tm = max_f(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-          const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tm),
-                                                             __float_as_uint(tm), false, false);
-          tm = max_f(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-        }
-        const float tmax = tm * a.sl2;
-        // The running max only moves when a head's tile max exceeds it by more than
-        // kRescaleSlack (always on the first tile with valid tokens).  Between raises the
-        // weights stay below 2^kRescaleSlack, exactly representable in bf16 / fp32, and
-        // the final normalisation by the running sum is exact either way.
-        const bool up = tmax > m + kRescaleSlack;
-        const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
-        if (up) {
-          m = tmax;
-          negm = -tmax;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(x[i], a.sl2, negm));
-        ls = ls * alpha + (((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7])));
-        // B operand of O^T += V^T P^T: k slots 8 g .. 8 g + 7 = tokens 4 g + [0, 4) and
-        // 16 + 4 g + [0, 4); the output lanes with the same index read these 16 bytes
-        *pdst = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-        if (g == 0) *adst = alpha;
-      }
-      vm0 = vm1;
-      vm1 = vm2;
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      bf16x8 k2[2];
+      kread(lds, ks, k2);
+      qk_step(k2, ks, sc);
     }
-    // ---- per-head normalisation for the output waves, and the lse
-    float lt = ls;
-    {
-      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt),
-                                                         false, false);
-      lt = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt),
-                                                         false, false);
-      lt = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-    }
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : neg_inf();
-    if (g == 0) {
-      const int head = head_p + 16 * kh;
-      ((float DCP_LDS*)(smem + kFOff))[own * 16 + i16] = inv;
-      if (single) a.lse_out[orow + head] = lse;
-      else a.plse[prow + head] = lse;
-    }
+    vmask_next = tile_mask(0);
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t + 1 has landed (only tile t + 2 may still be in flight); after the barrier
+    // every wave is past iteration t - 1, so buffer (t - 1) mod 4 takes tile t + 3
+    const bool staged = w == kBuilder && t > 0 && (t - 1) % kWin == 0 &&
+                        ((t - 1) / kWin + 1) * kWin < ntiles;
+    if (staged) wait_vmcnt<0>();
+    else if (t + 2 < ntiles) wait_vmcnt<kSlotsPerWave>();
+    else wait_vmcnt<0>();
     wait_lgkm0();
     asm volatile("s_barrier" ::: "memory");
-  } else {
-    // ============ output wave: head pair hp, value dims 128 dq .. + 128 ============
-    const int pv = w - kQkWaves;
-    const int hp = pv >> 2, dq = pv & 3;
-    // ---- HBM -> LDS tile copies, all issued by the output waves.  A tile is 36 slots of
-    // 1 KiB (64 lanes x 16 B); slot s, lane l holds chunk (q mod 72) ^ (row & 7) of tile row
-    // q / 72, q = 64 s + l.  Output wave p copies 5 slots from 5p (p < 4) or 4 slots from
-    // 20 + 4 (p - 4).
-    const int pvw = w - kQkWaves;
-    const int slot0 = pvw < 4 ? kSlotsHi * pvw : 4 * kSlotsHi + kSlotsLo * (pvw - 4);
-    const int nslots = is_qk ? 0 : (pvw < 4 ? kSlotsHi : kSlotsLo);
-    uint32_t slot_off[kSlotsHi], slot_col[kSlotsHi];
-    int slot_row[kSlotsHi];
+    // tables: window W + 1 is staged at iteration W * kWin and committed one iteration later
+    if (staged) commit_window((t - 1) / kWin + 1);
+    if (w == kBuilder && t % kWin == 0 && (t / kWin + 1) * kWin < ntiles)
+      stage_window(t / kWin + 1);
+    // tokens of tile t that do not exist (a partial tile, a bad page): scores -inf (a
+    // uniform branch, taken on few tiles)
+    const uint32_t vmask = vmask_next;
+    if (vmask != 0xffffffffu) {
+      const uint32_t mb = vmask >> (4 * g);   // bit e: token 4 g + e, bit 16 + e: 16 + 4 g + e
 #pragma unroll
-    for (int k = 0; k < kSlotsHi; ++k) {
-      const int sl = max(slot0 + k, 0) * 64 + lane;
-      const int r = min(sl / kRowChunks, kTile - 1);   // slots a wave does not copy: unused
-      slot_row[k] = r;
-      slot_col[k] = (uint32_t)(((sl - r * kRowChunks) ^ (r & 7)) * 16);
-      slot_off[k] = (uint32_t)r * kRowBytes + slot_col[k];
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          sc[0][hh][e] = ((mb >> e) & 1u) ? sc[0][hh][e] : neg_inf();
+          sc[1][hh][e] = ((mb >> (16 + e)) & 1u) ? sc[1][hh][e] : neg_inf();
+        }
     }
-    // all of this wave's copies of tile ti; returns the mask of valid rows
-    auto issue_tile = [&](int ti) -> uint64_t {
-      const uint32_t dst = lds_addr + (uint32_t)((ti % kNBuf) * kTileBytes + slot0 * 1024);
-      if constexpr (kFast) {
-        const TileSrc ts = tile_src(ti);
+
+    // ---- S^T of tile t + 1 (computed also after the last tile, on a buffer of stale data,
+    // and then unused: the loop body stays one block) with the online softmax of tile t
+    // (base 2) cut into one piece per k-step.  Scores stay unscaled until the exp2:
+    // scale * log2(e) > 0 keeps the maxima.
+    f4 sn[2][2];
+    const char DCP_LDS* tbn = lds + ((t + 1) % kNBuf) * kTileBytes;
+    constexpr int kAheadK = ahead_k<kFast>();
+    bf16x8 kop[kAheadK + 1][2];
 #pragma unroll
-        for (int k = 0; k < kSlotsHi; ++k) {
-          if (k < nslots) {
-            const uint32_t voff =
-                ts.full ? slot_off[k] : (slot_off[k] < ts.lim ? slot_off[k] : slot_col[k]);
-            copy16_sbase<false>(dst + k * 1024, voff, ts.base);
-          }
-        }
-        return vm_new;
+    for (int ks = 0; ks < kAheadK; ++ks) kread(tbn, ks, kop[ks]);
+    float tm[2], alpha[2], p[2][8];
+    bool grow = false;   // this lane's accumulators need rescaling
+    bf16x8 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + kAheadK < kKSteps) kread(tbn, ks + kAheadK, kop[(ks + kAheadK) % (kAheadK + 1)]);
+      qk_step(kop[ks % (kAheadK + 1)], ks, sn);
+      if (ks <= 1) {
+        // the lane's max of head tile hh over its 8 tokens
+        const int hh = ks;
+        const f4 u = sc[0][hh], v = sc[1][hh];
+        tm[hh] = max_f(max_f(max_f(u[0], u[1]), max_f(u[2], u[3])),
+                       max_f(max_f(v[0], v[1]), max_f(v[2], v[3])));
+      } else if (ks <= 3) {
+        const int hh = ks - 2;
+        tm[hh] = rows_max(tm[hh]) * a.sl2;   // the head's max over the tile (log2 units)
+      } else if (ks <= 5) {
+        // The running max only moves when the tile's max exceeds it by more than
+        // kRescaleSlack (always on the first tile with a valid token).  In between the
+        // weights stay below 2^kRescaleSlack and the final normalisation by the running sum
+        // is exact for any reference max.
+        const int hh = ks - 4;
+        const bool up = tm[hh] > m[hh] + kRescaleSlack;
+        alpha[hh] = up ? __builtin_amdgcn_exp2f(m[hh] - tm[hh]) : 1.f;   // m = -inf -> 0
+        grow = grow || (up && m[hh] != neg_inf());   // accumulators are 0 while m = -inf
+        m[hh] = up ? tm[hh] : m[hh];
+        negm[hh] = up ? -tm[hh] : negm[hh];
+      } else if (ks <= 13) {
+        // two weights per k-step: p = exp2(scale log2e s - m); masked tokens give 0
+        const int i = 2 * (ks - 6);           // 0 .. 14 over [hh][tt][e]
+        const int hh = i >> 3, tt = (i >> 2) & 1, e = i & 3;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          p[hh][4 * tt + e + u] =
+              __builtin_amdgcn_exp2f(fmaf(sc[tt][hh][e + u], a.sl2, negm[hh]));
+      } else if (ks <= 15) {
+        const int hh = ks - 14;
+        const float* q = p[hh];
+        ls[hh] = fmaf(ls[hh], alpha[hh],
+                      ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
       } else {
-        // general tiles: each copy takes the row of its token from the LDS table (rows
-        // without a valid token re-read row 0; their tokens are masked)
-        const uint32_t DCP_LDS* tr = rowtab + (ti % kTWin) * kTile;
-#pragma unroll
-        for (int k = 0; k < kSlotsHi; ++k) {
-          if (k < nslots) {
-            const uint32_t r = tr[slot_row[k]];
-            const uint32_t rr = r == ~0u ? 0u : r;
-            copy16_vaddr<false>(dst + k * 1024, a.lat + (size_t)rr * kRowBytes + slot_col[k]);
-          }
-        }
-        return 0ull;
+        // B operand of O^T += V^T P^T: k slots 8 g .. 8 g + 7 = tokens 4 g + [0, 4) and
+        // 16 + 4 g + [0, 4)
+        const int hh = ks - 16;
+        const float* q = p[hh];
+        pb[hh] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]),
+                                                  pack_bf16x2(q[4], q[5]), pack_bf16x2(q[6], q[7])});
+        // computed here, between the MFMAs, not sunk past the rescale branch
+        asm volatile("" : "+v"(pb[hh]), "+v"(ls[hh]));
       }
-    };
-
-    // prologue: tiles 0 and 1 in flight
-    if (ntiles > 0) (void)issue_tile(0);
-    if (ntiles > 1) (void)issue_tile(1);
-
-    // Barrier A of iteration t: this wave's copies of tile t have landed (those of tile t+1
-    // may still fly), then every wave's have; tile t+2 starts.  Bare barriers: the fence of
-    // __syncthreads would also wait for the copies still in flight.
-    auto barrier_a = [&](int t) {
-      if (t < ntiles) {
-        if (t + 1 < ntiles) {
-          if (nslots == kSlotsHi) wait_vmcnt<kSlotsHi>();
-          else wait_vmcnt<kSlotsLo>();
-        } else {
-          wait_vmcnt<0>();
-        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (__ballot(grow) != 0) {   // uniform, rare: rescale the accumulators
+      settle();
+#pragma unroll
+      for (int i = 0; i < kDvTiles; ++i) {
+        acc[0][i] *= alpha[0];
+        acc[1][i] *= alpha[1];
+        asm volatile("" : "+a"(acc[0][i]), "+a"(acc[1][i]));
       }
-      asm volatile("s_barrier" ::: "memory");
-      if (t + 2 < ntiles) (void)issue_tile(t + 2);
-    };
+    }
 
-
-    const int head_p = 16 * (kHeadTiles * hg + 2 * hp) + i16;   // lane's head, tile 2 hp
-    // Every definition of an accumulator comes out of an AGPR-constrained asm statement,
-    // so the register allocator keeps the loop-carried accumulators in AGPRs.
-    f4 acc[2][kQuarterTiles];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < kQuarterTiles; ++i) {
-        acc[hh][i] = f4{0.f, 0.f, 0.f, 0.f};
-        asm volatile("" : "+a"(acc[hh][i]));
-      }
-    // Wait states between the last accumulator MFMAs and VALU reads of the accumulators;
-    // every accumulator passes through an AGPR-constrained statement here, so the reads
-    // cannot be hoisted above it.
-    auto settle_acc = [&]() {
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                   : "+a"(acc[0][4]), "+a"(acc[0][5]), "+a"(acc[0][6]), "+a"(acc[0][7]),
-                     "+a"(acc[1][4]), "+a"(acc[1][5]), "+a"(acc[1][6]), "+a"(acc[1][7]));
-      asm volatile(""
-                   : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
-                     "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
-    };
-    // V^T operand (A of O^T = V^T P^T) for value-dim tile dt of this wave's quarter
-    const int rv = 4 * g + (i16 >> 2);
-    const int xv = rv & 7;
-    const int qv = (i16 >> 1) & 1;
-    int offv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      offv[u] = rv * kRowBytes + 16 * ((2 * u + qv) ^ xv) + (i16 & 1) * 8 + dq * 256;
-    const u32x4 DCP_LDS* psrc = (const u32x4 DCP_LDS*)(smem + kPOff) + 2 * hp * 64 + lane;
-    const float DCP_LDS* asrc = (const float DCP_LDS*)(smem + kAOff) + 2 * hp * 16 + i16;
-
-    // Iteration t: phase 1 = P of tile t-1 (written by the score waves in phase 2 of the
-    // previous iteration), the rescale, and the first kPhase1Tiles dv tiles; phase 2 = the
-    // other dv tiles, while the score waves run the softmax.
-    for (int t = 0; t <= ntiles; ++t) {
-      barrier_a(t);
-      const int u = t - 1;
-      const char DCP_LDS* tb = lds + ((u + kNBuf) % kNBuf) * kTileBytes;
+    // ---- O^T += V^T P^T of tile t, 16 value dims per MFMA pair; the copies of tile t + 3
+    // go out between them, one per two or three value tiles
+    {
+      const char DCP_LDS* tb = lds + (t % kNBuf) * kTileBytes;
       auto vop = [&](int dt) -> bf16x8 {
-        const int o = offv[dt & 3] + 128 * (dt >> 2);
+        const int o = (offv0 ^ (32 * (dt & 3))) + 128 * (dt >> 2);
         const u32x2 v0 = lds_tr16(tb + o);
         const u32x2 v1 = lds_tr16(tb + 16 * kRowBytes + o);
         return __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
       };
-      bf16x8 pb0, pb1;
+      const bool copies = copier && t + 3 < ntiles;
+      TileCopy cp;
+      if (copies) cp = plan_copy(t + 3);
+      if (t + 1 < ntiles) vmask_next = tile_mask(t + 1);
       bf16x8 va[kAheadV + 1];
-      if (t >= 1) {
-        pb0 = __builtin_bit_cast(bf16x8, psrc[0]);
-        pb1 = __builtin_bit_cast(bf16x8, psrc[64]);
-        const float alpha0 = asrc[0], alpha1 = asrc[16];
 #pragma unroll
-        for (int dt = 0; dt < kAheadV; ++dt) va[dt] = vop(dt);
-        if (__ballot(alpha0 != 1.f || alpha1 != 1.f) != 0) {
-          settle_acc();
+      for (int dt = 0; dt < kAheadV; ++dt) va[dt] = vop(dt);
 #pragma unroll
-          for (int i = 0; i < kQuarterTiles; ++i) {
-            acc[0][i] *= alpha0;
-            acc[1][i] *= alpha1;
-            asm volatile("" : "+a"(acc[0][i]), "+a"(acc[1][i]));
-          }
-        }
+      for (int dt = 0; dt < kDvTiles; ++dt) {
+        if (dt + kAheadV < kDvTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
+        if (dt == 0) mfma_acc<true>(acc[0][dt], va[dt % (kAheadV + 1)], pb[0]);
+        else mfma_acc<false>(acc[0][dt], va[dt % (kAheadV + 1)], pb[0]);
+        mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb[1]);
 #pragma unroll
-        for (int dt = 0; dt < kPhase1Tiles; ++dt) {
-          if (dt + kAheadV < kQuarterTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
-          if (dt == 0) mfma_acc<true>(acc[0][dt], va[dt % (kAheadV + 1)], pb0);
-          else mfma_acc<false>(acc[0][dt], va[dt % (kAheadV + 1)], pb0);
-          mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      asm volatile("s_barrier" ::: "memory");   // barrier B
-      if (t >= 1) {
-#pragma unroll
-        for (int dt = kPhase1Tiles; dt < kQuarterTiles; ++dt) {
-          if (dt + kAheadV < kQuarterTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
-          mfma_acc<false>(acc[0][dt], va[dt % (kAheadV + 1)], pb0);
-          mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int k = 0; k < kSlotsPerWave; ++k)
+          if (dt == 1 + (k * 8) / 3 && copies) copy_slot(cp, k);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    asm volatile("s_barrier" ::: "memory");
-    // ---- finalize: lane holds dims 128 dq + 16 dt + 4 g + [0, 4) of its heads
-    const float inv0 = ((const float DCP_LDS*)(smem + kFOff))[2 * hp * 16 + i16];
-    const float inv1 = ((const float DCP_LDS*)(smem + kFOff))[(2 * hp + 1) * 16 + i16];
-    settle_acc();
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int head = head_p + 16 * hh;
-      float* dst = (single ? static_cast<float*>(a.o_out) + (orow + head) * kDv
-                           : a.po + (prow + head) * kDv) +
-                   dq * 128;
-      uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + (orow + head) * kDv + dq * 128;
-      const float inv = hh ? inv1 : inv0;
-      if (single && a.o_bf16) {   // uniform
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int dt = 0; dt < kQuarterTiles; ++dt) {
-          const f4 v = acc[hh][dt] * inv;
-          *reinterpret_cast<uint2*>(dstb + 16 * dt + 4 * g) =
-              make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                         f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
-        }
-      } else {
+      for (int hh = 0; hh < 2; ++hh) sc[tt][hh] = sn[tt][hh];
+  }
+
+  // ---- finalize: O = acc / l per head, lse = (m + log2 l) ln 2
+  settle();
 #pragma unroll
-        for (int dt = 0; dt < kQuarterTiles; ++dt) {
-          const f4 v = acc[hh][dt] * inv;
-          *reinterpret_cast<f4*>(dst + 16 * dt + 4 * g) = v;
-        }
+  for (int hh = 0; hh < 2; ++hh) {
+    const float lt = rows_sum(ls[hh]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (m[hh] + __log2f(lt)) * kLn2 : neg_inf();
+    const int head = head0 + 16 * hh;
+    if (g == 0) {
+      if (single) a.lse_out[orow + head] = lse;
+      else a.plse[prow + head] = lse;
+    }
+    // lane holds dims 16 dt + 4 g + [0, 4) of its head
+    if (single && !a.o_bf16) {   // uniform
+      float* dst = static_cast<float*>(a.o_out) + (orow + head) * kDv + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < kDvTiles; ++dt)
+        *reinterpret_cast<f4*>(dst + 16 * dt) = acc[hh][dt] * inv;
+    } else {
+      uint16_t* dst = (single ? static_cast<uint16_t*>(a.o_out) + (orow + head) * kDv
+                              : a.po + (prow + head) * kDv) + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < kDvTiles; ++dt) {
+        const f4 v = acc[hh][dt] * inv;
+        *reinterpret_cast<uint2*>(dst + 16 * dt) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
   }
@@ -693,16 +620,22 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   k.off = ws.off;
   k.items = ws.items;
   k.plse = ws.plse;
-  k.po = ws.po;
-  const int64_t groups8 = (max_items + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(groups8 * kXcds * kGroups * a.rows.q_len));
+  k.po = static_cast<uint16_t*>(ws.po);
+  const int64_t groups32 = (max_items + 4 * kXcds - 1) / (4 * kXcds);
+  const dim3 grid((unsigned)(groups32 * 4 * kXcds * a.rows.q_len));
   const bool fast = (a.interleave % kTile) == 0 && (a.block_size % kTile) == 0;
-  if (fast)
-    hipExtLaunchKernelGGL(mla_shard_kernel<true>, grid, dim3(kWaves * 64), 0, stream, ev0, ev1, 0,
-                          k);
-  else
-    hipExtLaunchKernelGGL(mla_shard_kernel<false>, grid, dim3(kWaves * 64), 0, stream, ev0, ev1,
-                          0, k);
+  const bool nt = a.rows.q_len == 1;
+#define DCP_MLA_LAUNCH(F, N)                                                                 \
+  hipExtLaunchKernelGGL((mla_shard_kernel<F, N>), grid, dim3(kWaves * 64), 0, stream, ev0, ev1, \
+                        0, k)
+  if (fast) {
+    if (nt) DCP_MLA_LAUNCH(true, true);
+    else DCP_MLA_LAUNCH(true, false);
+  } else {
+    if (nt) DCP_MLA_LAUNCH(false, true);
+    else DCP_MLA_LAUNCH(false, false);
+  }
+#undef DCP_MLA_LAUNCH
   return hipGetLastError();
 }
 

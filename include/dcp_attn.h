@@ -118,7 +118,11 @@ size_t dcp_workspace_size(const dcp_attn_desc* desc, int batch, int64_t max_seq_
  *                int32 is the device error word (DCP_DEVERR_*) of the latest call.  It
  *                holds the call's plan and split partials until the call's kernels end:
  *                calls in flight at the same time need workspaces of their own (calls in
- *                order on one stream may share one).
+ *                order on one stream may share one).  A request's shard may be cut into
+ *                several work items whose partials are combined by their LSE; the GQA
+ *                kernels keep those split partials in float32, the MLA kernel in bf16
+ *                (round to nearest even; their LSE stays float32), which halves the bytes
+ *                of the 512-wide latent rows.
  * Returns DCP_OK or a negative dcp_status (nothing launched). */
 int dcp_attn_shard(const dcp_attn_desc* desc, const void* q, const void* kv_pages,
                    const void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
@@ -178,7 +182,7 @@ int dcp_attn_shard_mq_timed(const dcp_attn_desc* desc, int q_len, const void* q,
  *              value the float32 result rounded to nearest even.  The partials every rank
  *              exchanges and the merge reads then take half the bytes (the blog's "DCP
  *              execution flow" exchanges partial outputs with their LSE; the LSE stays
- *              float32).  Split partials inside the workspace stay float32.
+ *              float32).  Split partials inside the workspace are as in dcp_attn_shard.
  *   ev_begin, ev_end   nullable; as in dcp_attn_shard_timed.
  * Every other argument, the workspace (dcp_workspace_size_mq) and the errors are as for
  * dcp_attn_shard_mq; dcp_attn_shard, _timed, _mq and _mq_timed are this call with

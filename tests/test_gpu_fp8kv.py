@@ -82,9 +82,9 @@ def test_fp8kv_bf16_partials(gpu_lib):
 
 
 def test_fp8kv_rejects_unsupported(gpu_lib):
-    """A group of 32 query heads per KV head, float32 queries, missing scales: refused
-    before any launch."""
-    w = F.with_(name="fp8_g32", batch=1, num_q_heads=32, lengths=(100,), seed=107)
+    """A group of 80 query heads per KV head (more than 64 rows), float32 queries, missing
+    scales: refused before any launch."""
+    w = F.with_(name="fp8_g80", batch=1, num_q_heads=80, lengths=(100,), seed=107)
     inp = wl.make_inputs(w, device="cuda")
     with pytest.raises(dca.DCPError):
         dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"],

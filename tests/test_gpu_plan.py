@@ -66,7 +66,7 @@ def test_plan(gpu_lib, w, kind, rank):
     rows = w.q_len * (w.num_q_heads // w.num_kv_heads)
     slices = 2 if (kind == dca.GQA and w.dtype == "bf16" and rows > 32) else 1
     target = (max(1, cus * 2 // (w.num_kv_heads * slices)) if kind == dca.GQA
-              else max(1, cus // 2))
+              else max(1, cus // w.q_len))
     assert chunk % tile == 0 and chunk > 0
     assert n <= target + w.batch
     lens = [int(x) for x in inp["seq_lens"].cpu()]

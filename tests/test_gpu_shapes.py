@@ -4,8 +4,9 @@ Supported: bf16 with head_dim 128 or f32 with head_dim 64, and any group G = Hq 
 q_len * G <= 64 query rows per KV head ("GQA backend" of the blog names the Qwen3 and Llama
 families, whose groups include 3, 5, 6 and 7).  Every supported (dtype, G, q_len) runs a
 small ragged two-rank case checked against the oracle (every request, rank and head, and
-the merge); every unsupported (dtype, head_dim, G, q_len) must return DCP_EUNSUPPORTED from
-dcp_attn_shard_mq without launching (the outputs keep their sentinel values)."""
+the merge), for bf16 and f32 caches and for an fp8 cache (bf16 queries); every unsupported
+(dtype, head_dim, G, q_len) must return DCP_EUNSUPPORTED from dcp_attn_shard_mq without
+launching (the outputs keep their sentinel values)."""
 import ctypes
 
 import pytest
@@ -37,6 +38,25 @@ def test_supported_shape_parity(gpu_lib, dtype, g, q_len):
     w = base.with_(name=f"shape_{dtype}_g{g}_q{q_len}", batch=2, num_q_heads=g * hkv,
                    num_kv_heads=hkv, block_size=16, cp_size=2, interleave=16,
                    lengths=(q_len + 1, 700), q_len=q_len, seed=300 + g * 8 + q_len)
+    print(f"[shapes] {w.name}", flush=True)
+    inp = wl.make_inputs(w, device="cuda")
+    o_parts, l_parts = run_shards(inp, dca.GQA, w.cp_size, w.interleave, w.scale)
+    o_m, l_m = dca.merge(o_parts, l_parts)
+    torch.cuda.synchronize()
+    check_requests(inp, dca.GQA, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
+                   range(w.batch), w.name)
+
+
+FP8_CASES = [(g, ql) for g in (3, 5, 7, 12, 21, 32, 64) for ql in (1, 2, 3, 4) if g * ql <= 64]
+
+
+@pytest.mark.parametrize("g,q_len", FP8_CASES, ids=[f"fp8-g{g}-q{ql}" for g, ql in FP8_CASES])
+def test_supported_shape_parity_fp8_cache(gpu_lib, g, q_len):
+    """The fp8 KV cache takes the same group contract (bf16 queries, head_dim 128)."""
+    hkv = 2 if g <= 8 else 1
+    w = wl.GQA_SHARE_FP8.with_(name=f"shape_fp8_g{g}_q{q_len}", batch=2, num_q_heads=g * hkv,
+                               num_kv_heads=hkv, block_size=16, cp_size=2, interleave=16,
+                               lengths=(q_len + 1, 700), q_len=q_len, seed=500 + g * 8 + q_len)
     print(f"[shapes] {w.name}", flush=True)
     inp = wl.make_inputs(w, device="cuda")
     o_parts, l_parts = run_shards(inp, dca.GQA, w.cp_size, w.interleave, w.scale)
