@@ -8,8 +8,10 @@ on 1 KV head, head dim 128, bf16 cache in 128-token pages, DCP size 2 with inter
 
 Printed: one JSON line with the throughput (KV tokens of context attended per second), the
 roofline of the dominant kernel (the GQA shard kernel, timed with HIP events recorded on
-its own stream around every launch) and the CPU oracle timed on a bounded sample of the
-same workload.  `secondary` adds the MLA shard kernel (MFMA utilisation) and the 8-way
+its own stream around every launch), the CPU oracle timed on a bounded sample of the
+same workload, and `accuracy`: the oracle's verdict on sampled requests of every timed
+workload, read back from the outputs of the timed launches themselves (both oracle legs
+are skipped with --no-cpu-baseline).  `secondary` adds the MLA shard kernel (MFMA utilisation) and the 8-way
 merge on the MLA decode workload.
 """
 import argparse
@@ -153,6 +155,90 @@ def cpu_baseline(w, inp, seconds_target=12.0, max_requests=8, max_passes=200):
                       f"request in float64 numpy ({t_total:.1f} s of oracle time)"}
 
 
+def keep_sample(samples, w, inp, bufs, requests):
+    """Host copies of what sampled requests read (query, their pages compacted, a block-table
+    row addressing the copy) and of what the timed path wrote for them (every rank's
+    partial and the merged output), for the oracle comparison after the timed work."""
+    import numpy as np
+    if samples is None:
+        return
+    o_parts, l_parts, o, lse = bufs
+    B = w.block_size
+    rows = []
+    for b in requests:
+        L = int(inp["seq_lens"][b].item())
+        npages = (L + B - 1) // B
+        pages = inp["block_table"][b, :npages].long()
+        h = {"b": int(b), "L": L, "row": np.arange(npages),
+             "q": inp["q"][b].float().cpu().numpy().astype(np.float64),
+             "o_parts": o_parts[:, b].float().cpu().numpy(),
+             "l_parts": l_parts[:, b].float().cpu().numpy(),
+             "o": o[b].float().cpu().numpy(), "lse": lse[b].float().cpu().numpy()}
+        if w.kind == "gqa":
+            h["k"] = inp["k_pages"][pages].float().cpu().numpy().astype(np.float64)
+            h["v"] = inp["v_pages"][pages].float().cpu().numpy().astype(np.float64)
+        else:
+            h["lat"] = inp["latent_pages"][pages].float().cpu().numpy().astype(np.float64)
+        rows.append(h)
+    samples[w.name] = (w, rows)
+
+
+def accuracy(samples):
+    """Error of the timed path's outputs against the oracle on the kept requests, per
+    workload: merged O (max abs; max over head rows of max|err| / max|ref|; max over head
+    rows and over the whole sample of the relative L2 error), merged LSE (max abs), and the
+    largest per-row relative L2 error of any rank's partial O."""
+    import numpy as np
+    from oracle import dcp_oracle as orc
+    out = {}
+    for name, (w, rows) in samples.items():
+        t0 = time.perf_counter()
+        ea = er = el = 0.0
+        pl2 = 0.0
+        num = den = 0.0
+        for h in rows:
+            if w.kind == "gqa":
+                full = orc.gqa_full(h["q"], h["k"], h["v"], h["row"], h["L"], w.scale,
+                                    w.block_size)
+                shard = [orc.gqa_shard(h["q"], h["k"], h["v"], h["row"], h["L"], r, w.cp_size,
+                                       w.interleave, w.scale, w.block_size)
+                         for r in range(w.cp_size)]
+            else:
+                full = orc.mla_full(h["q"], h["lat"], h["row"], h["L"], w.scale, w.block_size)
+                shard = [orc.mla_shard(h["q"], h["lat"], h["row"], h["L"], r, w.cp_size,
+                                       w.interleave, w.scale, w.block_size)
+                         for r in range(w.cp_size)]
+            o_ref, l_ref = full
+            d = h["o"] - o_ref
+            ea = max(ea, float(np.abs(d).max()))
+            rn = np.linalg.norm(o_ref, axis=-1)
+            m = rn > 0                       # rows with tokens (an empty request has O = 0)
+            if m.any():
+                er = max(er, float((np.abs(d).max(axis=-1)[m] / np.abs(o_ref).max(axis=-1)[m])
+                                   .max()))
+                el = max(el, float((np.linalg.norm(d, axis=-1)[m] / rn[m]).max()))
+            num += float((d * d).sum())
+            den += float((o_ref * o_ref).sum())
+            fin = np.isfinite(l_ref)
+            lse_err = float(np.abs(h["lse"][fin] - l_ref[fin]).max()) if fin.any() else 0.0
+            out.setdefault(name, {"lse_max_abs": 0.0})
+            out[name]["lse_max_abs"] = max(out[name]["lse_max_abs"], lse_err)
+            for r, (po, _) in enumerate(shard):
+                pn = np.linalg.norm(po, axis=-1)
+                m = pn > 0
+                if m.any():
+                    pd = np.linalg.norm(h["o_parts"][r] - po, axis=-1)[m] / pn[m]
+                    pl2 = max(pl2, float(pd.max()))
+        out[name].update({
+            "requests": [h["b"] for h in rows], "o_max_abs": float(f"{ea:.3e}"),
+            "o_max_rel": float(f"{er:.3e}"), "o_rel_l2_row_max": float(f"{el:.3e}"),
+            "o_rel_l2": float(f"{np.sqrt(num / den):.3e}"),
+            "partial_o_rel_l2_row_max": float(f"{pl2:.3e}"),
+            "oracle_s": round(time.perf_counter() - t0, 1)})
+        out[name]["lse_max_abs"] = float(f"{out[name]['lse_max_abs']:.3e}")
+    return out
+
+
 def run_step_fns(dca, w, inp, kind):
     import torch
     q = inp["q"]
@@ -256,6 +342,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert dca.read_device_errors(ws) == 0
+    samples = None if args.no_cpu_baseline else {}
+    keep_sample(samples, w, inp, step.bufs, sorted({0, w.batch // 3, 2 * w.batch // 3,
+                                                    w.batch - 1}))
 
     shard_ms = [a.elapsed_time(b) for a, b in shard_ev]
     merge_ms = [a.elapsed_time(b) for a, b in merge_ev]
@@ -319,14 +408,15 @@ def main():
         line["kernels"][f"{kernel_name}_interleave1_us"] = fine_interleave_us(dca, torch, w, inp,
                                                                              kind)
     if not args.no_secondary and kind == dca.GQA:
-        line["secondary"] = secondary_mla(dca, wl, torch)
-        line["secondary_ragged"] = secondary_ragged(dca, wl, torch)
-        line["secondary_long"] = secondary_long(dca, wl, torch)
+        line["secondary"] = secondary_mla(dca, wl, torch, samples=samples)
+        line["secondary_ragged"] = secondary_ragged(dca, wl, torch, samples=samples)
+        line["secondary_long"] = secondary_long(dca, wl, torch, samples=samples)
         line["secondary_fp8kv"] = secondary_fp8kv(dca, wl, torch)
-        line["secondary_tiny"] = secondary_tiny(dca, wl, torch)
+        line["secondary_tiny"] = secondary_tiny(dca, wl, torch, samples=samples)
         line["secondary_multi_token"] = secondary_multi_token(dca, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
+        line["accuracy"] = accuracy(samples)
     print(json.dumps(line), flush=True)
 
 
@@ -358,7 +448,7 @@ def fine_interleave_us(dca, torch, w, inp, kind, steps=10):
     return round(ms[len(ms) // 2] * 1e3, 2)
 
 
-def secondary_mla(dca, wl, torch, steps=20):
+def secondary_mla(dca, wl, torch, steps=20, samples=None):
     """MLA decode workload (64 x 67584, 128 heads, C = 8): rank-0 shard kernel MFMA
     utilisation and HBM rate, and the 8-partial merge rate."""
     w = wl.MLA_DECODE
@@ -396,6 +486,7 @@ def secondary_mla(dca, wl, torch, steps=20):
             ms.append(ev[0].elapsed_time(ev[1]) * 1e3)
         return sorted(ms)[len(ms) // 2]
 
+    keep_sample(samples, w, inp, step.bufs, [0, w.batch - 1])
     mla_i1_us = fine_interleave_us(dca, torch, w, inp, dca.MLA)
     merge_hbm_us = merge_median(lambda: flush.sum())
     merge_cached_us = merge_median(lambda: None)
@@ -469,7 +560,7 @@ def secondary_multi_token(dca, wl, torch):
     return res
 
 
-def secondary_ragged(dca, wl, torch, steps=5):
+def secondary_ragged(dca, wl, torch, steps=5, samples=None):
     """Ragged MLA batch (512 requests, lognormal lengths around 67000 plus injected edge
     lengths, C = 8, I = 64): all 8 shard kernels (sum of their durations, MFMA utilisation,
     HBM rate) and the merge of 8 partials per (request, head) row, the largest merge of the
@@ -485,6 +576,10 @@ def secondary_ragged(dca, wl, torch, steps=5):
         step(True)
     torch.cuda.synchronize()
     assert dca.read_device_errors(ws) == 0
+    # sampled: requests of lengths 1, 65 and 4096 (edge lengths) and the first lognormal one
+    edge = [int(next(i for i, L in enumerate(lens) if L == e)) for e in (1, 65, 4096)]
+    keep_sample(samples, w, inp, step.bufs,
+                edge + [next(i for i in range(w.batch) if i not in edge and lens[i] < 150000)])
     C = w.cp_size
     shard_ms = [a.elapsed_time(b) for a, b in shard_ev]
     shards_s = sum(shard_ms) / steps / 1e3            # all C shard kernels of one step
@@ -535,7 +630,7 @@ def secondary_ragged(dca, wl, torch, steps=5):
             "kv_tokens_per_s": round(int(lens.sum()) / step_s, 1)}
 
 
-def secondary_tiny(dca, wl, torch, steps=200):
+def secondary_tiny(dca, wl, torch, steps=200, samples=None):
     """The tiny fp32 case (1 request x 1024 tokens, 8 query heads on 2 KV heads, D 64,
     C = 2, I = 16): latency-bound, so reported as latency: the graph-replayed step (both
     shard calls + the merge) and each shard kernel's own duration."""
@@ -548,6 +643,7 @@ def secondary_tiny(dca, wl, torch, steps=200):
         step(True)
     torch.cuda.synchronize()
     assert dca.read_device_errors(ws) == 0
+    keep_sample(samples, w, inp, step.bufs, [0])
     shard_us = sorted(a.elapsed_time(b) for a, b in shard_ev)[len(shard_ev) // 2] * 1e3
     merge_us = sorted(a.elapsed_time(b) for a, b in merge_ev)[len(merge_ev) // 2] * 1e3
     graph = capture_step(torch, step)
@@ -583,7 +679,7 @@ def secondary_fp8kv(dca, wl, torch):
     return res
 
 
-def secondary_long(dca, wl, torch, steps=10):
+def secondary_long(dca, wl, torch, steps=10, samples=None):
     """Long-context MLA (8 requests x 200000 tokens, C = 4, I = 128): all 4 shard kernels of
     a step (sum of their durations, MFMA utilisation, HBM rate), the merge of 4 partials per
     (request, head) row (10.5 MB: latency-bound), and the whole step replayed as a HIP
@@ -599,6 +695,7 @@ def secondary_long(dca, wl, torch, steps=10):
         step(True)
     torch.cuda.synchronize()
     assert dca.read_device_errors(ws) == 0
+    keep_sample(samples, w, inp, step.bufs, [w.batch - 1])
     C = w.cp_size
     shard_ms = [a.elapsed_time(b) for a, b in shard_ev]
     shards_s = sum(shard_ms) / steps / 1e3

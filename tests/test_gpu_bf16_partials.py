@@ -14,7 +14,8 @@ import torch
 import decode_attention_context_amd as dca
 from decode_attention_context_amd import workloads as wl
 from oracle import dcp_oracle as orc
-from parity_helpers import TOL_F32, assert_close, oracle_full, request_host
+from parity_helpers import (REL_L2_BF16, TOL_F32, assert_close, assert_rel_l2, oracle_full,
+                            request_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +71,7 @@ def test_bf16_partials(gpu_lib, w):
         h = request_host(inp, kind, b)
         o_ref, l_ref = oracle_full(h, kind, w.scale)
         assert_close(o_m[b].cpu().numpy(), o_ref, tol, f"{w.name} b={b} merged O")
+        assert_rel_l2(o_m[b].cpu().numpy(), o_ref, REL_L2_BF16, f"{w.name} b={b} merged O")
         assert_close(l_m[b].cpu().numpy(), l_ref, TOL_F32, f"{w.name} b={b} merged lse")
 
 

@@ -7,7 +7,8 @@ import torch
 import decode_attention_context_amd as dca
 from decode_attention_context_amd import workloads as wl
 from oracle import dcp_oracle as orc
-from parity_helpers import TOL_F32, assert_close
+from parity_helpers import (TOL_F32, assert_close, assert_rel_l2, o_rel_l2, o_tol,
+                            oracle_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,11 +103,35 @@ ERR_CASES = [
 ]
 
 
+def _check_survivors(inp, kind, bt, lens, rank, cp, il, scale, o, l, what):
+    """Each request's partial against the oracle over its surviving tokens: owned by the
+    rank, below min(seq_len, what the table row covers), on a page id inside the cache."""
+    B = (inp["k_pages"].shape[2] if kind == dca.GQA else inp["latent_pages"].shape[1])
+    bt_h = bt.cpu().numpy()
+    num_blocks = inp["num_blocks"]
+    o = o.cpu().numpy()
+    l = l.cpu().numpy()
+    tol = o_tol(kind, inp["q"].dtype)
+    for b in range(bt_h.shape[0]):
+        L = min(int(lens[b]), bt_h.shape[1] * B)
+        t = orc.owned_tokens(L, rank, cp, il)
+        pg = bt_h[b][t // B]
+        t = t[(pg >= 0) & (pg < num_blocks)]
+        good = inp["block_table"][b].cpu().numpy()
+        # the surviving tokens' pages are the same in bt and in the input table
+        assert np.array_equal(bt_h[b][t // B], good[t // B])
+        o_ref, l_ref = oracle_tokens(inp, kind, b, t, scale)
+        assert_close(l[b], l_ref, TOL_F32, f"{what}: b={b} lse")
+        assert_close(o[b], o_ref, tol, f"{what}: b={b} O")
+        assert_rel_l2(o[b], o_ref, o_rel_l2(inp["q"].dtype), f"{what}: b={b} O")
+
+
 @pytest.mark.parametrize("w,rank,cp,il", ERR_CASES,
                          ids=["gqa", "gqa_i1", "gqa_fp8", "gqa_fp8_i1", "mla", "mla_i1"])
 def test_device_error_word(gpu_lib, w, rank, cp, il):
     """Contract violations only the device sees are flagged, never fault, and leave the
-    remaining tokens' attention intact."""
+    remaining tokens' attention intact: every request's partial equals the oracle's
+    attention over the rank's tokens that lie inside the block table and on valid pages."""
     print(f"[deverr] {w.name} rank={rank} cp={cp} il={il}", flush=True)
     inp = wl.make_inputs(w, device="cuda")
     kind = dca.GQA if w.kind == "gqa" else dca.MLA
@@ -120,6 +145,7 @@ def test_device_error_word(gpu_lib, w, rank, cp, il):
     o, l, ws = dca.shard(inp["q"], kv, v, bt, lens, rank, cp, il, w.scale, **kw)
     assert dca.read_device_errors(ws) & dca.DEVERR_SEQ_LEN
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
+    _check_survivors(inp, kind, bt, lens, rank, cp, il, w.scale, o, l, "seq_len past table")
     # a block id outside the cache (logical page 1 of request 0; its other pages remain)
     bt2 = inp["block_table"].clone()
     bt2[0, 1] = 10 ** 6
@@ -127,6 +153,8 @@ def test_device_error_word(gpu_lib, w, rank, cp, il):
                          workspace=ws, **kw)
     assert dca.read_device_errors(ws) & dca.DEVERR_BLOCK_ID
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
+    _check_survivors(inp, kind, bt2, inp["seq_lens"], rank, cp, il, w.scale, o, l,
+                     "block id outside the cache")
     # a clean call clears the word
     dca.shard(inp["q"], kv, v, inp["block_table"], inp["seq_lens"], rank, cp, il, w.scale,
               workspace=ws, **kw)

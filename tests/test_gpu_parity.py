@@ -14,7 +14,8 @@ import torch
 
 import decode_attention_context_amd as dca
 from decode_attention_context_amd import workloads as wl
-from parity_helpers import check_requests, run_shards, scale_of
+from parity_helpers import (REL_L2_BF16, REL_L2_F32, TOL_F32, assert_close, assert_rel_l2,
+                            check_requests, run_shards, scale_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,8 +88,8 @@ def test_large_scores(gpu_lib, w):
 
 
 def test_gqa_full_share(gpu_lib):
-    """64 x 32768 bf16 GQA share, C = 2, I = 128: requests 0, 31, 63 checked exhaustively."""
-    _run_and_check(wl.GQA_SHARE, requests=[0, 31, 63])
+    """64 x 32768 bf16 GQA share, C = 2, I = 128: every request checked exhaustively."""
+    _run_and_check(wl.GQA_SHARE)
 
 
 def test_mla_full_decode(gpu_lib):
@@ -96,9 +97,26 @@ def test_mla_full_decode(gpu_lib):
     _run_and_check(wl.MLA_DECODE, requests=[0, 63])
 
 
-def test_mla_full_long(gpu_lib):
-    """8 x 200000 MLA, C = 4, I = 128: all 4 shards and the merge; requests 0 and 5."""
-    _run_and_check(wl.MLA_LONG, requests=[0, 5])
+@pytest.fixture(scope="module")
+def mla_long_run(gpu_lib):
+    """8 x 200000 MLA, C = 4, I = 128: all 4 shards and the merge, run once for the
+    per-request checks below."""
+    w = wl.MLA_LONG
+    print(f"[parity] {w.name}: batch={w.batch} C={w.cp_size} I={w.interleave}", flush=True)
+    inp = wl.make_inputs(w, device="cuda")
+    o_parts, l_parts = run_shards(inp, dca.MLA, w.cp_size, w.interleave, w.scale)
+    o_m, l_m = dca.merge(o_parts, l_parts)
+    torch.cuda.synchronize()
+    return w, inp, o_parts, l_parts, o_m, l_m
+
+
+@pytest.mark.parametrize("b", range(wl.MLA_LONG.batch))
+def test_mla_full_long(mla_long_run, b):
+    """Every request of the long-context workload, one test each (the oracle takes several
+    seconds per 200000-token request)."""
+    w, inp, o_parts, l_parts, o_m, l_m = mla_long_run
+    check_requests(inp, dca.MLA, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
+                   [b], w.name)
 
 
 def test_mla_full_ragged(gpu_lib):
@@ -109,3 +127,72 @@ def test_mla_full_ragged(gpu_lib):
     edge = [int(np.where(lens == L)[0][0]) for L in (1, 2, 63, 64, 65, 448, 449, 513, 262144)]
     rest = [i for i in range(w.batch) if i not in edge][:2]
     _run_and_check(w, requests=edge + rest)
+
+
+def _plan_chunk(ws):
+    """Tokens per work item of the plan a shard call left in its workspace (header[2])."""
+    return int(ws[8:12].cpu().numpy().view(np.int32)[0])
+
+
+SPLIT_CASES = [(wl.GQA_SHARE, dca.GQA, 17), (wl.MLA_DECODE, dca.MLA, 40)]
+
+
+@pytest.mark.parametrize("w,kind,b", SPLIT_CASES, ids=[c[0].name for c in SPLIT_CASES])
+def test_split_invariance(gpu_lib, w, kind, b):
+    """One request of a full-size batch, run alone: the planner then cuts its shard into
+    many more, shorter work items (a different split and split-combine), and the result
+    must agree with the batched one and with the oracle."""
+    print(f"[split] {w.name} request {b}", flush=True)
+    inp = wl.make_inputs(w, device="cuda")
+    kv = inp["k_pages"] if kind == dca.GQA else inp["latent_pages"]
+    v = inp["v_pages"] if kind == dca.GQA else None
+    one = dict(inp, q=inp["q"][b:b + 1].contiguous(),
+               block_table=inp["block_table"][b:b + 1].contiguous(),
+               seq_lens=inp["seq_lens"][b:b + 1].contiguous())
+    rl2 = REL_L2_BF16 if inp["q"].dtype == torch.bfloat16 else REL_L2_F32
+    o1_parts, l1_parts = [], []
+    for r in range(w.cp_size):
+        o_all, l_all, ws_all = dca.shard(inp["q"], kv, v, inp["block_table"], inp["seq_lens"], r,
+                                         w.cp_size, w.interleave, w.scale, kind=kind)
+        o_one, l_one, ws_one = dca.shard(one["q"], kv, v, one["block_table"], one["seq_lens"],
+                                         r, w.cp_size, w.interleave, w.scale, kind=kind)
+        torch.cuda.synchronize()
+        assert dca.read_device_errors(ws_all) == 0 and dca.read_device_errors(ws_one) == 0
+        c_all, c_one = _plan_chunk(ws_all), _plan_chunk(ws_one)
+        assert c_one < c_all, (c_one, c_all)
+        assert_close(l_one[0].cpu().numpy(), l_all[b].cpu().numpy(), TOL_F32,
+                     f"rank {r} lse alone vs batched")
+        assert_rel_l2(o_one[0].cpu().numpy(), o_all[b].cpu().numpy(), rl2,
+                      f"rank {r} O alone (items of {c_one}) vs batched (items of {c_all})")
+        o1_parts.append(o_one)
+        l1_parts.append(l_one)
+    o_parts, l_parts = torch.stack(o1_parts), torch.stack(l1_parts)
+    o_m, l_m = dca.merge(o_parts, l_parts)
+    torch.cuda.synchronize()
+    check_requests(one, kind, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
+                   [0], f"{w.name} request {b} alone")
+
+
+LONG_ITEM_CASES = [
+    wl.GQA_SHARE.with_(name="gqa_long_items", batch=2, num_q_heads=16, num_kv_heads=16,
+                       block_size=64, cp_size=1, interleave=64, lengths=(140000, 139001),
+                       seed=61),
+    wl.GQA_SHARE_FP8.with_(name="gqa_fp8_long_items", batch=2, num_q_heads=16,
+                           num_kv_heads=16, block_size=64, cp_size=1, interleave=64,
+                           lengths=(140000, 139001), seed=62),
+]
+
+
+@pytest.mark.parametrize("w", LONG_ITEM_CASES, ids=[w.name for w in LONG_ITEM_CASES])
+def test_gqa_items_beyond_64_tiles(gpu_lib, w):
+    """Work items longer than 64 tiles of 64 tokens: the GQA kernels rebuild their page
+    table in LDS every 64 tiles (16 KV heads leave the planner 32 items per call, so
+    279001 tokens give items of 8768 tokens, 137 tiles)."""
+    print(f"[parity] {w.name}", flush=True)
+    inp = wl.make_inputs(w, device="cuda")
+    _, _, ws = dca.shard(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"],
+                         inp["seq_lens"], 0, w.cp_size, w.interleave, w.scale, kind=dca.GQA,
+                         k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"))
+    torch.cuda.synchronize()
+    assert _plan_chunk(ws) > 64 * 64 * 2, _plan_chunk(ws)
+    _run_and_check(w)
