@@ -4,41 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "host_rules.h"
 #include "walker.h"
 
 namespace dcp {
-
-// ---------------------------------------------------------------------------------------
-// Workspace layout (every section 256-byte aligned).  Written by the planner, read by the
-// shard kernels and the split combine of the same call.
-//   header  int32[64]: [0] device error word, [1] number of work items, [2] tokens per item
-//   off     int32[batch + 1]: first work item of each request (prefix sum)
-//   items   int4[max_items]: (request, local token begin, local token end, partial index),
-//           in dispatch order (longest first); a request's partials have consecutive
-//           indices off[b] .. off[b+1)
-//   plse    float[max_items * rows]:      per-partial log-sum-exp (natural log)
-//   po      [max_items * rows * Dv]:      per-partial normalized output, float32 (GQA) or
-//                                         bf16 rounded to nearest even (MLA: 128 KiB per
-//                                         item and position instead of 256 KiB)
-// (rows = query rows per request: q_len * Hq)
-// ---------------------------------------------------------------------------------------
-struct WsLayout {
-  size_t off_off, items_off, plse_off, po_off, total;
-  int po_bf16;
-};
-
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-inline WsLayout ws_layout(int batch, int64_t max_items, int hq, int dv, bool po_bf16) {
-  WsLayout w;
-  w.po_bf16 = po_bf16 ? 1 : 0;
-  w.off_off = 256;
-  w.items_off = w.off_off + align256(sizeof(int32_t) * (size_t)(batch + 1));
-  w.plse_off = w.items_off + align256(sizeof(int32_t) * 4 * (size_t)max_items);
-  w.po_off = w.plse_off + align256(sizeof(float) * (size_t)max_items * hq);
-  w.total = w.po_off + align256((po_bf16 ? 2 : 4) * (size_t)max_items * hq * dv);
-  return w;
-}
 
 struct WsPtrs {
   int32_t* header;

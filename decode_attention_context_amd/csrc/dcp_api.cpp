@@ -1,5 +1,6 @@
-// dcp_api.cpp — the C ABI of include/dcp_attn.h: argument validation, workspace sizing
-// and the launch sequence of a shard call (plan -> shard kernel -> split combine).
+// dcp_api.cpp — the C ABI of include/dcp_attn.h: the launch sequence of a shard call
+// (plan -> shard kernel -> split combine) after the checks and the workspace sizing of
+// host_rules.h.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -12,9 +13,8 @@
 
 namespace {
 
-using dcp::WsLayout;
-
-constexpr int64_t kMaxI32 = 2147483647;
+using dcp::KvFp8;
+using dcp::Plan;
 
 int device_cus() {
   int dev = 0;
@@ -24,102 +24,17 @@ int device_cus() {
   return n;
 }
 
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-// Shape checks shared by the size query and the shard call.
-int check_desc(const dcp_attn_desc* d, int q_len, int batch, int64_t max_seq_len, int cp,
-               int il) {
-  if (!d || batch < 0 || max_seq_len < 0 || max_seq_len > kMaxI32) return DCP_EINVAL;
-  if (q_len < 1) return DCP_EINVAL;
-  if (q_len > dcp::kMaxQLen) return DCP_EUNSUPPORTED;
-  if (cp < 1 || il < 1 || (int64_t)cp * il > kMaxI32) return DCP_EINVAL;
-  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads) return DCP_EINVAL;
-  if (d->head_dim_qk < 1 || d->head_dim_v < 1 || d->block_size < 1 || d->max_blocks_per_seq < 1 ||
-      d->num_blocks < 1)
-    return DCP_EINVAL;
-  if (d->num_blocks * (int64_t)d->block_size * d->num_kv_heads > kMaxI32) return DCP_EUNSUPPORTED;
-  if ((int64_t)d->max_blocks_per_seq * d->block_size > kMaxI32) return DCP_EUNSUPPORTED;
-  if (d->dtype != DCP_F32 && d->dtype != DCP_BF16) return DCP_EINVAL;
-  if (d->kind == DCP_GQA) {
-    if (d->head_dim_qk != d->head_dim_v) return DCP_EUNSUPPORTED;
-    if (!dcp::gqa_supported(d->dtype, d->head_dim_qk, d->num_q_heads / d->num_kv_heads, q_len))
-      return DCP_EUNSUPPORTED;
-  } else if (d->kind == DCP_MLA) {
-    if (d->dtype != DCP_BF16 || d->num_q_heads != 128 || d->num_kv_heads != 1 ||
-        d->head_dim_qk != 576 || d->head_dim_v != 512)
-      return DCP_EUNSUPPORTED;
-  } else {
-    return DCP_EINVAL;
-  }
-  return DCP_OK;
-}
-
-struct Plan {
-  int64_t target = 0;
-  int tile = 64;
-  int min_chunk = 64;
-  int64_t max_items = 0;
-  WsLayout lay{};
-};
-
-// Work items: the planner splits the shard's tokens into about `target` items (never more
-// than target + batch), about one round of workgroups over the CUs (GQA: one workgroup per
-// item and KV head; MLA: one workgroup per item and query position).  Partials are kept per query row: q_len * num_q_heads rows per item.
-bool make_plan(const dcp_attn_desc* d, int q_len, int batch, Plan* p) {
-  const int cus = device_cus();
-  if (cus <= 0) return false;
-  if (d->kind == DCP_GQA) {
-    p->tile = dcp::kGqaTile;
-    // two resident workgroups (64 KiB double buffer each) per CU and KV head, one round;
-    // bf16 queries with more than 32 rows per KV head take two workgroups (32-row slices)
-    // per item and KV head, so half the items
-    const int rows = q_len * (d->num_q_heads / d->num_kv_heads);
-    const int slices = (d->dtype == DCP_BF16 && rows > 32) ? 2 : 1;
-    p->target = std::max<int64_t>(1, (int64_t)cus * 2 / (d->num_kv_heads * slices));
-    p->min_chunk = dcp::kGqaTile;
-  } else {
-    // one workgroup (all heads) per item and query position, one resident workgroup per CU
-    // (144 KiB of LDS)
-    p->tile = dcp::kMlaTile;
-    p->target = std::max<int64_t>(1, (int64_t)cus / q_len);
-    p->min_chunk = 4 * dcp::kMlaTile;
-  }
-  p->max_items = (int64_t)batch + p->target;
-  // MLA split partials in bf16 (the GQA ones are a few KiB per item and stay float32)
-  p->lay = dcp::ws_layout(batch, p->max_items, q_len * d->num_q_heads, d->head_dim_v,
-                          d->kind == DCP_MLA);
-  return true;
-}
-
-// fp8 KV cache of a GQA shard call: K / V pages hold fp8 codes, values code * scale.
-struct KvFp8 {
-  float k_scale, v_scale;
-};
-
 int shard_impl(const dcp_attn_desc* d, int q_len, int o_dtype, const void* q, const void* kv,
                const void* v, const int32_t* bt, const int32_t* lens, int batch,
                int64_t max_seq_len, int rank, int cp, int il, float scale, void* o, float* lse,
                void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
                const KvFp8* fp8 = nullptr) {
-  int st = check_desc(d, q_len, batch, max_seq_len, cp, il);
-  if (st != DCP_OK) return st;
-  if (fp8) {
-    if (d->kind != DCP_GQA || d->dtype != DCP_BF16) return DCP_EUNSUPPORTED;
-    if (!dcp::gqa_fp8_supported(d->head_dim_qk, d->num_q_heads / d->num_kv_heads, q_len))
-      return DCP_EUNSUPPORTED;
-    if (!std::isfinite(fp8->k_scale) || !std::isfinite(fp8->v_scale)) return DCP_EINVAL;
-  }
-  if (o_dtype != DCP_F32 && o_dtype != DCP_BF16) return DCP_EINVAL;
-  const int o_bf16 = o_dtype == DCP_BF16;
-  if (rank < 0 || rank >= cp || !std::isfinite(scale)) return DCP_EINVAL;
-  if (batch == 0) return DCP_OK;
-  if (!q || !kv || !bt || !lens || !o || !lse) return DCP_EINVAL;
-  if (d->kind == DCP_GQA ? v == nullptr : v != nullptr) return DCP_EINVAL;
-  if (!aligned(q, 16) || !aligned(kv, 16) || (v && !aligned(v, 16)) || !aligned(o, 16))
-    return DCP_EINVAL;
   Plan p;
-  if (!make_plan(d, q_len, batch, &p)) return DCP_ELAUNCH;
-  if (!ws || !aligned(ws, 256) || ws_bytes < p.lay.total) return DCP_EWORKSPACE;
+  const int st = dcp::check_shard_args(d, q_len, o_dtype, q, kv, v, bt, lens, batch, max_seq_len,
+                                       rank, cp, il, scale, o, lse, ws, ws_bytes, fp8,
+                                       device_cus, &p);
+  if (st != DCP_OK || batch == 0) return st;
+  const int o_bf16 = o_dtype == DCP_BF16;
   const dcp::WsPtrs w = dcp::ws_ptrs(ws, p.lay);
   const int64_t len_cap = (int64_t)d->max_blocks_per_seq * d->block_size;
   const dcp::RowArgs rows{lens, len_cap, q_len};
@@ -162,9 +77,9 @@ extern "C" {
 
 size_t dcp_workspace_size_mq(const dcp_attn_desc* desc, int q_len, int batch,
                              int64_t max_seq_len, int cp_size, int interleave) {
-  if (check_desc(desc, q_len, batch, max_seq_len, cp_size, interleave) != DCP_OK) return 0;
+  if (dcp::check_desc(desc, q_len, batch, max_seq_len, cp_size, interleave) != DCP_OK) return 0;
   Plan p;
-  if (!make_plan(desc, q_len, batch, &p)) return 0;
+  if (!dcp::make_plan(desc, q_len, batch, device_cus(), &p)) return 0;
   return p.lay.total;
 }
 
@@ -243,13 +158,9 @@ int dcp_attn_shard_timed(const dcp_attn_desc* desc, const void* q, const void* k
 int dcp_merge_ex(const void* o_partials, int in_dtype, const float* lse_partials, int cp_size,
                  int batch, int num_heads, int head_dim_v, void* o_out, int out_dtype,
                  float* lse_out, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (cp_size < 1 || batch < 0 || num_heads < 1 || head_dim_v < 1) return DCP_EINVAL;
-  if (out_dtype != DCP_F32 && out_dtype != DCP_BF16) return DCP_EINVAL;
-  if (in_dtype != DCP_F32 && in_dtype != DCP_BF16) return DCP_EINVAL;
-  if ((int64_t)batch * num_heads * head_dim_v * cp_size > ((int64_t)1 << 40)) return DCP_EUNSUPPORTED;
-  if (batch == 0) return DCP_OK;
-  if (!o_partials || !lse_partials || !o_out) return DCP_EINVAL;
-  if (!aligned(o_partials, 16) || !aligned(o_out, 16)) return DCP_EINVAL;
+  const int st = dcp::check_merge_args(o_partials, in_dtype, lse_partials, cp_size, batch,
+                                       num_heads, head_dim_v, o_out, out_dtype);
+  if (st != DCP_OK || batch == 0) return st;
   const hipError_t e = dcp::launch_merge(o_partials, in_dtype == DCP_BF16, lse_partials, cp_size,
                                          batch, num_heads, head_dim_v, o_out,
                                          out_dtype == DCP_BF16, lse_out, stream, ev_begin, ev_end);
@@ -274,14 +185,10 @@ int dcp_shard_slots(const int32_t* block_table, const int32_t* seq_lens, int bat
                     int max_blocks_per_seq, int block_size, int64_t num_blocks, int rank,
                     int cp_size, int interleave, const int64_t* out_offsets,
                     int64_t* slots_out, void* workspace, hipStream_t stream) {
-  if (batch < 0 || max_blocks_per_seq < 1 || block_size < 1 || num_blocks < 1) return DCP_EINVAL;
-  if (cp_size < 1 || interleave < 1 || rank < 0 || rank >= cp_size) return DCP_EINVAL;
-  if ((int64_t)cp_size * interleave > kMaxI32 ||
-      (int64_t)max_blocks_per_seq * block_size > kMaxI32)
-    return DCP_EUNSUPPORTED;
-  if (batch == 0) return DCP_OK;
-  if (!block_table || !seq_lens || !out_offsets || !slots_out) return DCP_EINVAL;
-  if (!workspace || !aligned(workspace, 256)) return DCP_EWORKSPACE;
+  const int st = dcp::check_slots_args(block_table, seq_lens, batch, max_blocks_per_seq,
+                                       block_size, num_blocks, rank, cp_size, interleave,
+                                       out_offsets, slots_out, workspace);
+  if (st != DCP_OK || batch == 0) return st;
   const hipError_t e = dcp::launch_shard_slots(
       block_table, seq_lens, batch, max_blocks_per_seq, block_size, num_blocks, rank, cp_size,
       interleave, out_offsets, slots_out, static_cast<int32_t*>(workspace), stream);

@@ -45,7 +45,7 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 #define DCP_LDS __attribute__((address_space(3)))
 
 constexpr int kTile = kGqaTile;                  // 64 tokens
-constexpr int kD = 128;                          // head dim
+constexpr int kD = kGqaFp8HeadDim;              // head dim
 constexpr int kRow = 128;                        // bytes per cached row (one code per dim)
 constexpr int kTileBytes = kTile * kRow;         // 8 KiB of K (and of V) per tile
 constexpr int kBufBytes = 2 * kTileBytes;        // K rows, then V rows
@@ -428,11 +428,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
 }
 
 }  // namespace
-
-bool gqa_fp8_supported(int head_dim, int group, int q_len) {
-  const int rows = group * q_len;
-  return head_dim == kD && q_len >= 1 && q_len <= kMaxQLen && rows >= 1 && rows <= 64;
-}
 
 hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
                                 int64_t max_items, const WsPtrs& ws, void* o_out,

@@ -63,7 +63,7 @@ typedef __attribute__((ext_vector_type(4))) short s4;
 #define DCP_CONST __attribute__((address_space(4)))
 
 constexpr int kTile = kGqaTile;      // tokens per tile (= lanes)
-constexpr int kRowBytes = 256;       // D * sizeof(T) for the supported shapes
+constexpr int kRowBytes = kGqaRowBytes;   // D * sizeof(T) for the supported shapes
 constexpr int kChunks = kRowBytes / 16;
 constexpr int kTileBytes = kTile * kRowBytes;   // 16 KiB of K (and of V) per tile
 constexpr int kNBuf = 2;                         // double buffer: one computed, one in flight
@@ -731,13 +731,6 @@ hipError_t launch_bf16(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hi
 
 // 256-byte rows (bf16 head_dim 128, f32 head_dim 64) and any group of up to 64 query rows
 // (q_len * G) per KV head.
-bool gqa_supported(int dtype, int head_dim, int group, int q_len) {
-  const int elem = dtype == 1 ? 2 : 4;
-  if (head_dim * elem != kRowBytes) return false;
-  if (q_len < 1 || q_len > kMaxQLen || group < 1) return false;
-  return group * q_len <= 64;
-}
-
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
                             void* o_out, float* lse_out, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1) {

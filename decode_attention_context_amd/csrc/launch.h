@@ -54,7 +54,6 @@ struct GqaArgs {
 hipError_t launch_gqa_shard(const GqaArgs& a, int64_t max_items, const WsPtrs& ws,
                             void* o_out, float* lse_out, hipStream_t stream,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-bool gqa_supported(int dtype, int head_dim, int group, int q_len);
 
 // fp8 KV cache (OCP FP8 E4M3 codes, one float32 scale per tensor; bf16 queries): the same
 // shard with K / V values decode(code) * scale.  Supported for head_dim 128 and up to 64
@@ -63,7 +62,6 @@ hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
                                 int64_t max_items, const WsPtrs& ws, void* o_out,
                                 float* lse_out, hipStream_t stream, hipEvent_t ev0 = nullptr,
                                 hipEvent_t ev1 = nullptr);
-bool gqa_fp8_supported(int head_dim, int group, int q_len);
 
 struct MlaArgs {
   const void* q;
@@ -84,11 +82,5 @@ hipError_t launch_shard_slots(const int32_t* block_table, const int32_t* seq_len
                               int max_blocks, int block_size, int64_t num_blocks, int rank,
                               int cp, int interleave, const int64_t* out_offsets,
                               int64_t* slots_out, int32_t* err_word, hipStream_t stream);
-
-// Tokens per tile of each shard kernel (work items are whole multiples of it).
-constexpr int kGqaTile = 64;
-constexpr int kMlaTile = 32;
-// Most query positions per request (multi-token decode).
-constexpr int kMaxQLen = 4;
 
 }  // namespace dcp
