@@ -71,6 +71,39 @@ __device__ __forceinline__ typename VecT<VEC>::T ldp(const void* base, int64_t e
   }
 }
 
+// bf16 partials kept as loaded (VEC / 2 32-bit words, or one 16-bit value) until their use,
+// so that the loads in flight take half the registers of the widened values
+template <int VEC>
+struct RawBf16;
+template <>
+struct RawBf16<4> { using T = __attribute__((ext_vector_type(2))) uint32_t; };
+template <>
+struct RawBf16<2> { using T = uint32_t; };
+template <>
+struct RawBf16<1> { using T = uint16_t; };
+
+template <int VEC>
+__device__ __forceinline__ typename RawBf16<VEC>::T ld_raw_bf16(const void* base, int64_t elem) {
+  using T = typename RawBf16<VEC>::T;
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(static_cast<const uint16_t*>(base) + elem));
+}
+
+template <int VEC>
+__device__ __forceinline__ void widen_bf16(const typename RawBf16<VEC>::T& u, float (&f)[VEC]) {
+  if constexpr (VEC == 1) {
+    f[0] = __uint_as_float((uint32_t)u << 16);
+  } else if constexpr (VEC == 2) {
+    f[0] = __uint_as_float(u << 16);
+    f[1] = __uint_as_float(u & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+}
+
 template <int VEC>
 __device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename VecT<VEC>::T& v) {
   const float* p = reinterpret_cast<const float*>(&v);
@@ -162,6 +195,75 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
 // accumulates in place in the registers of the first partial, so that the loads in flight
 // (up to 64 registers) leave room for the most waves per SIMD.  When every partial is empty
 // all weights are 0 and the row comes out as O = 0, lse = -inf.
+// merge_row_small for bf16 partials: the same steps, with the loads held raw (RawBf16) and
+// a separate float accumulator per chunk.
+template <int VEC, bool kBf16Out>
+__device__ __forceinline__ void merge_row_small_bf16in(const void* __restrict__ o_base,
+                                                       int64_t o_stride,
+                                                       const float* __restrict__ l_base,
+                                                       int64_t l_stride, int n, int dv,
+                                                       void* __restrict__ out,
+                                                       float* __restrict__ lse_out, int lane) {
+  using V = typename VecT<VEC>::T;
+  using R = typename RawBf16<VEC>::T;
+  constexpr int kMaxN = 8, kMaxC = 2;
+  const int nc = dv / (64 * VEC);
+  float x = lane < n ? ld<float>(l_base + lane * l_stride) : neg_inf();
+  R v[kMaxN][kMaxC];
+#pragma unroll
+  for (int r = 0; r < kMaxN; ++r)
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c)
+      if (r < n && c < nc)
+        v[r][c] = ld_raw_bf16<VEC>(o_base, (int64_t)r * o_stride + (c * 64 + lane) * VEC);
+  x = __builtin_isfinite(x) ? x : neg_inf();
+  const float m2 = lanes8_max(x) * kLog2e;   // -inf when every partial is empty
+  const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
+  const float sum = lanes8_sum(wl);
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  float acc[kMaxC][VEC];
+#pragma unroll
+  for (int c = 0; c < kMaxC; ++c)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[c][i] = 0.f;
+  // partials with weight 0 are never multiplied (their rows may hold anything)
+#pragma unroll
+  for (int r = 0; r < kMaxN; ++r) {
+    if (r < n) {
+      const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r));
+      if (wr != 0.f) {
+#pragma unroll
+        for (int c = 0; c < kMaxC; ++c) {
+          if (c < nc) {
+            float f[VEC];
+            widen_bf16<VEC>(v[r][c], f);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[c][i] = fmaf(wr, f[i], acc[c][i]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kMaxC; ++c) {
+    if (c < nc) {
+      const int d = (c * 64 + lane) * VEC;
+      if constexpr (!kBf16Out) {
+        V o;
+        float* po = reinterpret_cast<float*>(&o);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) po[i] = acc[c][i] * inv;
+        st<V>(static_cast<float*>(out) + d, o);
+      } else {
+        uint16_t* ob = static_cast<uint16_t*>(out);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ob[d + i] = (uint16_t)f32_to_bf16_rne(acc[c][i] * inv);
+      }
+    }
+  }
+  if (lse_out && lane == 0) *lse_out = sum > 0.f ? (m2 + __log2f(sum)) * kLn2 : neg_inf();
+}
+
 template <int VEC, bool kBf16Out, bool kBf16In = false>
 __device__ __forceinline__ void merge_row_small(const void* __restrict__ o_base,
                                                 int64_t o_stride,
@@ -169,6 +271,11 @@ __device__ __forceinline__ void merge_row_small(const void* __restrict__ o_base,
                                                 int64_t l_stride, int n, int dv,
                                                 void* __restrict__ out,
                                                 float* __restrict__ lse_out, int lane) {
+  if constexpr (kBf16In) {
+    merge_row_small_bf16in<VEC, kBf16Out>(o_base, o_stride, l_base, l_stride, n, dv, out,
+                                          lse_out, lane);
+    return;
+  }
   using V = typename VecT<VEC>::T;
   constexpr int kMaxN = 8, kMaxC = 2;
   const int nc = dv / (64 * VEC);
