@@ -29,43 +29,52 @@ struct VecT<2> { using T = __attribute__((ext_vector_type(2))) float; };
 template <>
 struct VecT<4> { using T = __attribute__((ext_vector_type(4))) float; };
 
-// Loads with the non-temporal cache policy (nt), plain stores.  Measured on MI355X with
-// eight partials of 128 heads x 512 dims, caches flushed: at 512 requests (1.21 GB moved)
-// 203 us with nt loads against 226 us with plain loads and 213 us with nt loads and stores;
-// at 64 requests (151 MB) all three take 30.4 us.
-template <typename T>
+// Partial loads with the non-temporal cache policy (nt) or plain (the launcher picks by
+// size), plain stores.  Measured on MI355X with eight partials of 128 heads x 512 dims,
+// caches flushed: at 512 requests (1.21 GB moved) 203 us with nt loads against 226 us with
+// plain loads and 213 us with nt loads and stores.
+template <typename T, bool kNt = true>
 __device__ __forceinline__ T ld(const float* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  if constexpr (kNt) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
 }
+// the partials' LSE values: plain loads (a few bytes per row; measured slightly faster)
+__device__ __forceinline__ float ld_lse(const float* p) { return *p; }
 template <typename T>
 __device__ __forceinline__ void st(float* p, T v) {
   *reinterpret_cast<T*>(p) = v;
 }
 
+template <bool kNt, typename T>
+__device__ __forceinline__ T nt_or_plain(const T* p) {
+  if constexpr (kNt) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // VEC consecutive elements of a partial row as floats: float32 partials are loaded as they
 // are, bf16 partials (2 bytes per element) are loaded at half the width and widened exactly.
-template <int VEC, bool kBf16In>
+template <int VEC, bool kBf16In, bool kNt>
 __device__ __forceinline__ typename VecT<VEC>::T ldp(const void* base, int64_t elem) {
   using V = typename VecT<VEC>::T;
   if constexpr (!kBf16In) {
-    return ld<V>(static_cast<const float*>(base) + elem);
+    return ld<V, kNt>(static_cast<const float*>(base) + elem);
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(base) + elem;
     V v;
     float* pv = reinterpret_cast<float*>(&v);
     if constexpr (VEC == 4) {
       typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-      const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      const u32x2 u = nt_or_plain<kNt>(reinterpret_cast<const u32x2*>(p));
       pv[0] = __uint_as_float(u.x << 16);
       pv[1] = __uint_as_float(u.x & 0xffff0000u);
       pv[2] = __uint_as_float(u.y << 16);
       pv[3] = __uint_as_float(u.y & 0xffff0000u);
     } else if constexpr (VEC == 2) {
-      const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+      const uint32_t u = nt_or_plain<kNt>(reinterpret_cast<const uint32_t*>(p));
       pv[0] = __uint_as_float(u << 16);
       pv[1] = __uint_as_float(u & 0xffff0000u);
     } else {
-      pv[0] = __uint_as_float((uint32_t)__builtin_nontemporal_load(p) << 16);
+      pv[0] = __uint_as_float((uint32_t)nt_or_plain<kNt>(p) << 16);
     }
     return v;
   }
@@ -82,10 +91,10 @@ struct RawBf16<2> { using T = uint32_t; };
 template <>
 struct RawBf16<1> { using T = uint16_t; };
 
-template <int VEC>
+template <int VEC, bool kNt>
 __device__ __forceinline__ typename RawBf16<VEC>::T ld_raw_bf16(const void* base, int64_t elem) {
   using T = typename RawBf16<VEC>::T;
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(static_cast<const uint16_t*>(base) + elem));
+  return nt_or_plain<kNt>(reinterpret_cast<const T*>(static_cast<const uint16_t*>(base) + elem));
 }
 
 template <int VEC>
@@ -114,7 +123,7 @@ __device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename 
 // Merge `n` partial rows o_base[r * o_stride .. + dv) with lse l_base[r * l_stride].
 // The lse values are spread over the lanes (64 per pass) and reduced with DPP, so the row
 // costs one round trip for them; the partial rows are then streamed 8 at a time.
-template <int VEC, bool kBf16In = false>
+template <int VEC, bool kBf16In, bool kNt>
 __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64_t o_stride,
                                           const float* __restrict__ l_base, int64_t l_stride,
                                           int n, int dv, float* __restrict__ out_f32,
@@ -123,7 +132,7 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
   using V = typename VecT<VEC>::T;
   auto lse_at = [&](int r) -> float {
     if (r >= n) return neg_inf();
-    const float x = ld<float>(l_base + r * l_stride);
+    const float x = ld_lse(l_base + r * l_stride);
     return __builtin_isfinite(x) ? x : neg_inf();
   };
   float m = neg_inf();
@@ -164,7 +173,7 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
         for (int u = 0; u < 8; ++u) {
           wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r + u));
           if (wv[u] != 0.f)
-            v[u] = ldp<VEC, kBf16In>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
+            v[u] = ldp<VEC, kBf16In, kNt>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -173,7 +182,7 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
       for (; r < nr; ++r) {
         const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r));
         if (wr != 0.f)
-          vfma<VEC>(acc, wr, ldp<VEC, kBf16In>(o_base, (int64_t)(r0 + r) * o_stride + d));
+          vfma<VEC>(acc, wr, ldp<VEC, kBf16In, kNt>(o_base, (int64_t)(r0 + r) * o_stride + d));
       }
     }
     if (out_f32) {
@@ -197,7 +206,7 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
 // all weights are 0 and the row comes out as O = 0, lse = -inf.
 // merge_row_small for bf16 partials: the same steps, with the loads held raw (RawBf16) and
 // a separate float accumulator per chunk.
-template <int VEC, bool kBf16Out>
+template <int VEC, bool kBf16Out, bool kNt>
 __device__ __forceinline__ void merge_row_small_bf16in(const void* __restrict__ o_base,
                                                        int64_t o_stride,
                                                        const float* __restrict__ l_base,
@@ -208,14 +217,14 @@ __device__ __forceinline__ void merge_row_small_bf16in(const void* __restrict__ 
   using R = typename RawBf16<VEC>::T;
   constexpr int kMaxN = 8, kMaxC = 2;
   const int nc = dv / (64 * VEC);
-  float x = lane < n ? ld<float>(l_base + lane * l_stride) : neg_inf();
+  float x = lane < n ? ld_lse(l_base + lane * l_stride) : neg_inf();
   R v[kMaxN][kMaxC];
 #pragma unroll
   for (int r = 0; r < kMaxN; ++r)
 #pragma unroll
     for (int c = 0; c < kMaxC; ++c)
       if (r < n && c < nc)
-        v[r][c] = ld_raw_bf16<VEC>(o_base, (int64_t)r * o_stride + (c * 64 + lane) * VEC);
+        v[r][c] = ld_raw_bf16<VEC, kNt>(o_base, (int64_t)r * o_stride + (c * 64 + lane) * VEC);
   x = __builtin_isfinite(x) ? x : neg_inf();
   const float m2 = lanes8_max(x) * kLog2e;   // -inf when every partial is empty
   const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
@@ -264,7 +273,7 @@ __device__ __forceinline__ void merge_row_small_bf16in(const void* __restrict__ 
   if (lse_out && lane == 0) *lse_out = sum > 0.f ? (m2 + __log2f(sum)) * kLn2 : neg_inf();
 }
 
-template <int VEC, bool kBf16Out, bool kBf16In = false>
+template <int VEC, bool kBf16Out, bool kBf16In, bool kNt>
 __device__ __forceinline__ void merge_row_small(const void* __restrict__ o_base,
                                                 int64_t o_stride,
                                                 const float* __restrict__ l_base,
@@ -272,21 +281,21 @@ __device__ __forceinline__ void merge_row_small(const void* __restrict__ o_base,
                                                 void* __restrict__ out,
                                                 float* __restrict__ lse_out, int lane) {
   if constexpr (kBf16In) {
-    merge_row_small_bf16in<VEC, kBf16Out>(o_base, o_stride, l_base, l_stride, n, dv, out,
+    merge_row_small_bf16in<VEC, kBf16Out, kNt>(o_base, o_stride, l_base, l_stride, n, dv, out,
                                           lse_out, lane);
     return;
   }
   using V = typename VecT<VEC>::T;
   constexpr int kMaxN = 8, kMaxC = 2;
   const int nc = dv / (64 * VEC);
-  float x = lane < n ? ld<float>(l_base + lane * l_stride) : neg_inf();
+  float x = lane < n ? ld_lse(l_base + lane * l_stride) : neg_inf();
   V v[kMaxN][kMaxC];
 #pragma unroll
   for (int r = 0; r < kMaxN; ++r)
 #pragma unroll
     for (int c = 0; c < kMaxC; ++c)
       if (r < n && c < nc)
-        v[r][c] = ldp<VEC, kBf16In>(o_base, (int64_t)r * o_stride + (c * 64 + lane) * VEC);
+        v[r][c] = ldp<VEC, kBf16In, kNt>(o_base, (int64_t)r * o_stride + (c * 64 + lane) * VEC);
   x = __builtin_isfinite(x) ? x : neg_inf();
   const float m2 = lanes8_max(x) * kLog2e;   // -inf when every partial is empty
   const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
@@ -350,7 +359,7 @@ template <bool kBf16In>
 constexpr int merge_rows_per_block() { return kBf16In ? 4 : 16; }
 
 // dcp_merge with at most 8 partials: one row per wave, all loads up front
-template <int VEC, bool kBf16Out, bool kBf16In>
+template <int VEC, bool kBf16Out, bool kBf16In, bool kNt>
 __global__ __launch_bounds__(64 * merge_rows_per_block<kBf16In>()) void merge_small_kernel(
     const void* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
     int batch, int heads, int dv, void* __restrict__ out, float* __restrict__ lse_out) {
@@ -363,11 +372,11 @@ __global__ __launch_bounds__(64 * merge_rows_per_block<kBf16In>()) void merge_sm
                      : (void*)(static_cast<float*>(out) + row * dv);
   const void* ob = kBf16In ? (const void*)(static_cast<const uint16_t*>(o_partials) + row * dv)
                            : (const void*)(static_cast<const float*>(o_partials) + row * dv);
-  merge_row_small<VEC, kBf16Out, kBf16In>(ob, rows * dv, lse_partials + row, rows, n, dv, o,
-                                          lse_out ? lse_out + row : nullptr, lane);
+  merge_row_small<VEC, kBf16Out, kBf16In, kNt>(ob, rows * dv, lse_partials + row, rows, n, dv,
+                                               o, lse_out ? lse_out + row : nullptr, lane);
 }
 
-template <int VEC, bool kBf16In>
+template <int VEC, bool kBf16In, bool kNt>
 __global__ __launch_bounds__(64 * merge_rows_per_block<kBf16In>()) void merge_kernel(
     const void* __restrict__ o_partials, const float* __restrict__ lse_partials, int n,
     int batch, int heads, int dv, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
@@ -379,10 +388,10 @@ __global__ __launch_bounds__(64 * merge_rows_per_block<kBf16In>()) void merge_ke
   const int lane = threadIdx.x & 63;
   const void* ob = kBf16In ? (const void*)(static_cast<const uint16_t*>(o_partials) + row * dv)
                            : (const void*)(static_cast<const float*>(o_partials) + row * dv);
-  merge_row<VEC, kBf16In>(ob, rows * dv, lse_partials + row, rows, n, dv,
-                          out_f32 ? out_f32 + row * dv : nullptr,
-                          out_bf16 ? out_bf16 + row * dv : nullptr,
-                          lse_out ? lse_out + row : nullptr, lane);
+  merge_row<VEC, kBf16In, kNt>(ob, rows * dv, lse_partials + row, rows, n, dv,
+                               out_f32 ? out_f32 + row * dv : nullptr,
+                               out_bf16 ? out_bf16 + row * dv : nullptr,
+                               lse_out ? lse_out + row : nullptr, lane);
 }
 
 // Split combine: request b's items [off[b], off[b+1]) hold partials of every head.  A
@@ -404,13 +413,15 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
   const int64_t e0 = ((int64_t)i0 * hq + h) * dv;   // first element of the request's partials
   const void* pb = kBf16In ? (const void*)(static_cast<const uint16_t*>(po) + e0)
                            : (const void*)(static_cast<const float*>(po) + e0);
+  // the split partials were just written by the shard kernel: plain loads (cache hits)
   if (merge_small_ok(n, dv, VEC))
-    merge_row_small<VEC, kBf16Out, kBf16In>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h,
-                                            hq, n, dv, kBf16Out ? (void*)obf : (void*)of,
-                                            lse_out + row, lane);
+    merge_row_small<VEC, kBf16Out, kBf16In, false>(pb, (int64_t)hq * dv,
+                                                   plse + (int64_t)i0 * hq + h, hq, n, dv,
+                                                   kBf16Out ? (void*)obf : (void*)of,
+                                                   lse_out + row, lane);
   else
-    merge_row<VEC, kBf16In>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h, hq, n, dv, of,
-                            obf, lse_out + row, lane);
+    merge_row<VEC, kBf16In, false>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h, hq, n, dv,
+                                   of, obf, lse_out + row, lane);
 }
 
 int pick_vec(int dv) {
@@ -432,10 +443,25 @@ hipError_t launch_merge(const void* o_partials, int in_bf16, const float* lse_pa
   float* of = out_bf16 ? nullptr : static_cast<float*>(o_out);
   uint16_t* ob = out_bf16 ? static_cast<uint16_t*>(o_out) : nullptr;
   const int vec = pick_vec(dv);
+  // Partials that fit well inside the 256 MB last-level cache (MALL) are usually still there
+  // when the merge follows the shard calls: plain loads hit it (measured at the MLA decode
+  // shape, 134 MB of float32 partials: 23.1 us in cache against 26.0 us with nt loads, and
+  // 28.6 against 28.0 us from HBM).  Larger ones stream with the nt policy (1.21 GB: 203
+  // against 226 us).
+  const double part_bytes = (double)n * rows * dv * (in_bf16 ? 2 : 4);
+  const bool nt = part_bytes > 192.0 * 1024 * 1024;
   if (merge_small_ok(n, dv, vec)) {
 #define DCP_MERGE_SMALL(V, B, I)                                                               \
-  hipExtLaunchKernelGGL((merge_small_kernel<V, B, I>), grid, block, 0, stream, ev0, ev1, 0,   \
-                        o_partials, lse_partials, n, batch, heads, dv, o_out, lse_out)
+  do {                                                                                         \
+    if (nt)                                                                                    \
+      hipExtLaunchKernelGGL((merge_small_kernel<V, B, I, true>), grid, block, 0, stream, ev0,  \
+                            ev1, 0, o_partials, lse_partials, n, batch, heads, dv, o_out,      \
+                            lse_out);                                                          \
+    else                                                                                       \
+      hipExtLaunchKernelGGL((merge_small_kernel<V, B, I, false>), grid, block, 0, stream, ev0, \
+                            ev1, 0, o_partials, lse_partials, n, batch, heads, dv, o_out,      \
+                            lse_out);                                                          \
+  } while (0)
 #define DCP_MERGE_SMALL_V(B, I)            \
   if (vec == 4) DCP_MERGE_SMALL(4, B, I);  \
   else if (vec == 2) DCP_MERGE_SMALL(2, B, I); \
@@ -449,9 +475,15 @@ hipError_t launch_merge(const void* o_partials, int in_bf16, const float* lse_pa
 #undef DCP_MERGE_SMALL
     return hipGetLastError();
   }
-#define DCP_MERGE(V, I)                                                                         \
-  hipExtLaunchKernelGGL((merge_kernel<V, I>), grid, block, 0, stream, ev0, ev1, 0, o_partials, \
-                        lse_partials, n, batch, heads, dv, of, ob, lse_out)
+#define DCP_MERGE(V, I)                                                                        \
+  do {                                                                                         \
+    if (nt)                                                                                    \
+      hipExtLaunchKernelGGL((merge_kernel<V, I, true>), grid, block, 0, stream, ev0, ev1, 0,   \
+                            o_partials, lse_partials, n, batch, heads, dv, of, ob, lse_out);   \
+    else                                                                                       \
+      hipExtLaunchKernelGGL((merge_kernel<V, I, false>), grid, block, 0, stream, ev0, ev1, 0,  \
+                            o_partials, lse_partials, n, batch, heads, dv, of, ob, lse_out);   \
+  } while (0)
   if (in_bf16) {
     if (vec == 4) DCP_MERGE(4, true);
     else if (vec == 2) DCP_MERGE(2, true);
