@@ -32,17 +32,18 @@
 //     more than 8 (log2 units); the accumulators are rescaled (a rare branch) only then.
 //   * 32-token tiles of latent rows (36 KiB) are copied HBM -> LDS by
 //     global_load_lds_dwordx4 (no register staging) into a 4-deep ring: tiles t and t + 1
-//     are read while t + 2 and t + 3 are in flight.  Waves 0..2 issue the copies from
-//     inline assembly (12 KiB each per tile), paced by their vector-memory counters and a
-//     bare s_barrier per tile, so the compiler never drains them before LDS reads.  The
-//     16-byte chunks of a row are XOR-swizzled by (row mod 8), which spreads the operand
-//     reads over the LDS banks.
+//     are read while t + 2 and t + 3 are in flight.  The copies are issued from inline
+//     assembly between the O^T MFMAs (all four waves, 9 KiB each per tile, for
+//     page-contiguous tiles; waves 0..2, 12 KiB each, otherwise), paced by the waves'
+//     vector-memory counters and a bare s_barrier per tile, so the compiler never drains
+//     them before LDS reads.  The 16-byte chunks of a row are XOR-swizzled by (row mod 8),
+//     which spreads the operand reads over the LDS banks.
 //   * Where each tile comes from is read from a table in LDS, built a window ahead by wave
-//     3, which issues no copies (its block-table loads can be waited for without draining
-//     a copy stream).  When the interleave and the block size are multiples of 32, a tile
-//     is one run of consecutive slots of one page and the table holds its first cache row
-//     (64 tiles per window); otherwise (down to interleave 1) it holds the cache row of
-//     every token (12 tiles per window).
+//     3.  When the interleave and the block size are multiples of 32, a tile is one run of
+//     consecutive slots of one page and the table holds its first cache row (64 tiles per
+//     window; the window build's wait also drains wave 3's copies, once per 64 tiles);
+//     otherwise (down to interleave 1) it holds the cache row of every token (12 tiles per
+//     window) and wave 3 issues no copies, so its block-table waits drain no copy stream.
 //   * Multi-token decode (q_len query positions per request, the last q_len cache tokens
 //     being the request's own draft tokens): each work item gets one workgroup per query
 //     position, all on one XCD (the later ones read the tiles from L2).  Position i sees
@@ -77,10 +78,12 @@ constexpr int kTileBytes = kTile * kRowBytes;  // 36 KiB
 constexpr int kKSteps = kDk / 32;              // 18 k-steps of S^T = K Q^T
 constexpr int kDvTiles = kDv / 16;             // 32 value-dim tiles of O^T
 constexpr int kWaves = 4;                      // 32 heads each
-constexpr int kCopyWaves = 3;                  // waves 0..2 copy; wave 3 builds the tables
-constexpr int kBuilder = 3;
+constexpr int kBuilder = 3;                    // wave 3 builds the tile tables
 constexpr int kSlots = kTileBytes / 1024;      // 36 one-KiB copies per tile
-constexpr int kSlotsPerWave = kSlots / kCopyWaves;   // 12
+// Copier waves: page-contiguous tiles are copied by all four waves (9 one-KiB copies each
+// per tile); with a fine interleave the table builder (wave 3), whose window builds then
+// come every 12 tiles, copies nothing and waves 0..2 take 12 copies each.
+template <bool kFast> constexpr int copy_waves() { return kFast ? 4 : 3; }
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kRescaleSlack = 8.f;
 // K operand prefetch distance (k-steps): 3 where the registers allow it (the page-contiguous
@@ -97,7 +100,7 @@ constexpr int kTabOff = kRingBytes;
 constexpr int kStageOff = kTabOff + 2 * kWinEntries * 4;   // + 3072: block-table entries
 constexpr int kSlotOff = kStageOff + kWinEntries * 4;      // + 1536: copy offsets per thread
 constexpr int kLdsBytes = kSlotOff + kWaves * 64 * 32;     // + 8192 = 160256
-static_assert(kSlots % kCopyWaves == 0, "copy slots");
+static_assert(kSlots % copy_waves<true>() == 0 && kSlots % copy_waves<false>() == 0, "copy slots");
 static_assert(kGenWin > 4 && kFastWin > 4, "a window is built before its first copy");
 
 struct MlaKArgs {
@@ -195,13 +198,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   const char DCP_LDS* lds = (const char DCP_LDS*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
   const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
-  const bool copier = w < kCopyWaves;
+  constexpr int kSlotsPerWave = kSlots / copy_waves<kFast>();
+  const bool copier = w < copy_waves<kFast>();
 
   // ---- tile tables (built by wave kBuilder): window W in half W & 1 of the table.
   // stage(W) copies the block-table entries of window W's tokens (page-contiguous: of each
   // tile's first token) into LDS by global_load_lds_dword; commit(W), one iteration later,
-  // turns them into cache rows (~0 for no token or a bad page).  The builder has no other
-  // vector-memory traffic in the tile loop, so its counter waits for exactly these copies.
+  // turns them into cache rows (~0 for no token or a bad page).  With a fine interleave the
+  // builder has no other vector-memory traffic in the tile loop, so its counter waits for
+  // exactly these copies; with page-contiguous tiles (a window build every 64 tiles) the
+  // wait also drains the builder's own tile copies in flight.
   constexpr int kWin = kFast ? kFastWin : kGenWin;
   constexpr int kPasses = kFast ? 1 : kWinEntries / 64;   // 64 entries per pass
   uint32_t DCP_LDS* const tab = (uint32_t DCP_LDS*)(smem + kTabOff);
@@ -251,11 +257,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     if (__ballot(bad) != 0 && lane == 0) atomicOr(&a.header[0], kErrBlockId);
   };
 
-  // ---- copies (waves 0..2): slot s = 12 w + k of a tile, lane l holds LDS bytes
-  // 16 (64 s + l) of the tile = row r = (64 s + l) / 72, position c = (64 s + l) mod 72,
-  // which receives the row's chunk c ^ (r & 7).  The byte offset of slot k's source chunk
-  // within the tile (< 2^16) is a 16-bit entry of a per-thread LDS record (the tile loop
-  // has no registers to spare for twelve of them).
+  // ---- copies (the copier waves): slot s = kSlotsPerWave w + k of a tile, lane l holds LDS
+  // bytes 16 (64 s + l) of the tile = row r = (64 s + l) / 72, position c = (64 s + l) mod
+  // 72, which receives the row's chunk c ^ (r & 7).  The byte offset of slot k's source
+  // chunk within the tile (< 2^16) is a 16-bit entry of a per-thread LDS record (the tile
+  // loop has no registers to spare for them).
   uint16_t DCP_LDS* const slot_rec = (uint16_t DCP_LDS*)(smem + kSlotOff) + threadIdx.x * 16;
   if (copier) {
 #pragma unroll
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   // The copies of one tile: plan() reads where the tile comes from (and this thread's slot
   // offsets), copy(k) issues slot k.
   struct TileCopy {
-    uint32_t so[kSlotsPerWave / 2];   // slot offsets, two per register
+    uint32_t so[(kSlotsPerWave + 1) / 2];   // slot offsets, two per register
     const char* base;                 // page-contiguous tiles: the tile's first row
     uint32_t dst;                     // LDS address of this wave's first slot
     int nvalid;                       // page-contiguous tiles: rows holding tokens
@@ -279,7 +285,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     TileCopy c;
     const u32x4 lo = *(const u32x4 DCP_LDS*)slot_rec;
     const u32x2 hi = *(const u32x2 DCP_LDS*)(slot_rec + 8);
-    c.so[0] = lo.x; c.so[1] = lo.y; c.so[2] = lo.z; c.so[3] = lo.w; c.so[4] = hi.x; c.so[5] = hi.y;
+    const uint32_t all[6] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y};
+#pragma unroll
+    for (int i = 0; i < (kSlotsPerWave + 1) / 2; ++i) c.so[i] = all[i];
     c.dst = lds_addr + (uint32_t)((ti % kNBuf) * kTileBytes + kSlotsPerWave * w * 1024);
     c.ti = ti;
     if constexpr (kFast) {
@@ -553,7 +561,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
         mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb[1]);
 #pragma unroll
         for (int k = 0; k < kSlotsPerWave; ++k)
-          if (dt == 1 + (k * 8) / 3 && copies) copy_slot(cp, k);
+          if (dt == 1 + (k * 30) / kSlotsPerWave && copies) copy_slot(cp, k);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
