@@ -404,9 +404,16 @@ def main():
                     "merge_us": round(merge_us, 2),
                     "merge_gbs": round(merge_bytes / (merge_us * 1e-6) / 1e9, 1)},
     }
+    copy_gbs = device_copy_gbs(torch)
+    line["device_copy_gbs"] = copy_gbs
+    if roof["unit"] == "GB/s":
+        roof["frac_of_device_copy"] = round(roof["achieved"] / copy_gbs, 4)
+    elif "hbm_gbs" in roof:
+        roof["hbm_frac_of_device_copy"] = round(roof["hbm_gbs"] / copy_gbs, 4)
     if not args.no_secondary:
         line["kernels"][f"{kernel_name}_interleave1_us"] = fine_interleave_us(dca, torch, w, inp,
                                                                              kind)
+        line["kernels"][f"{kernel_name}_cold_us"] = cold_shard_us(dca, torch, w, inp, kind)
     if not args.no_secondary and kind == dca.GQA:
         line["secondary"] = secondary_mla(dca, wl, torch, samples=samples)
         line["secondary_ragged"] = secondary_ragged(dca, wl, torch, samples=samples)
@@ -446,6 +453,47 @@ def fine_interleave_us(dca, torch, w, inp, kind, steps=10):
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in shard_ev)
     return round(ms[len(ms) // 2] * 1e3, 2)
+
+
+def device_copy_gbs(torch, nbytes=1 << 30, reps=5):
+    """Rate of a plain device-to-device copy of `nbytes` (bytes read + bytes written per
+    second, median of `reps`): the practical HBM ceiling the kernels are also compared with."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    ms = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        y.copy_(x)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms.append(ev[0].elapsed_time(ev[1]))
+    del x, y
+    return round(2 * nbytes / (sorted(ms)[reps // 2] * 1e-3) / 1e9, 1)
+
+
+def cold_shard_us(dca, torch, w, inp, kind, steps=10):
+    """Median rank-0 shard kernel duration with the last-level cache (256 MB MALL) and the
+    L2s flushed before each launch by a 1 GiB read: the cache holds nothing of the step's
+    inputs (the KV cache itself is several times larger than the MALL either way)."""
+    flush = torch.ones(1 << 28, device="cuda")
+    kv = inp["k_pages"] if kind == dca.GQA else inp["latent_pages"]
+    v = inp["v_pages"] if kind == dca.GQA else None
+    ws = None
+    ms = []
+    for i in range(steps + 2):
+        flush.sum()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        _, _, ws = dca.shard(inp["q"], kv, v, inp["block_table"], inp["seq_lens"], 0, w.cp_size,
+                             w.interleave, w.scale, kind=kind, max_seq_len=inp["max_seq_len"],
+                             workspace=ws, events=ev, k_scale=inp.get("k_scale"),
+                             v_scale=inp.get("v_scale"))
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(ev[0].elapsed_time(ev[1]))
+    del flush
+    return round(sorted(ms)[len(ms) // 2] * 1e3, 2)
 
 
 def secondary_mla(dca, wl, torch, steps=20, samples=None):
@@ -488,6 +536,7 @@ def secondary_mla(dca, wl, torch, steps=20, samples=None):
 
     keep_sample(samples, w, inp, step.bufs, [0, w.batch - 1])
     mla_i1_us = fine_interleave_us(dca, torch, w, inp, dca.MLA)
+    mla_cold_us = cold_shard_us(dca, torch, w, inp, dca.MLA)
     merge_hbm_us = merge_median(lambda: flush.sum())
     merge_cached_us = merge_median(lambda: None)
     del inp, flush
@@ -506,7 +555,8 @@ def secondary_mla(dca, wl, torch, steps=20, samples=None):
             "merge8_cached_us": round(merge_cached_us, 2),
             "merge8_cached_gbs": round(merge_bytes / (merge_cached_us * 1e-6) / 1e9, 1),
             "merge8_traffic": load_counters("merge_small", "merge.hip", w.name),
-            "mla_interleave1_shard_us": mla_i1_us}
+            "mla_interleave1_shard_us": mla_i1_us,
+            "mla_shard_cold_us": mla_cold_us}
 
 
 def shard_kernel_us(dca, torch, w, inp, kind, steps=10):
