@@ -155,6 +155,13 @@ def cpu_baseline(w, inp, seconds_target=12.0, max_requests=8, max_passes=200):
                       f"request in float64 numpy ({t_total:.1f} s of oracle time)"}
 
 
+def oracle_leg(w, inp, samples):
+    """The benchmark's one use of the CPU oracle, after all GPU timing: its own throughput
+    on a bounded sample of the workload (cpu_baseline) and its verdict on the kept outputs
+    of the timed launches (accuracy)."""
+    return cpu_baseline(w, inp), accuracy(samples)
+
+
 def keep_sample(samples, w, inp, bufs, requests):
     """Host copies of what sampled requests read (query, their pages compacted, a block-table
     row addressing the copy) and of what the timed path wrote for them (every rank's
@@ -422,8 +429,7 @@ def main():
         line["secondary_tiny"] = secondary_tiny(dca, wl, torch, samples=samples)
         line["secondary_multi_token"] = secondary_multi_token(dca, wl, torch)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp)
-        line["accuracy"] = accuracy(samples)
+        line["cpu_baseline"], line["accuracy"] = oracle_leg(w, inp, samples)
     print(json.dumps(line), flush=True)
 
 
