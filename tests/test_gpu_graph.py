@@ -1,6 +1,7 @@
 """The shard and merge entry points do no host synchronisation and allocate nothing
 themselves, so one decode step (every rank's shard call + the merge) can be captured in a
-HIP graph and replayed (GQA, MLA at interleave 1, and multi-token GQA over an fp8 cache).  Every replay must reproduce the eager result bit for bit (the
+HIP graph and replayed (GQA, MLA at interleave 1, multi-token GQA over an fp8 cache, and
+multi-token MLA on page-contiguous tiles).  Every replay must reproduce the eager result bit for bit (the
 kernels are deterministic), with the program's own eager work and synchronisations between
 the replays.
 """
@@ -18,6 +19,8 @@ CASES = [
                         lengths=(5, 300, 2100), seed=32),
     wl.GQA_SHARE_FP8.with_(name="graph_gqa_fp8kv_q2", batch=3, q_len=2, lengths=(3, 700, 4000),
                            seed=33),
+    wl.MLA_DECODE.with_(name="graph_mla_i64_q2", batch=3, q_len=2, lengths=(5, 3000, 9000),
+                        seed=34),
 ]
 
 
