@@ -588,7 +588,7 @@ def secondary_multi_token(dca, wl, torch):
     """Multi-token decode (q_len query positions per request, e.g. speculative decoding):
     the rank-0 shard kernel of the GQA share at q_len 2 and 4 (HBM rate; every K / V row is
     read once for all positions) and of the MLA decode workload at q_len 2 (MFMA
-    utilisation)."""
+    utilisation); and the MLA decode workload with 64 and 32 gathered heads."""
     res = {}
     for nq in (2, 4):
         w = wl.GQA_SHARE.with_(q_len=nq)
@@ -612,6 +612,17 @@ def secondary_multi_token(dca, wl, torch):
                             "tflops": round(flops / us / 1e6, 1),
                             "hbm_gbs": round(byts / us / 1e3, 1)}
     del inp
+    # fewer gathered heads (smaller DCP groups), same cache: 64 and 32 heads
+    for h in (64, 32):
+        w = wl.MLA_DECODE.with_(num_q_heads=h)
+        inp = wl.make_inputs(w, device="cuda")
+        us = shard_kernel_us(dca, torch, w, inp, dca.MLA)
+        byts, flops, tok = mla_launch_cost(w, w.seq_lens(), 0)
+        res[f"mla_decode_h{h}"] = {"shard_us": round(us, 2),
+                                   "mfma_util": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   "tflops": round(flops / us / 1e6, 1),
+                                   "hbm_gbs": round(byts / us / 1e3, 1)}
+        del inp
     torch.cuda.empty_cache()
     return res
 

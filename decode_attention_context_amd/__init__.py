@@ -175,7 +175,8 @@ def shard(q, kv_pages, v_pages, block_table, seq_lens, rank, cp_size, interleave
     """Partial attention of the gathered queries over rank `rank`'s shard.
 
     GQA: q [b, Hq, D], kv_pages = K pages [nb, Hkv, B, D], v_pages = V pages (same shape).
-    MLA: q [b, 128, 576] bf16, kv_pages = latent pages [nb, B, 576], v_pages None.
+    MLA: q [b, H, 576] bf16 with H = 16, 32, 64 or 128 gathered heads, kv_pages = latent
+    pages [nb, B, 576], v_pages None.
     Multi-token decode: q [b, q_len, Hq, D] (q_len <= 4), query position i of request b at
     global position seq_len - q_len + i, causally masked (dcp_attn_shard_mq).
     block_table int32 [b, max_blocks]; seq_lens int32 [b] (global lengths).

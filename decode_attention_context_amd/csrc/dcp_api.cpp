@@ -50,7 +50,7 @@ int shard_impl(const dcp_attn_desc* d, int q_len, int o_dtype, const void* q, co
                                         stream, ev0, ev1)
             : dcp::launch_gqa_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   } else {
-    dcp::MlaArgs a{q, kv, bt, d->block_size, d->max_blocks_per_seq, d->num_blocks,
+    dcp::MlaArgs a{q, kv, bt, d->num_q_heads, d->block_size, d->max_blocks_per_seq, d->num_blocks,
                    rank, cp, il, scale, rows, o_bf16};
     e = dcp::launch_mla_shard(a, p.max_items, w, o, lse, stream, ev0, ev1);
   }

@@ -25,9 +25,11 @@ constexpr int kMaxQLen = 4;
 constexpr int kGqaRowBytes = 256;
 // Head dim of the fp8-cache GQA kernel.
 constexpr int kGqaFp8HeadDim = 128;
-// MLA shape ("The memory wall in long-context inference", MLA item): 128 heads reading one
-// 576-wide latent row per token, the first 512 columns of which are the value.
-constexpr int kMlaHeads = 128;
+// MLA shape ("The memory wall in long-context inference", MLA item): the query heads read
+// one 576-wide latent row per token, the first 512 columns of which are the value.  The
+// gathered heads of a DCP group: 128 (e.g. 16 per rank under tensor parallelism 8, gathered
+// over a DCP group of 8), or 64, 32, 16 for smaller DCP groups.
+inline bool mla_heads_supported(int h) { return h == 16 || h == 32 || h == 64 || h == 128; }
 constexpr int kMlaDk = 576;
 constexpr int kMlaDv = 512;
 
@@ -104,7 +106,7 @@ inline int check_desc(const dcp_attn_desc* d, int q_len, int batch, int64_t max_
     if (!gqa_supported(d->dtype, d->head_dim_qk, d->num_q_heads / d->num_kv_heads, q_len))
       return DCP_EUNSUPPORTED;
   } else if (d->kind == DCP_MLA) {
-    if (d->dtype != DCP_BF16 || d->num_q_heads != kMlaHeads || d->num_kv_heads != 1 ||
+    if (d->dtype != DCP_BF16 || !mla_heads_supported(d->num_q_heads) || d->num_kv_heads != 1 ||
         d->head_dim_qk != kMlaDk || d->head_dim_v != kMlaDv)
       return DCP_EUNSUPPORTED;
   } else {

@@ -67,6 +67,7 @@ struct MlaArgs {
   const void* q;
   const void* latent;
   const int32_t* block_table;
+  int heads;   // query heads: 16, 32, 64 or 128
   int block_size, max_blocks;
   int64_t num_blocks;
   int rank, cp, interleave;

@@ -67,7 +67,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 #define DCP_LDS __attribute__((address_space(3)))
 
-constexpr int kHeads = 128;
+constexpr int kMaxHeads = 128;                 // 4 waves x 2 head tiles of 16
 constexpr int kDk = 576;
 constexpr int kDv = 512;
 constexpr int kTile = kMlaTile;                // 32 tokens per tile
@@ -114,6 +114,8 @@ struct MlaKArgs {
   const int32_t* seq_lens;
   int64_t len_cap;
   int q_len;
+  int heads;     // query heads H (rows per position): 16, 32, 64 or 128
+  int hpw;       // heads per wave, H / 4
   int o_bf16;    // O written in bf16 (requests with a single item; others via the combine)
   void* o_out;
   float* lse_out;
@@ -162,8 +164,12 @@ __device__ __forceinline__ void wait_lgkm0() {
 // vector instructions (or one exp2) beside it without slowing the matrix core (measured on
 // MI355X).  So the softmax of a tile is cut into 18 pieces of that size, one per k-step of
 // the next tile's S^T, and the tile copies are issued between the O^T MFMAs.
-template <bool kFast, bool kNt>
+//
+// HT: 16-head tiles per wave (2 for 128 heads, 1 for 64 or fewer; a wave with fewer than 16
+// heads pads its tile: the padding columns load a valid head's query and are never written).
+template <bool kFast, bool kNt, int HT>
 __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
+  static_assert(HT == 1 || HT == 2, "head tiles per wave");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   // Workgroup ids (dealt round-robin over the 8 XCDs): the q_len workgroups (query
@@ -186,8 +192,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
                                                         a.rank, a.cp, a.interleave));
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   // rows of (request b, position qi) and of (item, position qi) in the outputs
-  const size_t orow = ((size_t)b * a.q_len + qi) * kHeads;
-  const size_t prow = ((size_t)item * a.q_len + qi) * kHeads;
+  const size_t orow = ((size_t)b * a.q_len + qi) * a.heads;
+  const size_t prow = ((size_t)item * a.q_len + qi) * a.heads;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -334,14 +340,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   };
 
   // ---- the query of this wave's heads (B operand of S^T = K Q^T):
-  // qreg[hh][ks] = dims 32 ks + 8 g .. + 8 of head 32 w + 16 hh + i16.  Its loads overlap
+  // qreg[hh][ks] = dims 32 ks + 8 g .. + 8 of head hpw w + 16 hh + i16.  Its loads overlap
   // the table build and the first tile copies; the tile-0 wait below covers them (they
   // were issued first).
-  const int head0 = 32 * w + i16;
-  bf16x8 qreg[2][kKSteps];
+  const int head0 = a.hpw * w + i16;
+  bf16x8 qreg[HT][kKSteps];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const uint16_t* qrow = a.q + (orow + head0 + 16 * hh) * kDk + 8 * g;
+  for (int hh = 0; hh < HT; ++hh) {
+    // padding columns (i16 + 16 hh >= hpw) read the wave's last head
+    const int hq = a.hpw * w + min(i16 + 16 * hh, a.hpw - 1);
+    const uint16_t* qrow = a.q + (orow + hq) * kDk + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
       qreg[hh][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
@@ -362,9 +370,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 
   // O^T accumulators in AGPRs: every definition comes out of an AGPR-constrained asm
   // statement, so the register allocator keeps the loop-carried accumulators there
-  f4 acc[2][kDvTiles];
+  f4 acc[HT][kDvTiles];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
+  for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
     for (int i = 0; i < kDvTiles; ++i) {
       acc[hh][i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   auto settle = [&]() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
       for (int i = 0; i < kDvTiles; i += 4)
         asm volatile("" : "+a"(acc[hh][i]), "+a"(acc[hh][i + 1]), "+a"(acc[hh][i + 2]),
@@ -405,21 +413,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   // S^T MFMAs: compiler builtins, so that the hazard recognizer keeps every later write of
   // their operand registers clear of the matrix core's reads.  Their accumulators stay in
   // VGPRs (the file is built with -amdgpu-mfma-vgpr-form; the AGPRs all hold O^T).
-  auto qk_step = [&](const bf16x8 (&k2)[2], int ks, f4 (&s)[2][2]) {
+  auto qk_step = [&](const bf16x8 (&k2)[2], int ks, f4 (&s)[2][HT]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      for (int hh = 0; hh < HT; ++hh) {
         s[tt][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             k2[tt], qreg[hh][ks], ks == 0 ? f4{0.f, 0.f, 0.f, 0.f} : s[tt][hh], 0, 0, 0);
       }
   };
 
-  float m[2] = {neg_inf(), neg_inf()};   // running max (log2 units) of this lane's heads
-  float negm[2] = {0.f, 0.f};            // -m, or 0 while m is -inf
-  float ls[2] = {0.f, 0.f};              // this lane's share of the running sums
+  float m[HT], negm[HT], ls[HT];
+#pragma unroll
+  for (int hh = 0; hh < HT; ++hh) {
+    m[hh] = neg_inf();   // running max (log2 units) of this lane's heads
+    negm[hh] = 0.f;      // -m, or 0 while m is -inf
+    ls[hh] = 0.f;        // this lane's share of the running sums
+  }
 
-  f4 sc[2][2];   // S^T of the tile whose softmax runs next: [token half][head tile]
+  f4 sc[2][HT];   // S^T of the tile whose softmax runs next: [token half][head tile]
   // tile 0 (and the query, loaded before it) has landed in every wave's copies
   if (ntiles > 2) wait_vmcnt<2 * kSlotsPerWave>();
   else if (ntiles > 1) wait_vmcnt<kSlotsPerWave>();
@@ -458,7 +470,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < HT; ++hh) {
           sc[0][hh][e] = ((mb >> e) & 1u) ? sc[0][hh][e] : neg_inf();
           sc[1][hh][e] = ((mb >> (16 + e)) & 1u) ? sc[1][hh][e] : neg_inf();
         }
@@ -468,53 +480,62 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     // and then unused: the loop body stays one block) with the online softmax of tile t
     // (base 2) cut into one piece per k-step.  Scores stay unscaled until the exp2:
     // scale * log2(e) > 0 keeps the maxima.
-    f4 sn[2][2];
+    f4 sn[2][HT];
     const char DCP_LDS* tbn = lds + ((t + 1) % kNBuf) * kTileBytes;
     constexpr int kAheadK = ahead_k<kFast>();
     bf16x8 kop[kAheadK + 1][2];
 #pragma unroll
     for (int ks = 0; ks < kAheadK; ++ks) kread(tbn, ks, kop[ks]);
-    float tm[2], alpha[2], p[2][8];
+    float tm[HT], alpha[HT], p[HT][8];
     bool grow = false;   // this lane's accumulators need rescaling
-    bf16x8 pb[2];
+    bf16x8 pb[HT];
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
       if (ks + kAheadK < kKSteps) kread(tbn, ks + kAheadK, kop[(ks + kAheadK) % (kAheadK + 1)]);
       qk_step(kop[ks % (kAheadK + 1)], ks, sn);
       if (ks <= 1) {
         // the lane's max of head tile hh over its 8 tokens
-        const int hh = ks;
+        const int hh = ks < HT ? ks : 0;   // (HT = 1: k-step 1 has no piece)
+        if (ks < HT) {
         const f4 u = sc[0][hh], v = sc[1][hh];
         tm[hh] = max_f(max_f(max_f(u[0], u[1]), max_f(u[2], u[3])),
                        max_f(max_f(v[0], v[1]), max_f(v[2], v[3])));
+        }
       } else if (ks <= 3) {
-        const int hh = ks - 2;
-        tm[hh] = rows_max(tm[hh]) * a.sl2;   // the head's max over the tile (log2 units)
+        const int hh = ks - 2 < HT ? ks - 2 : 0;
+        if (ks - 2 < HT)
+          tm[hh] = rows_max(tm[hh]) * a.sl2;   // the head's max over the tile (log2 units)
       } else if (ks <= 5) {
         // The running max only moves when the tile's max exceeds it by more than
         // kRescaleSlack (always on the first tile with a valid token).  In between the
         // weights stay below 2^kRescaleSlack and the final normalisation by the running sum
         // is exact for any reference max.
-        const int hh = ks - 4;
-        const bool up = tm[hh] > m[hh] + kRescaleSlack;
-        alpha[hh] = up ? __builtin_amdgcn_exp2f(m[hh] - tm[hh]) : 1.f;   // m = -inf -> 0
-        grow = grow || (up && m[hh] != neg_inf());   // accumulators are 0 while m = -inf
-        m[hh] = up ? tm[hh] : m[hh];
-        negm[hh] = up ? -tm[hh] : negm[hh];
+        const int hh = ks - 4 < HT ? ks - 4 : 0;
+        if (ks - 4 < HT) {
+          const bool up = tm[hh] > m[hh] + kRescaleSlack;
+          alpha[hh] = up ? __builtin_amdgcn_exp2f(m[hh] - tm[hh]) : 1.f;   // m = -inf -> 0
+          grow = grow || (up && m[hh] != neg_inf());   // accumulators are 0 while m = -inf
+          m[hh] = up ? tm[hh] : m[hh];
+          negm[hh] = up ? -tm[hh] : negm[hh];
+        }
       } else if (ks <= 13) {
         // two weights per k-step: p = exp2(scale log2e s - m); masked tokens give 0
         const int i = 2 * (ks - 6);           // 0 .. 14 over [hh][tt][e]
-        const int hh = i >> 3, tt = (i >> 2) & 1, e = i & 3;
+        const int hh = (i >> 3) < HT ? (i >> 3) : 0, tt = (i >> 2) & 1, e = i & 3;
+        if ((i >> 3) < HT) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          p[hh][4 * tt + e + u] =
-              __builtin_amdgcn_exp2f(fmaf(sc[tt][hh][e + u], a.sl2, negm[hh]));
+          for (int u = 0; u < 2; ++u)
+            p[hh][4 * tt + e + u] =
+                __builtin_amdgcn_exp2f(fmaf(sc[tt][hh][e + u], a.sl2, negm[hh]));
+        }
       } else if (ks <= 15) {
-        const int hh = ks - 14;
-        const float* q = p[hh];
-        ls[hh] = fmaf(ls[hh], alpha[hh],
-                      ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
-      } else {
+        const int hh = ks - 14 < HT ? ks - 14 : 0;
+        if (ks - 14 < HT) {
+          const float* q = p[hh];
+          ls[hh] = fmaf(ls[hh], alpha[hh],
+                        ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
+        }
+      } else if (ks - 16 < HT) {
         // B operand of O^T += V^T P^T: k slots 8 g .. 8 g + 7 = tokens 4 g + [0, 4) and
         // 16 + 4 g + [0, 4)
         const int hh = ks - 16;
@@ -530,9 +551,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
       settle();
 #pragma unroll
       for (int i = 0; i < kDvTiles; ++i) {
-        acc[0][i] *= alpha[0];
-        acc[1][i] *= alpha[1];
-        asm volatile("" : "+a"(acc[0][i]), "+a"(acc[1][i]));
+#pragma unroll
+        for (int hh = 0; hh < HT; ++hh) {
+          acc[hh][i] *= alpha[hh];
+          asm volatile("" : "+a"(acc[hh][i]));
+        }
       }
     }
 
@@ -558,7 +581,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
         if (dt + kAheadV < kDvTiles) va[(dt + kAheadV) % (kAheadV + 1)] = vop(dt + kAheadV);
         if (dt == 0) mfma_acc<true>(acc[0][dt], va[dt % (kAheadV + 1)], pb[0]);
         else mfma_acc<false>(acc[0][dt], va[dt % (kAheadV + 1)], pb[0]);
-        mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb[1]);
+        if constexpr (HT == 2) mfma_acc<false>(acc[1][dt], va[dt % (kAheadV + 1)], pb[1]);
 #pragma unroll
         for (int k = 0; k < kSlotsPerWave; ++k)
           if (dt == 1 + (k * 30) / kSlotsPerWave && copies) copy_slot(cp, k);
@@ -568,17 +591,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) sc[tt][hh] = sn[tt][hh];
+      for (int hh = 0; hh < HT; ++hh) sc[tt][hh] = sn[tt][hh];
   }
 
   // ---- finalize: O = acc / l per head, lse = (m + log2 l) ln 2
   settle();
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
+  for (int hh = 0; hh < HT; ++hh) {
     const float lt = rows_sum(ls[hh]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (m[hh] + __log2f(lt)) * kLn2 : neg_inf();
     const int head = head0 + 16 * hh;
+    if (i16 + 16 * hh >= a.hpw) continue;   // a padding column (fewer than 16 heads a wave)
     if (g == 0) {
       if (single) a.lse_out[orow + head] = lse;
       else a.plse[prow + head] = lse;
@@ -621,6 +645,8 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   k.seq_lens = a.rows.seq_lens;
   k.len_cap = a.rows.len_cap;
   k.q_len = a.rows.q_len;
+  k.heads = a.heads;
+  k.hpw = a.heads / kWaves;
   k.o_bf16 = a.o_bf16;
   k.o_out = o_out;
   k.lse_out = lse_out;
@@ -633,16 +659,20 @@ hipError_t launch_mla_shard(const MlaArgs& a, int64_t max_items, const WsPtrs& w
   const dim3 grid((unsigned)(groups32 * 4 * kXcds * a.rows.q_len));
   const bool fast = (a.interleave % kTile) == 0 && (a.block_size % kTile) == 0;
   const bool nt = a.rows.q_len == 1;
-#define DCP_MLA_LAUNCH(F, N)                                                                 \
-  hipExtLaunchKernelGGL((mla_shard_kernel<F, N>), grid, dim3(kWaves * 64), 0, stream, ev0, ev1, \
-                        0, k)
+  if (a.heads < kWaves || a.heads > kMaxHeads || a.heads % kWaves != 0)
+    return hipErrorInvalidValue;
+#define DCP_MLA_LAUNCH(F, N, H)                                                              \
+  hipExtLaunchKernelGGL((mla_shard_kernel<F, N, H>), grid, dim3(kWaves * 64), 0, stream, ev0, \
+                        ev1, 0, k)
+#define DCP_MLA_LAUNCH_H(F, N)                  \
+  if (k.hpw > 16) DCP_MLA_LAUNCH(F, N, 2);      \
+  else DCP_MLA_LAUNCH(F, N, 1)
   if (fast) {
-    if (nt) DCP_MLA_LAUNCH(true, true);
-    else DCP_MLA_LAUNCH(true, false);
+    if (nt) { DCP_MLA_LAUNCH_H(true, true); } else { DCP_MLA_LAUNCH_H(true, false); }
   } else {
-    if (nt) DCP_MLA_LAUNCH(false, true);
-    else DCP_MLA_LAUNCH(false, false);
+    if (nt) { DCP_MLA_LAUNCH_H(false, true); } else { DCP_MLA_LAUNCH_H(false, false); }
   }
+#undef DCP_MLA_LAUNCH_H
 #undef DCP_MLA_LAUNCH
   return hipGetLastError();
 }

@@ -76,7 +76,9 @@ typedef enum { DCP_GQA = 0, DCP_MLA = 1 } dcp_kind;
  *        other GQA shape returns DCP_EUNSUPPORTED without launching.
  *   MLA: latent_pages [num_blocks][block_size][head_dim_qk] (BF16),
  *        q [batch][num_q_heads][head_dim_qk] (BF16).
- *        Supported: num_q_heads 128, head_dim_qk 576, head_dim_v 512, num_kv_heads 1.
+ *        Supported: num_q_heads 16, 32, 64 or 128 (the heads gathered over a DCP group:
+ *        e.g. 16 per rank under tensor parallelism 8, times the DCP size), head_dim_qk 576,
+ *        head_dim_v 512, num_kv_heads 1.  Every other MLA shape returns DCP_EUNSUPPORTED.
  *   Every kind: num_blocks * block_size * num_kv_heads < 2^31. */
 typedef struct {
   int32_t kind;               /* dcp_kind */

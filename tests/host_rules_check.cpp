@@ -163,7 +163,9 @@ int expect_desc(const dcp_attn_desc* d, int q_len, int batch, int64_t msl, int c
     return DCP_OK;
   }
   if (d->kind == DCP_MLA) {
-    if (d->dtype != DCP_BF16 || d->num_q_heads != 128 || d->num_kv_heads != 1 ||
+    const bool heads_ok = d->num_q_heads == 16 || d->num_q_heads == 32 ||
+                          d->num_q_heads == 64 || d->num_q_heads == 128;
+    if (d->dtype != DCP_BF16 || !heads_ok || d->num_kv_heads != 1 ||
         d->head_dim_qk != 576 || d->head_dim_v != 512)
       return DCP_EUNSUPPORTED;
     return DCP_OK;
@@ -189,7 +191,8 @@ dcp_attn_desc random_desc(bool plausible) {
     d.kind = mla ? DCP_MLA : DCP_GQA;
     d.dtype = (mla || (next_u64() & 1)) ? DCP_BF16 : DCP_F32;
     d.num_kv_heads = mla ? 1 : pick(hkvs);
-    d.num_q_heads = mla ? 128 : d.num_kv_heads * pick(groups);
+    const int32_t mla_heads[] = {16, 32, 64, 128, 48, 256};
+    d.num_q_heads = mla ? pick(mla_heads) : d.num_kv_heads * pick(groups);
     d.head_dim_qk = mla ? 576 : (d.dtype == DCP_BF16 ? 128 : 64);
     d.head_dim_v = mla ? 512 : d.head_dim_qk;
     const int32_t bss[] = {1, 16, 64, 128, 1024};

@@ -92,7 +92,7 @@ def test_argument_errors_are_host_side():
     assert lib.dcp_attn_shard(*args(0, 2, 128, bad)) == -1
     uns = dca.Desc(dca.GQA, dca.BF16, 8, 1, 96, 96, 128, 256, 1024)       # head dim 96
     assert lib.dcp_attn_shard(*args(0, 2, 128, uns)) == -2
-    mla_bad = dca.Desc(dca.MLA, dca.BF16, 64, 1, 576, 512, 64, 256, 1024)  # 64 heads
+    mla_bad = dca.Desc(dca.MLA, dca.BF16, 96, 1, 576, 512, 64, 256, 1024)  # 96 heads
     assert lib.dcp_attn_shard(*args(0, 2, 64, mla_bad)) == -2
     assert lib.dcp_merge(null, null, 0, 1, 1, 1, null, 0, null, null) == -1
     assert lib.dcp_merge(null, null, 2, 1, 1, 1, null, 5, null, null) == -1

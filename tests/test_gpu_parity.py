@@ -63,6 +63,15 @@ SMALL_MLA = [
     wl.MLA_DECODE.with_(name="mla_i1_c4", batch=2, cp_size=4, interleave=1,
                         lengths=(300, 701), seed=24),
     wl.MLA_LONG.with_(name="mla_i128_c4", batch=2, lengths=(9000, 513), seed=25),
+    # fewer gathered heads (smaller DCP groups): 64, 32 and 16 heads
+    wl.MLA_DECODE.with_(name="mla_h64_c4", batch=3, num_q_heads=64, cp_size=4,
+                        lengths=(1, 700, 3000), seed=26),
+    wl.MLA_DECODE.with_(name="mla_h32_i1_c2", batch=2, num_q_heads=32, cp_size=2, interleave=1,
+                        lengths=(5, 900), seed=27),
+    wl.MLA_DECODE.with_(name="mla_h16_q2_c2", batch=2, num_q_heads=16, cp_size=2, q_len=2,
+                        lengths=(3, 2200), seed=28),
+    wl.MLA_DECODE.with_(name="mla_h64_b16_i100_c3", batch=2, num_q_heads=64, block_size=16,
+                        cp_size=3, interleave=100, lengths=(64, 2500), seed=29),
 ]
 
 
@@ -196,3 +205,15 @@ def test_gqa_items_beyond_64_tiles(gpu_lib, w):
     torch.cuda.synchronize()
     assert _plan_chunk(ws) > 64 * 64 * 2, _plan_chunk(ws)
     _run_and_check(w)
+
+
+@pytest.mark.parametrize("heads", [8, 48, 96, 256])
+def test_mla_rejects_head_counts(gpu_lib, heads):
+    """MLA takes 16, 32, 64 or 128 gathered heads; other counts are refused before any
+    launch."""
+    w = wl.MLA_DECODE.with_(name=f"mla_h{heads}", batch=1, num_q_heads=heads, cp_size=2,
+                            lengths=(100,), seed=30)
+    inp = wl.make_inputs(w, device="cuda")
+    with pytest.raises(dca.DCPError):
+        dca.shard(inp["q"], inp["latent_pages"], None, inp["block_table"], inp["seq_lens"], 0,
+                  w.cp_size, w.interleave, w.scale, kind=dca.MLA)

@@ -29,7 +29,9 @@ def _draw(seed):
     lengths = tuple(int(rng.choice(edges)) if rng.random() < 0.3 else int(rng.integers(1, 2500))
                     for _ in range(batch))
     if kind == "mla":
+        heads = int(rng.choice([16, 32, 64, 128]))
         return wl.MLA_DECODE.with_(name=f"rand{seed}_mla", batch=batch, q_len=q_len,
+                                   num_q_heads=heads,
                                    block_size=block, cp_size=cp, interleave=il,
                                    lengths=lengths, seed=seed)
     hkv = int(rng.choice([1, 2, 4]))
