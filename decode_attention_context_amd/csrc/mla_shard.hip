@@ -3,22 +3,23 @@
 // What it computes ("vLLM Decode Context Parallelism for long-context workloads" blog,
 // "DCP execution flow", step "Compute", and "The memory wall in long-context inference",
 // MLA item: all query heads share one low-rank latent KV row): for every request b and
-// each of the 128 gathered query heads h, attention over the tokens this rank owns, with
-// key = the token's 576-wide latent row and value = its first 512 columns, plus the
-// natural-log LSE of the scaled scores.
+// each of the H gathered query heads h (H = 128, or 64, 32, 16 for smaller DCP groups),
+// attention over the tokens this rank owns, with key = the token's 576-wide latent row and
+// value = its first 512 columns, plus the natural-log LSE of the scaled scores.
 //
-// Per token this is 128 x (576 + 512) multiply-adds against 1152 bytes of cache: a dense
-// contraction (about 242 flop/byte, just below the bf16 ridge of MI355X), so both products
-// run on v_mfma_f32_16x16x32_bf16 and the kernel has to keep the HBM stream and the matrix
-// cores busy at the same time.
+// Per token at 128 heads this is 128 x (576 + 512) multiply-adds against 1152 bytes of
+// cache: a dense contraction (about 242 flop/byte, just below the bf16 ridge of MI355X), so
+// both products run on v_mfma_f32_16x16x32_bf16 and the kernel has to keep the HBM stream
+// and the matrix cores busy at the same time.
 //
-// Design:
+// Design (described at 128 heads; fewer heads give each wave one 16-head tile, H / 4 of its
+// columns real):
 //   * One workgroup of four waves (one per SIMD) per work item (request, local token range)
-//     and query position, holding all 128 heads, so each latent tile is copied from HBM
-//     into LDS exactly once.  Wave w owns heads 32 w .. 32 w + 31 (two 16-head tiles) from
-//     end to end: its query lives in 144 VGPRs and its O^T accumulators (32 heads x 512
-//     dims, float32) in all 256 AGPRs, so no score, weight or rescale factor ever moves
-//     between waves.
+//     and query position, holding all heads, so each latent tile is copied from HBM into
+//     LDS exactly once.  Wave w owns heads 32 w .. 32 w + 31 (two 16-head tiles) from end
+//     to end: its query lives in 144 VGPRs and its O^T accumulators (32 heads x 512 dims,
+//     float32) in all 256 AGPRs, so no score, weight or rescale factor ever moves between
+//     waves.
 //   * S^T = K Q^T per 16 tokens x 16 heads on v_mfma_f32_16x16x32_bf16 (K operand: one
 //     16-byte LDS read per lane feeding the MFMAs of both head tiles); the lane holding
 //     head i16 and tokens 4 g .. 4 g + 3 of each 16-token half then holds, packed to bf16,
