@@ -78,7 +78,7 @@ constexpr int kRowChunks = kRowBytes / 16;     // 72
 constexpr int kTileBytes = kTile * kRowBytes;  // 36 KiB
 constexpr int kKSteps = kDk / 32;              // 18 k-steps of S^T = K Q^T
 constexpr int kDvTiles = kDv / 16;             // 32 value-dim tiles of O^T
-constexpr int kWaves = 4;                      // 32 heads each
+constexpr int kWaves = 4;                      // H / 4 heads each (32 at 128 heads)
 constexpr int kBuilder = 3;                    // wave 3 builds the tile tables
 constexpr int kSlots = kTileBytes / 1024;      // 36 one-KiB copies per tile
 // Copier waves: page-contiguous tiles are copied by all four waves (9 one-KiB copies each
