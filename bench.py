@@ -9,7 +9,7 @@ on 1 KV head, head dim 128, bf16 cache in 128-token pages, DCP size 2 with inter
 Printed: one JSON line with the throughput (KV tokens of context attended per second), the
 roofline of the dominant kernel (the GQA shard kernel, timed with HIP events recorded on
 its own stream around every launch), the CPU oracle timed on a bounded sample of the
-same workload, and `accuracy`: the oracle's verdict on sampled requests of every timed
+same workload, and `accuracy`: the oracle's comparison with sampled requests of every timed
 workload, read back from the outputs of the timed launches themselves (both oracle legs
 are skipped with --no-cpu-baseline).  `secondary` adds the MLA shard kernel (MFMA utilisation) and the 8-way
 merge on the MLA decode workload.
