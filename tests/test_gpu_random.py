@@ -17,24 +17,27 @@ from parity_helpers import check_requests, run_shards
 pytestmark = pytest.mark.gpu
 
 
-def _draw(seed):
+def _draw(seed, wide=False):
+    """wide: longer sequences (to 20000 tokens, items of many tiles), batches to 6, blocks to
+    256, interleaves to 512, up to 8 KV heads."""
     rng = np.random.default_rng(seed)
     kind = ["gqa_bf16", "gqa_f32", "gqa_fp8", "mla"][seed % 4]
     q_len = int(rng.integers(1, 5))
-    block = int(rng.choice([16, 32, 64, 128]))
+    block = int(rng.choice([16, 32, 64, 128, 256] if wide else [16, 32, 64, 128]))
     cp = int(rng.integers(1, 9))
-    il = int(rng.choice([1, 2, 3, 16, 32, 64, 100, 128, 256]))
-    batch = int(rng.integers(1, 4))
-    edges = [1, block, block + 1, il * cp, il * cp + 1]
-    lengths = tuple(int(rng.choice(edges)) if rng.random() < 0.3 else int(rng.integers(1, 2500))
-                    for _ in range(batch))
+    il = int(rng.choice([1, 2, 3, 7, 16, 32, 64, 96, 128, 256, 512] if wide else
+                        [1, 2, 3, 16, 32, 64, 100, 128, 256]))
+    batch = int(rng.integers(1, 7 if wide else 4))
+    edges = [1, block, block + 1, il * cp, il * cp + 1] + ([2, 4096, 8193] if wide else [])
+    lengths = tuple(int(rng.choice(edges)) if rng.random() < 0.3 else
+                    int(rng.integers(1, 20000 if wide else 2500)) for _ in range(batch))
     if kind == "mla":
         heads = int(rng.choice([16, 32, 64, 128]))
         return wl.MLA_DECODE.with_(name=f"rand{seed}_mla", batch=batch, q_len=q_len,
                                    num_q_heads=heads,
                                    block_size=block, cp_size=cp, interleave=il,
                                    lengths=lengths, seed=seed)
-    hkv = int(rng.choice([1, 2, 4]))
+    hkv = int(rng.choice([1, 2, 4, 8] if wide else [1, 2, 4]))
     # every group the GQA kernels take: q_len * G <= 64 rows per KV head
     groups = [g for g in (1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 21, 32, 64) if g * q_len <= 64]
     g = int(rng.choice(groups))
@@ -48,9 +51,10 @@ def _draw(seed):
 SEEDS = list(range(2000, 2096))
 
 
-@pytest.mark.parametrize("seed", SEEDS)
-def test_random_case(gpu_lib, seed):
-    w = _draw(seed)
+WIDE_SEEDS = list(range(5000, 5048))
+
+
+def _check(w):
     print(f"[rand] {w.name}: q_len={w.q_len} batch={w.batch} Hq={w.num_q_heads} "
           f"Hkv={w.num_kv_heads} C={w.cp_size} I={w.interleave} B={w.block_size} "
           f"lengths={w.lengths}", flush=True)
@@ -60,3 +64,13 @@ def test_random_case(gpu_lib, seed):
     o_m, l_m = dca.merge(o_parts, l_parts)
     check_requests(inp, kind, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
                    list(range(w.batch)), w.name)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_case(gpu_lib, seed):
+    _check(_draw(seed))
+
+
+@pytest.mark.parametrize("seed", WIDE_SEEDS)
+def test_random_wide_case(gpu_lib, seed):
+    _check(_draw(seed, wide=True))
