@@ -352,9 +352,10 @@ __host__ __device__ __forceinline__ bool merge_small_ok(int n, int dv, int vec) 
 
 constexpr int kRowsPerBlock = 4;
 // dcp_merge rows (waves) per workgroup.  Measured on MI355X, eight float32 partials of
-// 64 x 128 rows x 512 dims from HBM: 28.4 us at 16 rows against 29.4 us at 4 and 31.4 us at
-// 1 (fewer, larger workgroups reach the stream's full rate sooner), 512 x 128 rows equal;
-// bf16 partials of 512 x 128 rows: 137 us at 4 rows against 177 us at 16.
+// 64 x 128 rows x 512 dims from HBM: 28.4 us at 16 rows against 29.0 us at 8, 29.4 us at 4
+// and 31.4 us at 1 (fewer, larger workgroups reach the stream's full rate sooner), 512 x 128
+// rows equal; bf16 partials of 512 x 128 rows (held raw until use): 114.5 us at 4 rows,
+// 113.0-115.0 at 8 and 115.7-116.7 at 16.
 template <bool kBf16In>
 constexpr int merge_rows_per_block() { return kBf16In ? 4 : 16; }
 
