@@ -32,8 +32,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 def _src_hash(name):
     """sha256[:16] of a kernel source together with the headers every kernel includes."""
     h = hashlib.sha256()
-    for n in (name, "common.h", "launch.h"):
-        with open(os.path.join(ROOT, "decode_attention_context_amd", "csrc", n), "rb") as f:
+    csrc = os.path.join(ROOT, "decode_attention_context_amd", "csrc")
+    for path in [os.path.join(csrc, n) for n in (name, "common.h", "launch.h", "host_rules.h",
+                                                 "walker.h")] + \
+            [os.path.join(ROOT, "include", "dcp_attn.h")]:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 

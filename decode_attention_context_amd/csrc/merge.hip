@@ -14,6 +14,8 @@
 // load, so a row costs one memory round trip; weights of empty partials are exactly 0 and
 // their rows (which may hold garbage) are excluded by a select, never multiplied.  More
 // partials are streamed eight at a time, empty ones not read.  The kernel is HBM-bound.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace dcp {
@@ -120,13 +122,16 @@ __device__ __forceinline__ void vfma(float (&acc)[VEC], float w, const typename 
   for (int i = 0; i < VEC; ++i) acc[i] = fmaf(w, p[i], acc[i]);
 }
 
-// Merge `n` partial rows o_base[r * o_stride .. + dv) with lse l_base[r * l_stride].
-// The lse values are spread over the lanes (64 per pass) and reduced with DPP, so the row
-// costs one round trip for them; the partial rows are then streamed 8 at a time.
-template <int VEC, bool kBf16In, bool kNt>
+// Merge `n` partial rows o_base[r * o_stride + c] with lse l_base[r * l_stride] over the
+// columns c in [c0, c1) (a multiple of 64 * VEC wide, or the whole row); lse_out, when given,
+// receives the merged lse.  The lse values are spread over the lanes (64 per pass) and
+// reduced with DPP, so the row costs one round trip for them; the partial rows are then
+// streamed in batches of kB whose loads all leave before the first is used (bf16 partials
+// held raw until use), a batch's tail predicated rather than loaded one partial at a time.
+template <int VEC, bool kBf16In, bool kNt, int kB = 8>
 __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64_t o_stride,
                                           const float* __restrict__ l_base, int64_t l_stride,
-                                          int n, int dv, float* __restrict__ out_f32,
+                                          int n, int c0, int c1, float* __restrict__ out_f32,
                                           uint16_t* __restrict__ out_bf16,
                                           float* __restrict__ lse_out, int lane) {
   using V = typename VecT<VEC>::T;
@@ -140,7 +145,7 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
   m = wave_max_dpp(m);
   if (m == neg_inf()) {
     // every partial is empty
-    for (int d = lane * VEC; d < dv; d += 64 * VEC) {
+    for (int d = c0 + lane * VEC; d < c1; d += 64 * VEC) {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         if (out_f32) out_f32[d + i] = 0.f;
@@ -157,7 +162,7 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
     wpart += x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
   }
   const float inv = 1.f / wave_sum_dpp(wpart);
-  for (int d = lane * VEC; d < dv; d += 64 * VEC) {
+  for (int d = c0 + lane * VEC; d < c1; d += 64 * VEC) {
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
@@ -165,24 +170,36 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
       const float x = lse_at(r0 + lane);
       const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
       const int nr = n - r0 < 64 ? n - r0 : 64;
-      int r = 0;
-      for (; r + 8 <= nr; r += 8) {
-        V v[8];
-        float wv[8];
+      for (int r = 0; r < nr; r += kB) {
+        float wv[kB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          wv[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r + u));
-          if (wv[u] != 0.f)
-            v[u] = ldp<VEC, kBf16In, kNt>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
+        for (int u = 0; u < kB; ++u)   // 0 past the row's partials (readlane of lanes >= nr)
+          wv[u] = r + u < nr ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r + u))
+                             : 0.f;
+        if constexpr (kBf16In) {
+          typename RawBf16<VEC>::T v[kB];
+#pragma unroll
+          for (int u = 0; u < kB; ++u)
+            if (wv[u] != 0.f)
+              v[u] = ld_raw_bf16<VEC, kNt>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
+#pragma unroll
+          for (int u = 0; u < kB; ++u) {
+            if (wv[u] != 0.f) {
+              float f[VEC];
+              widen_bf16<VEC>(v[u], f);
+#pragma unroll
+              for (int i = 0; i < VEC; ++i) acc[i] = fmaf(wv[u], f[i], acc[i]);
+            }
+          }
+        } else {
+          V v[kB];
+#pragma unroll
+          for (int u = 0; u < kB; ++u)
+            if (wv[u] != 0.f) v[u] = ldp<VEC, false, kNt>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
+#pragma unroll
+          for (int u = 0; u < kB; ++u)
+            if (wv[u] != 0.f) vfma<VEC>(acc, wv[u], v[u]);
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (wv[u] != 0.f) vfma<VEC>(acc, wv[u], v[u]);
-      }
-      for (; r < nr; ++r) {
-        const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r));
-        if (wr != 0.f)
-          vfma<VEC>(acc, wr, ldp<VEC, kBf16In, kNt>(o_base, (int64_t)(r0 + r) * o_stride + d));
       }
     }
     if (out_f32) {
@@ -195,6 +212,110 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
 #pragma unroll
       for (int i = 0; i < VEC; ++i) out_bf16[d + i] = (uint16_t)f32_to_bf16_rne(acc[i] * inv);
     }
+  }
+  if (lse_out && lane == 0) *lse_out = (m2 - __log2f(inv)) * kLn2;
+}
+
+// One wave merges the columns [c0, c0 + 64 * VEC) of a row (a split combine with few rows).
+// The first kB partials' loads leave together with the lse loads, before their weights are
+// known, so a row of at most kB partials costs one round trip; later partials follow in
+// batches of kB.  Every item of a request has a partial row in the workspace, so the early
+// loads stay in bounds; an empty partial's row (any bits) is never used.
+template <int VEC, bool kBf16In, int kB>
+__device__ __forceinline__ void merge_cols(const void* __restrict__ o_base, int64_t o_stride,
+                                           const float* __restrict__ l_base, int64_t l_stride,
+                                           int n, int c0, float* __restrict__ out_f32,
+                                           uint16_t* __restrict__ out_bf16,
+                                           float* __restrict__ lse_out, int lane) {
+  using V = typename VecT<VEC>::T;
+  using R = typename std::conditional<kBf16In, typename RawBf16<VEC>::T, V>::type;
+  const int d = c0 + lane * VEC;
+  auto load = [&](int r) -> R {
+    const int64_t e = (int64_t)r * o_stride + d;
+    if constexpr (kBf16In) return ld_raw_bf16<VEC, false>(o_base, e);
+    else return ld<V, false>(static_cast<const float*>(o_base) + e);
+  };
+  R first[kB];
+#pragma unroll
+  for (int u = 0; u < kB; ++u)
+    if (u < n) first[u] = load(u);
+  auto lse_at = [&](int r) -> float {
+    if (r >= n) return neg_inf();
+    const float x = ld_lse(l_base + r * l_stride);
+    return __builtin_isfinite(x) ? x : neg_inf();
+  };
+  float m = neg_inf();
+  for (int r0 = 0; r0 < n; r0 += 64) m = fmaxf(m, lse_at(r0 + lane));
+  m = wave_max_dpp(m);
+  if (m == neg_inf()) {
+    // every partial is empty
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      if (out_f32) out_f32[d + i] = 0.f;
+      else out_bf16[d + i] = 0;
+    }
+    if (lse_out && lane == 0) *lse_out = neg_inf();
+    return;
+  }
+  const float m2 = m * kLog2e;
+  float wpart = 0.f;
+  for (int r0 = 0; r0 < n; r0 += 64) {
+    const float x = lse_at(r0 + lane);
+    wpart += x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
+  }
+  const float inv = 1.f / wave_sum_dpp(wpart);
+  float acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+  auto add = [&](float w, const R& v) {
+    float f[VEC];
+    if constexpr (kBf16In) {
+      widen_bf16<VEC>(v, f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) f[i] = reinterpret_cast<const float*>(&v)[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = fmaf(w, f[i], acc[i]);
+  };
+  for (int r0 = 0; r0 < n; r0 += 64) {
+    const float x = lse_at(r0 + lane);
+    const float wl = x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
+    const int nr = n - r0 < 64 ? n - r0 : 64;
+    // the weight of partial r0 + r + u (0 past the row's partials: lanes >= nr)
+    auto wt = [&](int r, int u) -> float {
+      return r + u < nr ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), r + u))
+                        : 0.f;
+    };
+    if (r0 == 0) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const float w = wt(0, u);
+        if (w != 0.f) add(w, first[u]);
+      }
+    }
+    for (int r = r0 == 0 ? kB : 0; r < nr; r += kB) {
+      float wv[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) wv[u] = wt(r, u);
+      R v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (wv[u] != 0.f) v[u] = load(r0 + r + u);
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (wv[u] != 0.f) add(wv[u], v[u]);
+    }
+  }
+  if (out_f32) {
+    V o;
+    float* po = reinterpret_cast<float*>(&o);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) po[i] = acc[i] * inv;
+    st<V>(out_f32 + d, o);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) out_bf16[d + i] = (uint16_t)f32_to_bf16_rne(acc[i] * inv);
   }
   if (lse_out && lane == 0) *lse_out = (m2 - __log2f(inv)) * kLn2;
 }
@@ -351,6 +472,10 @@ __host__ __device__ __forceinline__ bool merge_small_ok(int n, int dv, int vec) 
 }
 
 constexpr int kRowsPerBlock = 4;
+// Split combines whose rows come to at most this many column chunks (two waves per SIMD on
+// 256 CUs) give each chunk a wave of its own; that kernel holds up to 32 partial chunks per
+// lane in registers (two waves per SIMD).
+constexpr int64_t kWideCombineWaves = 2048;
 // dcp_merge rows (waves) per workgroup.  Measured on MI355X, eight float32 partials of
 // 64 x 128 rows x 512 dims from HBM: 28.4 us at 16 rows against 29.0 us at 8, 29.4 us at 4
 // and 31.4 us at 1 (fewer, larger workgroups reach the stream's full rate sooner), 512 x 128
@@ -389,7 +514,7 @@ __global__ __launch_bounds__(64 * merge_rows_per_block<kBf16In>()) void merge_ke
   const int lane = threadIdx.x & 63;
   const void* ob = kBf16In ? (const void*)(static_cast<const uint16_t*>(o_partials) + row * dv)
                            : (const void*)(static_cast<const float*>(o_partials) + row * dv);
-  merge_row<VEC, kBf16In, kNt>(ob, rows * dv, lse_partials + row, rows, n, dv,
+  merge_row<VEC, kBf16In, kNt>(ob, rows * dv, lse_partials + row, rows, n, 0, dv,
                                out_f32 ? out_f32 + row * dv : nullptr,
                                out_bf16 ? out_bf16 + row * dv : nullptr,
                                lse_out ? lse_out + row : nullptr, lane);
@@ -399,11 +524,22 @@ __global__ __launch_bounds__(64 * merge_rows_per_block<kBf16In>()) void merge_ke
 // request with a single item was written directly by the shard kernel; a request with no
 // item (empty shard) gets O = 0, lse = -inf.
 // Split partials are float32, or bf16 when kBf16In (widened exactly).
-template <int VEC, bool kBf16Out, bool kBf16In>
+// One wave per row, or with kWide (few rows: long sequences split over many items) one wave
+// per 64 * VEC columns of a row, whose first 32 bf16 (16 float32) partial loads leave with
+// the lse loads: a row of up to 32 items costs one round trip instead of one per 8 partials.
+// Measured on MI355X, MLA over 8 requests x 50000 local tokens (1024 rows of 512 columns,
+// 32 bf16 partials each): 11.0 us against 24.8 us one wave per row; 64 requests (8192 rows,
+// 4 partials) 9.7 us one wave per row against 24 us column-split.  The wave of the first
+// columns writes lse.
+template <int VEC, bool kBf16Out, bool kBf16In, bool kWide>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
     const int32_t* __restrict__ off, const float* __restrict__ plse, const void* __restrict__ po,
     int batch, int hq, int dv, void* __restrict__ o_out, float* __restrict__ lse_out) {
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int kCols = 64 * VEC;
+  const int chunks = kWide ? dv / kCols : 1;   // the launcher picks kWide only if dv % kCols == 0
+  const int64_t row = kWide ? wave / chunks : wave;
+  const int c0 = kWide ? (int)(wave - row * chunks) * kCols : 0;
   if (row >= (int64_t)batch * hq) return;
   const int b = (int)(row / hq), h = (int)(row - (int64_t)b * hq);
   const int i0 = off[b], n = off[b + 1] - i0;
@@ -415,14 +551,18 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void split_combine_kernel(
   const void* pb = kBf16In ? (const void*)(static_cast<const uint16_t*>(po) + e0)
                            : (const void*)(static_cast<const float*>(po) + e0);
   // the split partials were just written by the shard kernel: plain loads (cache hits)
-  if (merge_small_ok(n, dv, VEC))
+  if constexpr (kWide)
+    merge_cols<VEC, kBf16In, kBf16In ? 32 : 16>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h,
+                                                hq, n, c0, of, obf,
+                                                c0 == 0 ? lse_out + row : nullptr, lane);
+  else if (merge_small_ok(n, dv, VEC))
     merge_row_small<VEC, kBf16Out, kBf16In, false>(pb, (int64_t)hq * dv,
                                                    plse + (int64_t)i0 * hq + h, hq, n, dv,
                                                    kBf16Out ? (void*)obf : (void*)of,
                                                    lse_out + row, lane);
   else
-    merge_row<VEC, kBf16In, false>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h, hq, n, dv,
-                                   of, obf, lse_out + row, lane);
+    merge_row<VEC, kBf16In, false>(pb, (int64_t)hq * dv, plse + (int64_t)i0 * hq + h, hq, n,
+                                   0, dv, of, obf, lse_out + row, lane);
 }
 
 int pick_vec(int dv) {
@@ -501,15 +641,25 @@ hipError_t launch_merge(const void* o_partials, int in_bf16, const float* lse_pa
 hipError_t launch_split_combine(const WsPtrs& ws, int batch, int hq, int dv, void* o_out,
                                 int out_bf16, float* lse_out, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * hq;
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int vec = pick_vec(dv);
+  const int64_t chunks = dv % (64 * vec) == 0 ? dv / (64 * vec) : 1;
+  const bool wide = chunks > 1 && rows * chunks <= kWideCombineWaves;
+  const int64_t waves = wide ? rows * chunks : rows;
+  const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
   const dim3 block(64 * kRowsPerBlock);
-#define DCP_COMBINE(V, B, I)                                                                  \
-  hipLaunchKernelGGL((split_combine_kernel<V, B, I>), grid, block, 0, stream, ws.off, ws.plse, \
-                     ws.po, batch, hq, dv, o_out, lse_out)
+#define DCP_COMBINE(V, B, I)                                                                   \
+  do {                                                                                         \
+    if (wide)                                                                                  \
+      hipLaunchKernelGGL((split_combine_kernel<V, B, I, true>), grid, block, 0, stream, ws.off, \
+                         ws.plse, ws.po, batch, hq, dv, o_out, lse_out);                       \
+    else                                                                                       \
+      hipLaunchKernelGGL((split_combine_kernel<V, B, I, false>), grid, block, 0, stream,       \
+                         ws.off, ws.plse, ws.po, batch, hq, dv, o_out, lse_out);               \
+  } while (0)
 #define DCP_COMBINE_I(V, B)                \
   if (ws.po_bf16) DCP_COMBINE(V, B, true); \
   else DCP_COMBINE(V, B, false)
-  switch (pick_vec(dv) * 2 + (out_bf16 ? 1 : 0)) {
+  switch (vec * 2 + (out_bf16 ? 1 : 0)) {
     case 8: DCP_COMBINE_I(4, false); break;
     case 9: DCP_COMBINE_I(4, true); break;
     case 4: DCP_COMBINE_I(2, false); break;
