@@ -8,11 +8,12 @@
 // variant, half the bytes per token of bf16.
 //
 // Design (the bf16 kernel's matrix-core variant, re-laid for 128-byte rows):
-//   * Four waves per (work item, KV head, slice of 32 of the R = q_len * G <= 64 query
-//     rows), two workgroups per CU; wave w takes token quarter w of every 64-token tile for
-//     all rows of the slice (one or two 16-row tiles, rows past R padding: idle matrix
-//     lanes cost nothing in an HBM-bound kernel) and keeps its own online softmax; the
-//     quarters merge through LDS by the LSE identity after the last tile.
+//   * Four waves per (work item, KV head) for R = q_len * G <= 48 query rows, or per (work
+//     item, KV head, slice of 32 rows) for R up to 64, two workgroups per CU; wave w takes
+//     token quarter w of every 64-token tile for all rows of the workgroup (one to three
+//     16-row tiles, rows past R padding: idle matrix lanes cost nothing in an HBM-bound
+//     kernel) and keeps its own online softmax; the quarters merge through LDS by the LSE
+//     identity after the last tile, one row tile at a time.
 //   * 64-token tiles of K and V rows (8 KiB each) are copied HBM -> LDS by
 //     global_load_lds_dwordx4 with the non-temporal policy into a double buffer, paced by
 //     each wave's vector-memory counter and a bare s_barrier (a 3-deep ring, two tiles in
@@ -94,7 +95,7 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w) {
 template <int RT>
 __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
   constexpr int kOStride = kD + 4;                 // merge scratch: floats per row
-  constexpr int kRows = 16 * RT;                   // query rows per wave
+  constexpr int kRows = 16;                        // scratch rows per wave (one row tile a pass)
   constexpr int kScratch = kWaves * kRows * kOStride * 4;
   constexpr int kLds = kScratch > kNBuf * kBufBytes ? kScratch : kNBuf * kBufBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
@@ -106,13 +107,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
   const int4 it = a.items[blockIdx.x];   // in dispatch order, longest first
   const int b = it.x, j0 = it.y, j1 = it.z;
   const int item = it.w;
-  // blockIdx.y = KV head + hkv * (32-row slice); the slices of one item share its K / V
-  // tiles (a later slice's reads mostly hit L2)
+  // blockIdx.y = KV head + hkv * (row slice); the slices of one item share its K / V tiles
+  // (a later slice's reads mostly hit L2)
   const int kvh = (int)blockIdx.y % a.hkv;
-  const int rbase = 32 * ((int)blockIdx.y / a.hkv);   // first query row of the slice
+  const int rbase = 16 * RT * ((int)blockIdx.y / a.hkv);   // first query row of the slice
   // K / V copies stream with the non-temporal policy, except when two slices read the same
   // tiles: the second then finds them in L2
-  const bool nt = a.q_len * (a.hq / a.hkv) <= 32;
+  const bool nt = a.q_len * (a.hq / a.hkv) <= 16 * RT;
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   const int G = a.hq / a.hkv;
   const int R = a.q_len * G;
@@ -349,40 +350,40 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
     vm0 = vm1;
   }
 
-  // ---- merge the four token quarters of each row through LDS (the tile buffers are free
-  // once every wave has passed the barrier; no copy is in flight).  Scratch rows are
-  // (wave, row tile, lane column), dims in natural order.
+  // ---- merge the four token quarters of each row through LDS, one row tile per pass (the
+  // tile buffers are free once every wave has passed the barrier; no copy is in flight).
+  // Scratch rows are (wave, lane column), dims in natural order.
   float DCP_LDS* osc = (float DCP_LDS*)smem;
   wait_vmcnt<0>();
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const float lt = rows_sum(ls[r]);
-    const int sr = w * kRows + 16 * r + i16;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f4 v = {acc[r][4 * h][e], acc[r][4 * h + 1][e], acc[r][4 * h + 2][e],
-                      acc[r][4 * h + 3][e]};
-        *reinterpret_cast<f4 DCP_LDS*>(osc + sr * kOStride + 64 * h + 16 * g + 4 * e) = v;
-      }
-    if (g == 0) {
-      mls[sr * 2] = m[r];
-      mls[sr * 2 + 1] = lt;
-    }
-  }
-  __syncthreads();
   // wave tq finishes dims 32 tq .. 32 tq + 31 of every row
   const int d0 = 32 * tq + 8 * (lane & 3);
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int row = 16 * r + (lane >> 2);   // in the slice; rbase + row in the request
+    __syncthreads();   // the tile buffers (first pass) or the previous pass's rows are free
+    {
+      const float lt = rows_sum(ls[r]);
+      const int sr = w * kRows + i16;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f4 v = {acc[r][4 * h][e], acc[r][4 * h + 1][e], acc[r][4 * h + 2][e],
+                        acc[r][4 * h + 3][e]};
+          *reinterpret_cast<f4 DCP_LDS*>(osc + sr * kOStride + 64 * h + 16 * g + 4 * e) = v;
+        }
+      if (g == 0) {
+        mls[sr * 2] = m[r];
+        mls[sr * 2 + 1] = lt;
+      }
+    }
+    __syncthreads();
+    const int srow = lane >> 2;                // scratch row of this pass
+    const int row = 16 * r + (lane >> 2);      // in the slice; rbase + row in the request
     float mk[4];
     float M = neg_inf();
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      mk[k] = mls[(k * kRows + row) * 2];
+      mk[k] = mls[(k * kRows + srow) * 2];
       M = max_f(M, mk[k]);
     }
     float L = 0.f;
@@ -390,8 +391,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void gqa_fp8_kernel(Fp8KArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float wk = mk[k] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
-      L += wk * mls[(k * kRows + row) * 2 + 1];
-      const float DCP_LDS* src = osc + (k * kRows + row) * kOStride + d0;
+      L += wk * mls[(k * kRows + srow) * 2 + 1];
+      const float DCP_LDS* src = osc + (k * kRows + srow) * kOStride + d0;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const f4 v = *reinterpret_cast<const f4 DCP_LDS*>(src + 4 * hh);
@@ -461,11 +462,15 @@ hipError_t launch_gqa_fp8_shard(const GqaArgs& a, float k_scale, float v_scale,
   k.po = static_cast<float*>(ws.po);
   const int rows = a.rows.q_len * (a.hq / a.hkv);
   if (rows < 1 || rows > 64) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)max_items, (unsigned)(a.hkv * ((rows + 31) / 32)));
-  if (rows <= 16)
+  // rows past one workgroup's share run as 32-row slices (the planner sized the items so)
+  const int slices = gqa_bf16_slices(rows);
+  const dim3 grid((unsigned)max_items, (unsigned)(a.hkv * slices));
+  if (slices == 1 && rows <= 16)
     hipExtLaunchKernelGGL((gqa_fp8_kernel<1>), grid, dim3(64 * kWaves), 0, stream, ev0, ev1, 0, k);
-  else
+  else if (slices > 1 || rows <= 32)
     hipExtLaunchKernelGGL((gqa_fp8_kernel<2>), grid, dim3(64 * kWaves), 0, stream, ev0, ev1, 0, k);
+  else
+    hipExtLaunchKernelGGL((gqa_fp8_kernel<3>), grid, dim3(64 * kWaves), 0, stream, ev0, ev1, 0, k);
   return hipGetLastError();
 }
 

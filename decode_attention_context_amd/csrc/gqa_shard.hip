@@ -118,8 +118,10 @@ constexpr int waves_for(int r) { return r >= 8 ? 8 : (r > 4 ? 8 : (r > 2 ? 4 : r
 constexpr int rows_per_wave(int r) { return (r + waves_for(r) - 1) / waves_for(r); }
 
 // kMfma: the matrix-core variant, bf16 only: four waves, HPW = 16-row tiles per wave (rows
-// past R are padding); a workgroup takes a slice of 32 of the R query rows (R > 32: two
-// workgroups per item and KV head).  Wave w takes token quarter
+// past R are padding); a workgroup takes all R <= 48 query rows (three row tiles: 48 rows at
+// the G = 16 share's q_len 3 in 98.9 us, against 107.8-116.5 us as two 32-row slices, on
+// MI355X; four row tiles spill), or a slice of 32 of them (R > 48: two workgroups per item
+// and KV head, the second reading the tiles from L2).  Wave w takes token quarter
 // w of every tile for all rows and keeps its own online softmax over those tokens:
 //   * S^T (16 tokens x 16 rows) = K (16 x 128) . Q^T on v_mfma_f32_16x16x32_bf16, the K
 //     operand (lane = token, 8 dims) read straight from the 4-row K blocks and the query
@@ -162,10 +164,10 @@ __global__ __launch_bounds__(64 * NW, min_waves_per_simd(NW)) void gqa_shard_ker
   // matrix-core variant: blockIdx.y = KV head + hkv * (32-row slice); the slices of one
   // item share its K / V tiles (a later slice's reads mostly hit L2)
   const int kvh = kMfma ? (int)blockIdx.y % a.hkv : (int)blockIdx.y;
-  const int rbase = kMfma ? 32 * ((int)blockIdx.y / a.hkv) : 0;   // first row of the slice
+  const int rbase = kMfma ? 16 * HPW * ((int)blockIdx.y / a.hkv) : 0;   // slice's first row
   // K / V copies stream with the non-temporal policy, except when two slices read the same
   // tiles: the second then finds them in L2
-  const bool nt = !(kMfma && a.q_len * (a.hq / a.hkv) > 32);
+  const bool nt = !(kMfma && a.q_len * (a.hq / a.hkv) > 16 * HPW);
   const bool single = (a.off[b + 1] - a.off[b]) == 1;
   // The wave's query rows (wave-uniform): row rho = w * HPW + h of the R = q_len * G rows
   // of this KV head is query position qi = rho / G, head kvh * G + rho % G, request row
@@ -434,73 +436,79 @@ __global__ __launch_bounds__(64 * NW, min_waves_per_simd(NW)) void gqa_shard_ker
     // once every wave has passed the barrier; no copy is in flight).  Scratch rows are
     // (wave, row tile, lane column).
     constexpr int kOStride = D + 4;   // floats per row: rows 16 bytes apart in the banks
-    constexpr int kRows = 16 * RT;    // rows per wave
+    // row tiles merged per pass: all of them where the scratch fits, else one at a time
+    constexpr int kPass = NW * 16 * RT * kOStride * 4 <= (int)sizeof(kvs) ? RT : 1;
+    constexpr int kRows = 16 * kPass;   // scratch rows per wave and pass
     static_assert(NW * kRows * kOStride * 4 <= (int)sizeof(kvs), "merge scratch");
     float DCP_LDS* osc = (float DCP_LDS*)&kvs[0];
     wait_vmcnt<0>();
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const float lt = rows_sum(ls[r]);
-      const int sr = w * kRows + 16 * r + i16;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        *reinterpret_cast<f4 DCP_LDS*>(osc + sr * kOStride + 16 * db + 4 * g) = acc[r][db];
-      if (g == 0) {
-        mls[sr * 2] = m[r];
-        mls[sr * 2 + 1] = lt;
-      }
-    }
-    __syncthreads();
     // wave tq finishes dims 32 tq .. 32 tq + 31 of every row
     const int d0 = 32 * tq + 8 * (lane & 3);
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int row = 16 * r + (lane >> 2);   // in the slice; rbase + row in the request
-      float mk[4];
-      float M = neg_inf();
+    for (int r0 = 0; r0 < RT; r0 += kPass) {
+      __syncthreads();   // the tile buffers (first pass) or the previous pass's rows are free
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mk[k] = mls[(k * kRows + row) * 2];
-        M = max_f(M, mk[k]);
-      }
-      float L = 0.f;
-      float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < kPass; ++rr) {
+        const float lt = rows_sum(ls[r0 + rr]);
+        const int sr = w * kRows + 16 * rr + i16;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float wk = mk[k] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
-        L += wk * mls[(k * kRows + row) * 2 + 1];
-        const float DCP_LDS* src = osc + (k * kRows + row) * kOStride + d0;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const f4 v = *reinterpret_cast<const f4 DCP_LDS*>(src + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[4 * hh + e] += wk * v[e];
+        for (int db = 0; db < D / 16; ++db)
+          *reinterpret_cast<f4 DCP_LDS*>(osc + sr * kOStride + 16 * db + 4 * g) = acc[r0 + rr][db];
+        if (g == 0) {
+          mls[sr * 2] = m[r0 + rr];
+          mls[sr * 2 + 1] = lt;
         }
       }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
-      if (rbase + row < R) {
-        const int qi_o = (rbase + row) / G;
-        const int orow = qi_o * a.hq + kvh * G + (rbase + row - qi_o * G);
+      __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= inv;
-        if (single && a.o_bf16) {
-          uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0;
-          *reinterpret_cast<uint4*>(dstb) =
-              make_uint4(f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16),
-                         f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16),
-                         f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16),
-                         f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16));
-        } else {
-          float* dst = single ? static_cast<float*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0
-                              : a.po + ((size_t)item * RQ + orow) * D + d0;
-          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      for (int rr = 0; rr < kPass; ++rr) {
+        const int srow = 16 * rr + (lane >> 2);        // scratch row of this pass
+        const int row = 16 * (r0 + rr) + (lane >> 2);  // in the slice; rbase + row in the request
+        float mk[4];
+        float M = neg_inf();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          mk[k] = mls[(k * kRows + srow) * 2];
+          M = max_f(M, mk[k]);
         }
-        if (tq == 0 && (lane & 3) == 0) {
-          if (single) a.lse_out[(size_t)b * RQ + orow] = lse;
-          else a.plse[(size_t)item * RQ + orow] = lse;
+        float L = 0.f;
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float wk = mk[k] == neg_inf() ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
+          L += wk * mls[(k * kRows + srow) * 2 + 1];
+          const float DCP_LDS* src = osc + (k * kRows + srow) * kOStride + d0;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const f4 v = *reinterpret_cast<const f4 DCP_LDS*>(src + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[4 * hh + e] += wk * v[e];
+          }
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const float lse = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
+        if (rbase + row < R) {
+          const int qi_o = (rbase + row) / G;
+          const int orow = qi_o * a.hq + kvh * G + (rbase + row - qi_o * G);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] *= inv;
+          if (single && a.o_bf16) {
+            uint16_t* dstb = static_cast<uint16_t*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0;
+            *reinterpret_cast<uint4*>(dstb) =
+                make_uint4(f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16),
+                           f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16),
+                           f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16),
+                           f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16));
+          } else {
+            float* dst = single ? static_cast<float*>(a.o_out) + ((size_t)b * RQ + orow) * D + d0
+                                : a.po + ((size_t)item * RQ + orow) * D + d0;
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+          }
+          if (tq == 0 && (lane & 3) == 0) {
+            if (single) a.lse_out[(size_t)b * RQ + orow] = lse;
+            else a.plse[(size_t)item * RQ + orow] = lse;
+          }
         }
       }
     }
@@ -706,7 +714,8 @@ hipError_t launch_f32(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hip
 }
 
 // bf16: the matrix-core variant, four waves, RT 16-row tiles per wave, one workgroup per
-// (item, KV head, slice of 32 rows); rows past R pad the 16-row tile.  The per-token work,
+// (item, KV head) or, past 48 rows, per (item, KV head, slice of 32 rows); rows past R pad
+// the 16-row tile.  The per-token work,
 // 4 R D flops against 4 D bytes of K and V, then stays off the vector ALUs, which did not
 // hide entirely under the HBM -> LDS stream at R = 1..8 (measured at the share's shape with
 // the vector ALUs doing the bf16 products in v_dot2: 73-76% of HBM peak against 79-82% on
@@ -722,8 +731,12 @@ void launch_m(const GqaKArgs& k, dim3 grid, int slices, hipStream_t s, hipEvent_
 hipError_t launch_bf16(const GqaKArgs& k, int rows, dim3 grid, hipStream_t s, hipEvent_t e0,
                        hipEvent_t e1) {
   if (rows < 1 || rows > 64) return hipErrorInvalidValue;
-  if (rows <= 16) launch_m<1>(k, grid, 1, s, e0, e1);
-  else launch_m<2>(k, grid, (rows + 31) / 32, s, e0, e1);
+  static_assert(kGqaSliceRows <= 48, "at most three 16-row tiles per wave");
+  const int slices = gqa_bf16_slices(rows);
+  if (slices > 1) launch_m<2>(k, grid, slices, s, e0, e1);
+  else if (rows <= 16) launch_m<1>(k, grid, 1, s, e0, e1);
+  else if (rows <= 32) launch_m<2>(k, grid, 1, s, e0, e1);
+  else launch_m<3>(k, grid, 1, s, e0, e1);
   return hipGetLastError();
 }
 

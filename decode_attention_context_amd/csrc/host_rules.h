@@ -23,6 +23,10 @@ constexpr int kMlaTile = 32;
 constexpr int kMaxQLen = 4;
 // Bytes of one GQA K or V row the vector and matrix-core kernels are written for.
 constexpr int kGqaRowBytes = 256;
+// bf16 GQA: query rows (q_len x group) one workgroup takes per item and KV head (up to three
+// 16-row tiles per wave); more rows are cut into slices of 32, one workgroup each
+constexpr int kGqaSliceRows = 48;
+inline int gqa_bf16_slices(int rows) { return rows > kGqaSliceRows ? (rows + 31) / 32 : 1; }
 // Head dim of the fp8-cache GQA kernel.
 constexpr int kGqaFp8HeadDim = 128;
 // MLA shape ("The memory wall in long-context inference", MLA item): the query heads read
@@ -133,10 +137,10 @@ inline bool make_plan(const dcp_attn_desc* d, int q_len, int batch, int cus, Pla
   if (d->kind == DCP_GQA) {
     p->tile = kGqaTile;
     // two resident workgroups (64 KiB double buffer each) per CU and KV head, one round;
-    // bf16 queries with more than 32 rows per KV head take two workgroups (32-row slices)
-    // per item and KV head, so half the items
+    // bf16 queries with more rows per KV head than one workgroup takes run as 32-row slices,
+    // one workgroup each per item and KV head, so proportionally fewer items
     const int rows = q_len * (d->num_q_heads / d->num_kv_heads);
-    const int slices = (d->dtype == DCP_BF16 && rows > 32) ? 2 : 1;
+    const int slices = d->dtype == DCP_BF16 ? gqa_bf16_slices(rows) : 1;
     p->target = std::max<int64_t>(1, (int64_t)cus * 2 / ((int64_t)d->num_kv_heads * slices));
     p->min_chunk = kGqaTile;
   } else {
