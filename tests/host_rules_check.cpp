@@ -232,7 +232,8 @@ void layout_invariants(const dcp_attn_desc& d, int q_len, int batch, int cus,
         (long long)p.target);
   if (d.kind == DCP_GQA) {
     const int64_t rows = (int64_t)q_len * (d.num_q_heads / d.num_kv_heads);
-    const int64_t slices = (d.dtype == DCP_BF16 && rows > 32) ? 2 : 1;
+    // bf16 queries: up to 48 rows per workgroup, more as two 32-row slices
+    const int64_t slices = (d.dtype == DCP_BF16 && rows > 48) ? 2 : 1;
     CHECK(p.target == std::max<int64_t>(1, 2LL * cus / (d.num_kv_heads * slices)), "gqa target");
     CHECK(p.tile == 64 && p.min_chunk == 64 && w.po_bf16 == 0, "gqa plan");
   } else {
