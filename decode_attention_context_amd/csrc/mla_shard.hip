@@ -90,7 +90,11 @@ constexpr float kRescaleSlack = 8.f;
 // K operand prefetch distance (k-steps): 3 where the registers allow it (the page-contiguous
 // path); the general path keeps more table state live and stays at 2 to avoid spills
 template <bool kFast> constexpr int ahead_k() { return kFast ? 3 : 2; }
-constexpr int kAheadV = 3;                     // V^T operand prefetch distance (dv tiles)
+// V^T operand prefetch distance (dv tiles): up to 14 transposed LDS reads in flight per wave
+// (the counter's limit is 15).  Measured on MI355X at the MLA decode shape, 60 interleaved
+// launches each: 171.5 -> 166.1 us against 3 tiles ahead (175.0 -> 170.6 us on another box);
+// K prefetch beyond 3 k-steps spills and gains nothing.
+constexpr int kAheadV = 7;
 // tile tables: two windows; page-contiguous tiles keep one entry (first row) per tile and
 // 64 tiles per window, general tiles one entry (row) per token and 12 tiles per window
 constexpr int kFastWin = 64;
