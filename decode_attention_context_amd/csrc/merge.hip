@@ -162,7 +162,12 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
     wpart += x == neg_inf() ? 0.f : exp2f(fmaf(x, kLog2e, -m2));
   }
   const float inv = 1.f / wave_sum_dpp(wpart);
-  for (int d = c0 + lane * VEC; d < c1; d += 64 * VEC) {
+  // The column loop is wave-uniform: every lane computes its weight wl in every pass, since
+  // the weights are read across lanes (readlane); lanes past the row's end (dv not a
+  // multiple of 64 VEC) load and store nothing.
+  for (int d0 = c0; d0 < c1; d0 += 64 * VEC) {
+    const int d = d0 + lane * VEC;
+    const bool act = d < c1;
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
@@ -180,11 +185,11 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
           typename RawBf16<VEC>::T v[kB];
 #pragma unroll
           for (int u = 0; u < kB; ++u)
-            if (wv[u] != 0.f)
+            if (wv[u] != 0.f && act)
               v[u] = ld_raw_bf16<VEC, kNt>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
 #pragma unroll
           for (int u = 0; u < kB; ++u) {
-            if (wv[u] != 0.f) {
+            if (wv[u] != 0.f && act) {
               float f[VEC];
               widen_bf16<VEC>(v[u], f);
 #pragma unroll
@@ -195,13 +200,15 @@ __device__ __forceinline__ void merge_row(const void* __restrict__ o_base, int64
           V v[kB];
 #pragma unroll
           for (int u = 0; u < kB; ++u)
-            if (wv[u] != 0.f) v[u] = ldp<VEC, false, kNt>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
+            if (wv[u] != 0.f && act)
+              v[u] = ldp<VEC, false, kNt>(o_base, (int64_t)(r0 + r + u) * o_stride + d);
 #pragma unroll
           for (int u = 0; u < kB; ++u)
-            if (wv[u] != 0.f) vfma<VEC>(acc, wv[u], v[u]);
+            if (wv[u] != 0.f && act) vfma<VEC>(acc, wv[u], v[u]);
         }
       }
     }
+    if (!act) continue;
     if (out_f32) {
       V o;
       float* po = reinterpret_cast<float*>(&o);
