@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64 * NW, min_waves_per_simd(NW)) void gqa_shard_ker
   const int4 it = a.items[blockIdx.x];   // in dispatch order, longest first
   const int b = it.x, j0 = it.y, j1 = it.z;
   const int item = it.w;                 // index of the item's partial
-  // matrix-core variant: blockIdx.y = KV head + hkv * (32-row slice); the slices of one
+  // matrix-core variant: blockIdx.y = KV head + hkv * (row slice); the slices of one
   // item share its K / V tiles (a later slice's reads mostly hit L2)
   const int kvh = kMfma ? (int)blockIdx.y % a.hkv : (int)blockIdx.y;
   const int rbase = kMfma ? 16 * HPW * ((int)blockIdx.y / a.hkv) : 0;   // slice's first row

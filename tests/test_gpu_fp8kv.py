@@ -34,7 +34,7 @@ CASES = [
             interleave=3, lengths=(7, 1100), seed=109),
     F.with_(name="fp8_g4_c4", batch=3, num_q_heads=8, num_kv_heads=2, cp_size=4, interleave=64,
             block_size=64, lengths=(1, 300, 2600), seed=110),
-    # 48 and 64 rows per KV head: two 32-row slices
+    # 48 rows per KV head: one workgroup (three row tiles per wave); 64: two 32-row slices
     F.with_(name="fp8_g16_q4", batch=2, q_len=4, num_q_heads=16, lengths=(3, 2000), seed=111),
     F.with_(name="fp8_g16_q3_h2_i3", batch=2, q_len=3, num_q_heads=32, num_kv_heads=2,
             block_size=16, interleave=3, lengths=(40, 900), seed=112),

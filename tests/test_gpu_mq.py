@@ -4,8 +4,8 @@ the request's draft tokens) against the CPU oracle (GPU).
 Every case runs all ranks' shards through dcp_attn_shard_mq, merges them with dcp_merge
 and compares every rank's partial and the merged output of the checked requests with the
 oracle, elementwise (tolerances in parity_helpers).  The cases cover every q_len, GQA rows
-per KV head from 1 to 64 (bf16 on the matrix cores, 32-row slices past 32 rows; fp32 on
-the vector ALUs), both dtypes, both
+per KV head from 1 to 64 (bf16 on the matrix cores, one workgroup up to 48 rows and
+32-row slices past 48; fp32 on the vector ALUs), both dtypes, both
 MLA tile paths (page-contiguous and token-granular), requests shorter than q_len (query
 positions before the sequence start: empty rows), positions whose visible tokens end
 inside or before an item, and the full-size GQA share and MLA decode shapes.
@@ -46,7 +46,7 @@ MQ_GQA = [
     G.with_(name="mq_gqa_g8_q3", batch=4, q_len=3, lengths=(1, 2, 129, 2050), seed=52),
     G.with_(name="mq_gqa_g8_q4_i1", batch=3, q_len=4, block_size=32, cp_size=4, interleave=1,
             lengths=(3, 515, 1800), seed=53),
-    # G = 16, q_len 4 / 3: 64 / 48 rows per KV head (two 32-row slices)
+    # G = 16, q_len 4 / 3: 64 rows per KV head (two 32-row slices) / 48 (one workgroup)
     G.with_(name="mq_gqa_g16_q4", batch=2, q_len=4, num_q_heads=16, lengths=(9, 1300),
             seed=54),
     G.with_(name="mq_gqa_g16_q3_h2_i1", batch=2, q_len=3, num_q_heads=32, num_kv_heads=2,

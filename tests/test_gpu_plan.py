@@ -29,6 +29,9 @@ CASES = [
     # 64 query rows per KV head on two KV heads: two 32-row slices per item and KV head
     (wl.GQA_SHARE.with_(name="plan_gqa_g16_q4_h2", batch=5, q_len=4, num_q_heads=32,
                         num_kv_heads=2, lengths=(1, 65, 5000, 20001, 300), seed=84), dca.GQA, 1),
+    # 48 query rows per KV head: one workgroup per item and KV head
+    (wl.GQA_SHARE.with_(name="plan_gqa_g16_q3", batch=4, q_len=3, num_q_heads=16,
+                        lengths=(2, 300, 9000, 20001), seed=86), dca.GQA, 1),
     # fp32 queries and cache (vector-ALU kernel)
     (wl.GQA_SHARE.with_(name="plan_gqa_f32", dtype="f32", head_dim_qk=64, head_dim_v=64,
                         batch=3, lengths=(1, 4000, 20001), seed=85), dca.GQA, 1),
@@ -64,7 +67,7 @@ def test_plan(gpu_lib, w, kind, rank):
     tile = 64 if kind == dca.GQA else 32
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rows = w.q_len * (w.num_q_heads // w.num_kv_heads)
-    slices = 2 if (kind == dca.GQA and w.dtype == "bf16" and rows > 32) else 1
+    slices = 2 if (kind == dca.GQA and w.dtype == "bf16" and rows > 48) else 1
     target = (max(1, cus * 2 // (w.num_kv_heads * slices)) if kind == dca.GQA
               else max(1, cus // w.q_len))
     assert chunk % tile == 0 and chunk > 0
