@@ -82,3 +82,6 @@ def test_merge_many_partials(gpu_lib, c, b, h, dv, in_bf16):
     assert_close(lse_out.cpu().numpy(), ref_l, (1e-5, 1e-5), "merged lse")
     assert_close(out.cpu().numpy(), ref_o, (1e-5, 1e-5), "merged O")
     assert torch.all(out[0, 0] == 0)
+    # bf16 output: the float32 result rounded to nearest even
+    out_bf, _ = dca.merge(o.cuda(), lse.cuda(), out_dtype=torch.bfloat16, want_lse=False)
+    assert torch.equal(out_bf.cpu(), out.cpu().to(torch.bfloat16))

@@ -77,6 +77,10 @@ def test_slots_bit_exact_workloads(gpu_lib, w):
     (8, 4, 8, [32, 64, 96]),                # L = 0 mod I C
     (4, 5, 7, [1, 2, 3, 34, 35, 36]),
     (64, 8, 64, [1, 63, 64, 65, 511, 512, 513]),
+    (1, 3, 5, [1, 2, 15, 16, 301]),         # one token per page
+    (16, 64, 1, [1, 63, 64, 65, 200]),      # many ranks, most shards of short requests empty
+    (128, 4, 100000, [1, 5000, 70000]),     # an interleave longer than every sequence
+    (1024, 2, 1024, [1, 1024, 1025, 3000]), # large pages
 ])
 def test_slots_bit_exact_edges(gpu_lib, B, C, I, lens):
     rng = np.random.default_rng(B * 100 + C * 10 + I)
