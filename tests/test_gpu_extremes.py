@@ -85,3 +85,36 @@ def test_merge_many_partials(gpu_lib, c, b, h, dv, in_bf16):
     # bf16 output: the float32 result rounded to nearest even
     out_bf, _ = dca.merge(o.cuda(), lse.cuda(), out_dtype=torch.bfloat16, want_lse=False)
     assert torch.equal(out_bf.cpu(), out.cpu().to(torch.bfloat16))
+
+
+ITEM_CASES = [
+    # one long request per call: the planner cuts it into hundreds of work items, so the
+    # split combine merges more than 64 partials per row (GQA: one wave per row; MLA: one
+    # wave per 256 columns, the first 32 partials loaded with the lse)
+    G.with_(name="x_gqa_one_long", batch=1, cp_size=1, lengths=(100000,), seed=320),
+    F.with_(name="x_fp8_one_long", batch=1, cp_size=1, lengths=(100000,), seed=321),
+    M.with_(name="x_mla_one_long", batch=1, cp_size=1, lengths=(60000,), seed=322),
+    M.with_(name="x_mla_one_long_q2", batch=1, cp_size=2, q_len=2, lengths=(61000,), seed=323),
+    T.with_(name="x_f32_one_long", batch=1, cp_size=1, lengths=(50000,), seed=324),
+]
+
+
+@pytest.mark.parametrize("w", ITEM_CASES, ids=[w.name for w in ITEM_CASES])
+def test_many_items_per_request(gpu_lib, w):
+    """A single long request, split over many work items, against the oracle."""
+    kind = dca.MLA if w.kind == "mla" else dca.GQA
+    inp = wl.make_inputs(w, device="cuda")
+    o_parts, l_parts = run_shards(inp, kind, w.cp_size, w.interleave, w.scale)
+    o_m, l_m = dca.merge(o_parts, l_parts)
+    torch.cuda.synchronize()
+    _, _, ws = dca.shard(inp["q"], inp["k_pages"] if kind == dca.GQA else inp["latent_pages"],
+                         inp["v_pages"] if kind == dca.GQA else None, inp["block_table"],
+                         inp["seq_lens"], 0, w.cp_size, w.interleave, w.scale, kind=kind,
+                         max_seq_len=inp["max_seq_len"], k_scale=inp.get("k_scale"),
+                         v_scale=inp.get("v_scale"))
+    torch.cuda.synchronize()
+    n_items = int(ws[:8].cpu().numpy().view("int32")[1])   # plan header: item count
+    print(f"[items] {w.name}: {n_items} work items on rank 0", flush=True)
+    assert n_items > 64
+    check_requests(inp, kind, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
+                   range(w.batch), w.name)
