@@ -5,7 +5,9 @@ Each case draws a kernel (bf16 GQA, fp32 GQA, GQA over an fp8 cache, MLA), a gro
 KV heads, q_len, cp_size, interleave, block size and ragged lengths (with edge values:
 1, a block, a block + 1, an interleave period) from its own seed, runs every rank's shard
 and the merge, and compares them elementwise with the oracle (tolerances in
-parity_helpers).  The draws are fixed by the seeds, so a failure names its case.
+parity_helpers).  Three classes: small, wide (longer sequences, more KV heads) and extreme
+(odd block sizes from 1 to 1024 tokens, up to 64 ranks, interleaves past every sequence).
+The draws are fixed by the seeds, so a failure names its case.
 """
 import numpy as np
 import pytest
@@ -48,10 +50,42 @@ def _draw(seed, wide=False):
                       interleave=il, lengths=lengths, seed=seed)
 
 
+def _draw_extreme(seed):
+    """Extreme layouts: blocks of 1 to 1024 tokens (odd sizes included), up to 64 ranks,
+    interleaves to 70000 (past every sequence), batches to 8, up to 16 KV heads."""
+    rng = np.random.default_rng(seed)
+    kind = ["gqa_bf16", "gqa_f32", "gqa_fp8", "mla"][seed % 4]
+    q_len = int(rng.integers(1, 5))
+    block = int(rng.choice([1, 3, 5, 16, 48, 64, 100, 128, 512, 1024]))
+    cp = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 64]))
+    il = int(rng.choice([1, 2, 5, 31, 64, 100, 128, 1000, 70000]))
+    batch = int(rng.integers(1, 9))
+    top = 12000 if kind == "mla" else 30000
+    edges = [1, 2, block, block + 1, il, il + 1, min(il * cp, top), min(il * cp + 1, top), q_len]
+    lengths = tuple(int(rng.choice(edges)) if rng.random() < 0.35 else
+                    int(rng.integers(1, top)) for _ in range(batch))
+    if kind == "mla":
+        heads = int(rng.choice([16, 32, 64, 128]))
+        return wl.MLA_DECODE.with_(name=f"ext{seed}_mla", batch=batch, q_len=q_len,
+                                   num_q_heads=heads, block_size=block, cp_size=cp,
+                                   interleave=il, lengths=lengths, seed=seed)
+    hkv = int(rng.choice([1, 2, 4, 8, 16]))
+    groups = [g for g in (1, 2, 3, 5, 7, 8, 11, 16, 24, 32, 48, 64) if g * q_len <= 64]
+    g = int(rng.choice(groups))
+    base = wl.TINY_GQA if kind == "gqa_f32" else (wl.GQA_SHARE_FP8 if kind == "gqa_fp8"
+                                                   else wl.GQA_SHARE)
+    return base.with_(name=f"ext{seed}_{kind}", batch=batch, q_len=q_len, num_q_heads=g * hkv,
+                      num_kv_heads=hkv, block_size=block, cp_size=cp, interleave=il,
+                      lengths=lengths, seed=seed)
+
+
 SEEDS = list(range(2000, 2096))
 
 
 WIDE_SEEDS = list(range(5000, 5048))
+
+
+EXTREME_SEEDS = list(range(9000, 9024))
 
 
 def _check(w):
@@ -74,3 +108,8 @@ def test_random_case(gpu_lib, seed):
 @pytest.mark.parametrize("seed", WIDE_SEEDS)
 def test_random_wide_case(gpu_lib, seed):
     _check(_draw(seed, wide=True))
+
+
+@pytest.mark.parametrize("seed", EXTREME_SEEDS)
+def test_random_extreme_case(gpu_lib, seed):
+    _check(_draw_extreme(seed))
