@@ -13,7 +13,9 @@
 // practice) each lane issues the loads of all its partial-row chunks together with the lse
 // load, so a row costs one memory round trip; weights of empty partials are exactly 0 and
 // their rows (which may hold garbage) are excluded by a select, never multiplied.  More
-// partials are streamed eight at a time, empty ones not read.  The kernel is HBM-bound.
+// partials are streamed eight at a time, empty ones not read.  A split combine over few
+// rows gives each 64 * VEC columns of a row a wave of its own instead.  The kernel is
+// HBM-bound.
 #include <type_traits>
 
 #include "launch.h"
@@ -478,10 +480,11 @@ __host__ __device__ __forceinline__ bool merge_small_ok(int n, int dv, int vec) 
   return n <= 8 && dv % (64 * vec) == 0 && dv <= 2 * 64 * vec;
 }
 
+// split combine: waves (rows, or column chunks of rows) per workgroup
 constexpr int kRowsPerBlock = 4;
-// Split combines whose rows come to at most this many column chunks (two waves per SIMD on
-// 256 CUs) give each chunk a wave of its own; that kernel holds up to 32 partial chunks per
-// lane in registers (two waves per SIMD).
+// Split combines whose rows come to at most this many column chunks give each chunk a wave
+// of its own: two waves per SIMD on 256 CUs, which is also what that kernel's registers
+// allow (it holds up to 32 partial chunks per lane).
 constexpr int64_t kWideCombineWaves = 2048;
 // dcp_merge rows (waves) per workgroup.  Measured on MI355X, eight float32 partials of
 // 64 x 128 rows x 512 dims from HBM: 28.4 us at 16 rows against 29.0 us at 8, 29.4 us at 4
