@@ -60,7 +60,7 @@ def test_noalloc_matches_workspace_call(gpu_lib, pair, out_dtype):
 
 
 def test_noalloc_rejects_beyond_scratch(gpu_lib):
-    # 1024 MLA requests: the float32 split partials alone need far more than the scratch
+    # 1024 MLA requests: the split partials alone need far more than the scratch
     print("[noalloc] oversize", flush=True)
     b = 1024
     q = torch.zeros(b, 128, 576, dtype=torch.bfloat16, device="cuda")
