@@ -749,7 +749,7 @@ def secondary_fp8kv(dca, wl, torch):
     return res
 
 
-def secondary_long(dca, wl, torch, steps=10, samples=None):
+def secondary_long(dca, wl, torch, steps=30, samples=None):
     """Long-context MLA (8 requests x 200000 tokens, C = 4, I = 128): all 4 shard kernels of
     a step (sum of their durations, MFMA utilisation, HBM rate), the merge of 4 partials per
     (request, head) row (10.5 MB: latency-bound), and the whole step replayed as a HIP
@@ -758,7 +758,7 @@ def secondary_long(dca, wl, torch, steps=10, samples=None):
     inp = wl.make_inputs(w, device="cuda")
     lens = w.seq_lens()
     step, shard_ev, merge_ev, ws = run_step_fns(dca, w, inp, dca.MLA)
-    for _ in range(2):
+    for _ in range(3):
         step(False)
     torch.cuda.synchronize()
     for _ in range(steps):
@@ -775,7 +775,8 @@ def secondary_long(dca, wl, torch, steps=10, samples=None):
     merge_s = sorted(a.elapsed_time(b) for a, b in merge_ev)[len(merge_ev) // 2] / 1e3
     merge_bytes = (C + 1) * w.batch * w.num_q_heads * (w.head_dim_v + 1) * 4
     graph = capture_step(torch, step)
-    graph.replay()
+    for _ in range(3):
+        graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
