@@ -38,12 +38,13 @@
 //     waves' vector-memory counters and a bare s_barrier per tile, so the compiler never
 //     drains them before LDS reads.  The 16-byte chunks of a row are XOR-swizzled by
 //     (row mod 8), which spreads the operand reads over the LDS banks.
-//   * Where each tile comes from is read from a table in LDS, built a window ahead by wave
-//     3.  When the interleave and the block size are multiples of 32, a tile is one run of
+//   * Where each tile comes from is read from a table in LDS, built a window ahead.  When
+//     the interleave and the block size are multiples of 32, a tile is one run of
 //     consecutive slots of one page and the table holds its first cache row (64 tiles per
-//     window); otherwise (down to interleave 1) it holds the cache row of every token (12
-//     tiles per window).  Wave 3 stages a window's block-table entries just before its own
-//     copies of the next tile, so the per-tile counter wait covers them (no drain).
+//     window, one pass built by wave 3); otherwise (down to interleave 1) it holds the cache
+//     row of every token (12 tiles per window, six passes spread over the four waves and
+//     six iterations).  A wave stages its block-table entries just before its own copies of
+//     the next tile, so the per-tile counter wait covers them (no drain).
 //   * Multi-token decode (q_len query positions per request, the last q_len cache tokens
 //     being the request's own draft tokens): each work item gets one workgroup per query
 //     position, all on one XCD (the later ones read the tiles from L2).  Position i sees
@@ -78,15 +79,18 @@ constexpr int kTileBytes = kTile * kRowBytes;  // 36 KiB
 constexpr int kKSteps = kDk / 32;              // 18 k-steps of S^T = K Q^T
 constexpr int kDvTiles = kDv / 16;             // 32 value-dim tiles of O^T
 constexpr int kWaves = 4;                      // H / 4 heads each (32 at 128 heads)
-constexpr int kBuilder = 3;                    // wave 3 builds the tile tables
+constexpr int kBuilder = 3;                    // wave 3 builds window 0 and page-run tables
 constexpr int kSlots = kTileBytes / 1024;      // 36 one-KiB copies per tile
-// All four waves copy every tile (9 one-KiB copies each), the table builder (wave 3)
-// included: its block-table entries are staged before its copies of the next tile and
+// All four waves copy every tile (9 one-KiB copies each), the table builders included: a
+// wave's block-table entries are staged before its copies of the next tile and
 // vector-memory loads complete in order, so the wait that lets the next tile's copies stay
-// in flight also covers the staged entries (no drain at a window build).  Against a builder
-// that copied nothing on fine interleaves (waves 0..2 taking 12 copies each) and drained its
-// copies at every window build, measured on MI355X: 197.1 -> 180.1 us at interleave 1 and
-// 169.3 -> 161.7 us at interleave 64 (MLA decode shape, median of 40 interleaved launches).
+// in flight also covers the staged entries (no drain at a window build).  Against one
+// builder wave that copied nothing on fine interleaves (waves 0..2 taking 12 copies each)
+// and drained its copies at every window build, measured on MI355X: 197.1 -> 180.1 us at
+// interleave 1 and 169.3 -> 161.7 us at interleave 64 (MLA decode shape, median of 40
+// interleaved launches); spreading the per-token window build over the four waves and
+// reading each copy's row one copy ahead then took interleave 1 from 191.0 to 183.2 us
+// (5626 -> 5076 cycles per tile and wave).
 constexpr int kCopyWaves = kWaves;
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kRescaleSlack = 8.f;
@@ -215,12 +219,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   constexpr int kSlotsPerWave = kSlots / kCopyWaves;
   const bool copier = w < kCopyWaves;
 
-  // ---- tile tables (built by wave kBuilder): window W in half W & 1 of the table.
-  // stage(W) copies the block-table entries of window W's tokens (page-contiguous: of each
-  // tile's first token) into LDS by global_load_lds_dword; commit(W), one iteration later,
-  // turns them into cache rows (~0 for no token or a bad page).  In the tile loop the
-  // staged entries go out at the top of an iteration, before the builder's copies of tile
-  // t + 3, so the next iteration's wait (everything but those copies) covers them.
+  // ---- tile tables: window W in half W & 1 of the table.  stage_pass(W, p) copies the
+  // block-table entries of 64 of window W's tokens (page-contiguous: of each tile's first
+  // token) into LDS by global_load_lds_dword; commit_pass(W, p), one iteration later and by
+  // the same wave, turns them into cache rows (~0 for no token or a bad page).  In the tile
+  // loop the staged entries go out at the top of an iteration, before that wave's copies of
+  // tile t + 3, so the next iteration's wait (everything but those copies) covers them.
   constexpr int kWin = kFast ? kFastWin : kGenWin;
   constexpr int kPasses = kFast ? 1 : kWinEntries / 64;   // 64 entries per pass
   uint32_t DCP_LDS* const tab = (uint32_t DCP_LDS*)(smem + kTabOff);
@@ -238,34 +242,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   };
   // (the passes stay a loop: unrolled, their walks would be scheduled together and need
   // registers the tile loop does not have)
-  auto stage_window = [&](int W) {
-    const uint32_t dst = lds_addr + kStageOff;
-#pragma unroll 1
-    for (int p = 0; p < kPasses; ++p) {
-      uint32_t t;
-      const bool valid = entry_pos(W, p * 64 + lane, t);
-      const int32_t* src = btb + (valid ? t / B : 0u);
-      asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
-                   :
-                   : "v"(src), "{m0}"(dst + p * 256)
-                   : "memory");
-    }
+  auto stage_pass = [&](int W, int p) {
+    uint32_t t;
+    const bool valid = entry_pos(W, p * 64 + lane, t);
+    const int32_t* src = btb + (valid ? t / B : 0u);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "{m0}"(lds_addr + kStageOff + p * 256)
+                 : "memory");
   };
-  auto commit_window = [&](int W) {   // the staged entries have landed (see the callers)
+  auto commit_pass = [&](int W, int p) {   // the staged entries have landed (see the callers)
+    const int e = p * 64 + lane;
+    uint32_t t;
+    uint32_t row = ~0u;
     bool bad = false;
-#pragma unroll 1
-    for (int p = 0; p < kPasses; ++p) {
-      const int e = p * 64 + lane;
-      uint32_t t;
-      uint32_t row = ~0u;
-      if (entry_pos(W, e, t)) {
-        const int32_t pg = stage[e];
-        if (pg < 0 || (uint32_t)pg >= a.num_blocks) bad = true;
-        else row = (uint32_t)pg * B + (t - (t / B) * B);
-      }
-      if (!kFast || e < kWin)
-        *tab_entry(W * kWin + (kFast ? e : e / kTile), kFast ? 0 : e % kTile) = row;
+    if (entry_pos(W, e, t)) {
+      const int32_t pg = stage[e];
+      if (pg < 0 || (uint32_t)pg >= a.num_blocks) bad = true;
+      else row = (uint32_t)pg * B + (t - (t / B) * B);
     }
+    if (!kFast || e < kWin)
+      *tab_entry(W * kWin + (kFast ? e : e / kTile), kFast ? 0 : e % kTile) = row;
     if (__ballot(bad) != 0 && lane == 0) atomicOr(&a.header[0], kErrBlockId);
   };
 
@@ -291,6 +288,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     uint32_t dst;                     // LDS address of this wave's first slot
     int nvalid;                       // page-contiguous tiles: rows holding tokens
     int ti;                           // the tile (general tiles: its rows are in the table)
+    uint32_t row;                     // general tiles: the row of the next copy's token
     __device__ uint32_t off(int k) const { return (k & 1) ? so[k / 2] >> 16 : so[k / 2] & 0xffffu; }
   };
   auto plan_copy = [&](int ti) -> TileCopy {
@@ -302,6 +300,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     for (int i = 0; i < (kSlotsPerWave + 1) / 2; ++i) c.so[i] = all[i];
     c.dst = lds_addr + (uint32_t)((ti % kNBuf) * kTileBytes + kSlotsPerWave * w * 1024);
     c.ti = ti;
+    if constexpr (!kFast) c.row = *tab_entry(ti, (int)(c.off(0) / kRowBytes));
     if constexpr (kFast) {
       const uint32_t row0 = __builtin_amdgcn_readfirstlane(*tab_entry(ti, 0));
       const bool ok = row0 != ~0u;
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     }
     return c;
   };
-  auto copy_slot = [&](const TileCopy& c, int k) {
+  auto copy_slot = [&](TileCopy& c, int k) {
     if constexpr (kFast) {
       // rows past the valid ones re-read row 0 (their tokens are masked)
       uint32_t voff = c.off(k);
@@ -321,15 +320,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
       copy16_sbase<kNt>(c.dst + k * 1024, voff, c.base);
     } else {
       // each copy takes the row of its token from the table (tokens without a valid row
-      // re-read row 0)
+      // re-read row 0); the next copy's row is read from the table one copy ahead
       const uint32_t r = c.off(k) / kRowBytes;
-      const uint32_t row = *tab_entry(c.ti, (int)r);
+      const uint32_t row = c.row;
+      if (k + 1 < kSlotsPerWave) c.row = *tab_entry(c.ti, (int)(c.off(k + 1) / kRowBytes));
       const char* src = a.lat + (size_t)(row == ~0u ? 0u : row) * kRowBytes + (c.off(k) - r * kRowBytes);
       copy16_vaddr<kNt>(c.dst + k * 1024, src);
     }
   };
   auto issue_tile = [&](int ti) {
-    const TileCopy c = plan_copy(ti);
+    TileCopy c = plan_copy(ti);
 #pragma unroll
     for (int k = 0; k < kSlotsPerWave; ++k) copy_slot(c, k);
   };
@@ -362,9 +362,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
   }
   // window 0 of the tile table before the first copy
   if (w == kBuilder && ntiles > 0) {
-    stage_window(0);
+#pragma unroll 1
+    for (int p = 0; p < kPasses; ++p) stage_pass(0, p);
     wait_vmcnt<0>();
-    commit_window(0);
+#pragma unroll 1
+    for (int p = 0; p < kPasses; ++p) commit_pass(0, p);
   }
   wait_lgkm0();
   asm volatile("s_barrier" ::: "memory");
@@ -466,10 +468,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_shard_kernel(MlaKArgs a) {
     else wait_vmcnt<0>();
     wait_lgkm0();
     asm volatile("s_barrier" ::: "memory");
-    // tables: window W + 1 is staged at iteration W * kWin and committed one iteration later
-    if (staged) commit_window((t - 1) / kWin + 1);
-    if (w == kBuilder && t % kWin == 0 && (t / kWin + 1) * kWin < ntiles)
-      stage_window(t / kWin + 1);
+    // tables: page-contiguous tiles: window W + 1 (one pass) is staged by wave 3 at
+    // iteration W kWin and committed one iteration later; per-token tables: pass p of window
+    // W + 1 is staged at iteration W kWin + p by wave p mod 4 and committed one iteration
+    // later by the same wave, so the build is spread over the waves and the iterations
+    if constexpr (kFast) {
+      if (staged) commit_pass((t - 1) / kWin + 1, 0);
+      if (w == kBuilder && t % kWin == 0 && (t / kWin + 1) * kWin < ntiles)
+        stage_pass(t / kWin + 1, 0);
+    } else {
+      const int tw = t % kWin;
+      if ((t / kWin + 1) * kWin < ntiles) {
+        if (tw >= 1 && tw <= kPasses && (tw - 1) % kWaves == w) commit_pass(t / kWin + 1, tw - 1);
+        if (tw < kPasses && tw % kWaves == w) stage_pass(t / kWin + 1, tw);
+      }
+    }
     // tokens of tile t that do not exist (a partial tile, a bad page): scores -inf (a
     // uniform branch, taken on few tiles)
     const uint32_t vmask = vmask_next;
