@@ -118,3 +118,32 @@ def test_many_items_per_request(gpu_lib, w):
     assert n_items > 64
     check_requests(inp, kind, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
                    range(w.batch), w.name)
+
+
+WINDOW_CASES = [
+    # per-token tile tables (interleave or block size not a multiple of 32) with items long
+    # enough that the table windows (12 tiles each) are rebuilt several times inside an item
+    M.with_(name="x_mla_i1_windows", batch=1, num_q_heads=16, cp_size=2, interleave=1,
+            lengths=(600000,), seed=330),
+    M.with_(name="x_mla_b16_i3_windows", batch=2, num_q_heads=32, block_size=16, cp_size=1,
+            interleave=3, lengths=(300000, 5), seed=331),
+    M.with_(name="x_mla_i1_q2_windows", batch=1, num_q_heads=16, cp_size=2, interleave=1,
+            q_len=2, lengths=(400000,), seed=332),
+]
+
+
+@pytest.mark.parametrize("w", WINDOW_CASES, ids=[w.name for w in WINDOW_CASES])
+def test_mla_table_windows_inside_items(gpu_lib, w):
+    """MLA work items spanning several per-token table windows, against the oracle."""
+    inp = wl.make_inputs(w, device="cuda")
+    o_parts, l_parts = run_shards(inp, dca.MLA, w.cp_size, w.interleave, w.scale)
+    o_m, l_m = dca.merge(o_parts, l_parts)
+    _, _, ws = dca.shard(inp["q"], inp["latent_pages"], None, inp["block_table"],
+                         inp["seq_lens"], 0, w.cp_size, w.interleave, w.scale, kind=dca.MLA,
+                         max_seq_len=inp["max_seq_len"])
+    torch.cuda.synchronize()
+    chunk = int(ws[:16].cpu().numpy().view("int32")[2])   # plan header: item size (tokens)
+    print(f"[windows] {w.name}: items of {chunk} tokens ({chunk // 32} tiles)", flush=True)
+    assert chunk // 32 > 24
+    check_requests(inp, dca.MLA, w.cp_size, w.interleave, w.scale, o_parts, l_parts, o_m, l_m,
+                   range(w.batch), w.name)
